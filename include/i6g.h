@@ -1,0 +1,241 @@
+/*
+ * i6g.h -- C ABI of the int6/int8 per-row scoring library for MI355X (gfx950).
+ *
+ * The library runs the scoring forward pass of a small GPT whose block
+ * matrices are stored as per-row integer codes with one binary16 scale per
+ * row, and reduces the per-token cross-entropy to bits per byte over
+ * sliding windows.  The operations follow these web pages (cited by page
+ * and section; the same citations appear beside each entry point):
+ *
+ *   [11L]  pwwt.cn, "parameter-golf 16MB 极限压缩实战：11L MLP3x + Int6 QAT +
+ *          zstd-22 记录详解" -- 训练时的模拟量化, 后训练量化导出, 架构：11 层
+ *          U-Net 变压器, 滑动窗口评估：每 64 token 计一次分.
+ *   [363]  kwkr.cn write-up of parameter-golf PR #363 "Depth Recurrence +
+ *          Mixed-Precision Quantization" -- Middle-Cycle Stem/Core/Tail
+ *          layout, DepthLoRA, BigramHash, Noisy-QAT code block.
+ *   [RM]   pigsec.cn mirror of the openai/parameter-golf README -- bits per
+ *          byte; parallel residual lanes and looped layers 4-5.
+ *
+ * Conventions
+ *   - Pointers named *_dev are HIP device pointers.  Pointers inside
+ *     i6g_model_desc may be host or device memory (copied with
+ *     hipMemcpyDefault).  All other pointers are host pointers.
+ *   - Every function that takes a `stream` enqueues its GPU work on that HIP
+ *     stream (hipStream_t passed as void*; NULL = the null stream) and
+ *     returns after enqueueing.  Outputs are valid once the stream has
+ *     synchronised.
+ *   - Functions return an i6g_status.  No function aborts the process.  On
+ *     failure i6g_last_error() gives a readable reason (thread-local).
+ *   - All arrays are row-major and densely packed.
+ */
+#ifndef I6G_H
+#define I6G_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  I6G_OK = 0,
+  I6G_EINVAL = -1,        /* invalid argument (shape, range, null pointer) */
+  I6G_ENOMEM = -2,        /* device allocation failed */
+  I6G_EDEVICE = -3,       /* a HIP runtime call failed */
+  I6G_ENONFINITE = -4,    /* a weight row held NaN or Inf */
+  I6G_ETOKEN = -5,        /* a token id outside [0, vocab) */
+  I6G_EUNSUPPORTED = -6,  /* valid but unsupported shape (see each call) */
+  I6G_EBYTES = -7         /* a negative byte count, or zero total bytes */
+} i6g_status;
+
+/* Bits of the device flag word written by kernels (see i6g_quantize_rows and
+ * i6g_model_status). */
+enum { I6G_FLAG_NONFINITE = 1, I6G_FLAG_TOKEN = 2, I6G_FLAG_BYTES = 4 };
+
+enum { I6G_SKIP_NONE = 0, I6G_SKIP_UNET = 1, I6G_SKIP_STEM_TAIL = 2 };
+enum { I6G_DTYPE_F16 = 0, I6G_DTYPE_F32 = 1 };
+
+/*
+ * i6g_quantize_rows -- per-row int8 / int6 quantisation of an fp32 matrix.
+ *
+ * [11L] 训练时的模拟量化 and 后训练量化导出: one scale per row, scale =
+ * c / 127 where c is the row's clipped absolute maximum; codes are
+ * round(w / scale) and, in int6 mode, round(code / 4) * 4 clamped to
+ * [-128, 124] (64 levels in an int8 container); the stored scale is binary16.
+ * [363] Noisy-QAT block: c is floored at 1e-12.
+ *
+ * Exact steps (all binary32, each operation rounded separately):
+ *   c      = s[lo] + f * (s[hi] - s[lo]), s = |w| sorted ascending,
+ *            pos = clip_quantile * (cols - 1) (binary64), lo = floor(pos),
+ *            hi = min(lo + 1, cols - 1), f = (float)(pos - lo);
+ *   c      = max(c, 1e-12f);   scale = c / 127.0f (correctly rounded);
+ *   r      = clamp(w, -c, c) / scale;   k = rint(r) (half to even);
+ *   bits 8: code = clamp(k, -127, 127)
+ *   bits 6: code = clamp(rint(k / 4) * 4, -128, 124)
+ *   scale_f16 = binary16 round-to-nearest-even of scale (subnormals kept).
+ *
+ * w_dev          [rows, cols] fp32, device.
+ * bits           6 or 8.
+ * clip_quantile  in (0, 1]; 1.0 = plain absolute maximum.
+ * codes_dev      [rows, cols] int8 output, device (caller-owned).
+ * scales_dev     [rows] binary16 bit patterns output, device (caller-owned).
+ * flags_dev      optional device int32; I6G_FLAG_NONFINITE is OR-ed in when
+ *                a row holds NaN/Inf (that row's codes are then 0 and its
+ *                scale is the binary16 NaN 0x7e00).  May be NULL.
+ * Errors: I6G_EINVAL for rows/cols < 1, bits not in {6, 8}, quantile out of
+ * (0, 1] or a NULL array; I6G_EUNSUPPORTED if cols - floor(pos) > 8 (the
+ * kernel keeps the 8 largest |w| of a row) or cols > 65536.
+ */
+int i6g_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int bits,
+                      double clip_quantile, int8_t* codes_dev, uint16_t* scales_dev,
+                      int32_t* flags_dev, void* stream);
+
+/* One quantised [out, in] matrix: codes (int8) and per-row binary16 scales. */
+typedef struct {
+  const int8_t* codes;
+  const uint16_t* scales;
+} i6g_matrix;
+
+/* The six matrices of a transformer block, [out, in] each:
+ * q [d, d], k [Hkv*hd, d], v [Hkv*hd, d], o [d, d], fc [d_ff, d],
+ * proj [d, d_ff]. */
+typedef struct {
+  i6g_matrix q, k, v, o, fc, proj;
+} i6g_block;
+
+/*
+ * Model descriptor.  Architecture per [11L] 架构 (GQA attention with RoPE,
+ * ReLU^2 MLP, tied embedding, U-Net skips), [363] (Stem/Core x R/Tail with
+ * stem->tail skips, DepthLoRA on Q/V per effective depth, BigramHash) and
+ * [RM] (parallel attention/MLP lanes, looped layers).
+ *
+ * vocab, d_model, n_heads, n_kv_heads, head_dim, d_ff   model sizes;
+ *     d_model = n_heads * head_dim; n_heads = 2 * n_kv_heads;
+ *     head_dim in {32, 64, 80}; d_model and d_ff multiples of 128.
+ * rope_base          RoPE base (pairs (i, i + hd/2), theta_i = base^(-2i/hd)).
+ * norm_eps           RMSNorm epsilon (no gain).
+ * n_unique, blocks   unique blocks (host array of n_unique i6g_block).
+ * n_eff, schedule    effective depth and the unique block run at each
+ *                    effective layer (host int32 [n_eff]).
+ * embed_dtype, embed tied embedding [vocab, d_model], binary16 or fp32.
+ * skip_kind, n_skip, skip_weights
+ *     I6G_SKIP_UNET: encoder = first n_eff/2 layers push their output;
+ *       decoder layer i < n_eff/2 adds skip_weights[i] * pop() first.
+ *     I6G_SKIP_STEM_TAIL: the first n_skip layers push; the last n_skip
+ *       layers (tail j) add skip_weights[j] * pop() first.
+ *     skip_weights is binary16 [n_skip, d_model].
+ * parallel_residual  1: x += Attn(N(x)) + MLP(N(x)); 0: sequential.
+ * lora_rank, lora_*  rank r (0 = off) and binary16 factors for every
+ *     effective layer: aq [n_eff, r, d], bq [n_eff, d, r],
+ *     av [n_eff, r, d], bv [n_eff, Hkv*hd, r];
+ *     q += (N(x) aq^T) bq^T, v += (N(x) av^T) bv^T.  r <= 8.
+ * bigram_buckets, bigram_dim, bigram_table [buckets, dim], bigram_proj
+ *     [d, dim] (binary16): x0[j] += proj * table[(u[j-1]*1000003 + u[j])
+ *     mod buckets] for window positions j >= 1.  0 buckets = off.
+ */
+typedef struct {
+  int32_t vocab, d_model, n_heads, n_kv_heads, head_dim, d_ff;
+  double rope_base, norm_eps;
+  int32_t n_unique, n_eff;
+  const int32_t* schedule;
+  const i6g_block* blocks;
+  int32_t embed_dtype;
+  const void* embed;
+  int32_t skip_kind, n_skip;
+  const uint16_t* skip_weights;
+  int32_t parallel_residual;
+  int32_t lora_rank;
+  const uint16_t *lora_aq, *lora_bq, *lora_av, *lora_bv;
+  int32_t bigram_buckets, bigram_dim;
+  const uint16_t *bigram_table, *bigram_proj;
+} i6g_model_desc;
+
+typedef struct i6g_model i6g_model; /* opaque, owned by the library */
+
+/*
+ * i6g_load_model -- copy a quantised model into library-owned device memory
+ * on the current HIP device and prepare its constant tables.  The caller may
+ * free everything `desc` points to once the stream has synchronised.
+ * Errors: I6G_EINVAL (inconsistent sizes, bad schedule or skip plan, NULL
+ * tensors), I6G_EUNSUPPORTED (head_dim, head ratio or tile alignment not
+ * supported), I6G_ENOMEM, I6G_EDEVICE.  On error *out is NULL.
+ */
+int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out);
+
+/*
+ * i6g_score_tokens -- sliding-window scoring of a token stream.
+ *
+ * [11L] 滑动窗口评估: windows of `window` tokens every `stride` tokens, each
+ * scored on its last `stride` positions, every token evaluated with up to a
+ * full window of context; the chunked eval is stride == window.
+ * [RM]: the score is bits per byte.
+ *
+ * Exact plan: P = n_tokens - 1 predictions, prediction p predicts
+ * tokens[p+1]; window k has inputs tokens[s_k, e_k) at positions
+ * 0..e_k-s_k-1 with s_k = k*stride, e_k = min(s_k + window, P), and scores
+ * p in [max(s_k, e_{k-1}), e_k) (e_{-1} = 0); K = 1 + ceil((P - window) /
+ * stride) windows (1 if P <= window).  Every prediction is scored once.
+ *
+ * tokens_dev  [n_tokens] int32 token ids, device.
+ * bytes_dev   [n_tokens] int32 byte count of each token, device.
+ * nats_dev    [n_tokens - 1] fp32 output: nats_dev[p] = -ln p(tokens[p+1]).
+ * totals_dev  [4] fp64 output: sum of nats, sum of bytes[1..P], number of
+ *             scored predictions (P), bits per byte = sum_nats / (ln 2 *
+ *             sum_bytes).
+ * Errors (returned now): I6G_EINVAL for n_tokens < 2, window < 1,
+ * stride < 1 or > window, NULL arrays; I6G_ENOMEM; I6G_EDEVICE.
+ * Errors detected on the device (token outside [0, vocab): that token is
+ * read as id 0; negative byte count: counted as 0) are latched in the
+ * model and returned by i6g_model_status().
+ * A model must not be used from two streams at once (its scratch is shared).
+ */
+int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* bytes_dev,
+                     int64_t n_tokens, int32_t window, int32_t stride, float* nats_dev,
+                     double* totals_dev, void* stream);
+
+/* Synchronise `stream`, then return and clear the device-side error latch of
+ * `m`: I6G_ETOKEN, I6G_EBYTES or I6G_OK. */
+int i6g_model_status(i6g_model* m, void* stream);
+
+/* Release a model and its scratch.  NULL is ignored.  The caller must have
+ * synchronised every stream that used it. */
+void i6g_free_model(i6g_model* m);
+
+/* Text of the last failure on this thread ("" if none). */
+const char* i6g_last_error(void);
+
+/*
+ * i6g_plan_windows -- the window plan of i6g_score_tokens, on the host
+ * (no GPU needed).  Writes min(K, capacity) entries of starts/ends/score_from
+ * (each may be NULL) and the window count K to *n_windows.
+ * Errors: I6G_EINVAL as for i6g_score_tokens.
+ */
+int i6g_plan_windows(int64_t n_tokens, int32_t window, int32_t stride, int64_t* n_windows,
+                     int64_t* starts, int64_t* ends, int64_t* score_from, int64_t capacity);
+
+/* Windows processed per batch inside i6g_score_tokens (tuning; default chosen
+ * from the window length).  0 restores the default. */
+int i6g_set_batch_windows(i6g_model* m, int32_t windows);
+
+/* Per-launch kernel timing with HIP events, for measurement.  Kernel
+ * classes: */
+enum {
+  I6G_K_EMBED = 0, I6G_K_QKV = 1, I6G_K_ATTN = 2, I6G_K_OPROJ = 3, I6G_K_FC = 4,
+  I6G_K_PROJ = 5, I6G_K_HEAD = 6, I6G_K_REDUCE = 7, I6G_K_LORA = 8, I6G_K_COUNT = 9
+};
+/* enable != 0 records an event pair around every launch of the classes in
+ * `class_mask` (bit i = class i) in later i6g_score_tokens calls; counters
+ * are reset.  Event timestamps are collected when the stream is synchronised
+ * by i6g_get_timing. */
+int i6g_set_timing(i6g_model* m, int enable, uint32_t class_mask);
+/* Synchronise the timed stream and report, for one kernel class, the summed
+ * launch durations (ms), the number of launches, and the algorithmic FLOPs
+ * and bytes of those launches. */
+int i6g_get_timing(i6g_model* m, int kernel_class, double* total_ms, int64_t* launches,
+                   double* flops, double* bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* I6G_H */

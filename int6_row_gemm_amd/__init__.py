@@ -1,0 +1,270 @@
+"""Python binding of ``libi6g.so``, the int6/int8 per-row scoring library.
+
+Argument marshalling only: every step of the scoring pass runs in the HIP
+kernels behind the C ABI declared in ``include/i6g.h``.  PyTorch provides
+device memory and the current HIP stream.  There is no CPU fallback: if the
+library has not been built, importing the functions below raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libi6g.so")
+
+I6G_OK = 0
+STATUS = {0: "I6G_OK", -1: "I6G_EINVAL", -2: "I6G_ENOMEM", -3: "I6G_EDEVICE",
+          -4: "I6G_ENONFINITE", -5: "I6G_ETOKEN", -6: "I6G_EUNSUPPORTED", -7: "I6G_EBYTES"}
+SKIP_KINDS = {"none": 0, "unet": 1, "stem_tail": 2}
+KERNEL_CLASSES = ["embed", "qkv", "attn", "oproj", "fc", "proj", "head", "reduce", "lora"]
+
+EXPORTED = [
+    "i6g_quantize_rows", "i6g_load_model", "i6g_score_tokens", "i6g_model_status",
+    "i6g_free_model", "i6g_last_error", "i6g_plan_windows", "i6g_set_batch_windows",
+    "i6g_set_timing", "i6g_get_timing",
+]
+
+
+class I6GError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class _Matrix(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class _Block(ctypes.Structure):
+    _fields_ = [(n, _Matrix) for n in ("q", "k", "v", "o", "fc", "proj")]
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [
+        ("vocab", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+        ("rope_base", ctypes.c_double), ("norm_eps", ctypes.c_double),
+        ("n_unique", ctypes.c_int32), ("n_eff", ctypes.c_int32),
+        ("schedule", ctypes.c_void_p), ("blocks", ctypes.c_void_p),
+        ("embed_dtype", ctypes.c_int32), ("embed", ctypes.c_void_p),
+        ("skip_kind", ctypes.c_int32), ("n_skip", ctypes.c_int32), ("skip_weights", ctypes.c_void_p),
+        ("parallel_residual", ctypes.c_int32), ("lora_rank", ctypes.c_int32),
+        ("lora_aq", ctypes.c_void_p), ("lora_bq", ctypes.c_void_p),
+        ("lora_av", ctypes.c_void_p), ("lora_bv", ctypes.c_void_p),
+        ("bigram_buckets", ctypes.c_int32), ("bigram_dim", ctypes.c_int32),
+        ("bigram_table", ctypes.c_void_p), ("bigram_proj", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+        L.i6g_quantize_rows.argtypes = [vp, i64, i64, ctypes.c_int, dbl, vp, vp, vp, vp]
+        L.i6g_load_model.argtypes = [vp, vp, ctypes.POINTER(vp)]
+        L.i6g_score_tokens.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, vp]
+        L.i6g_model_status.argtypes = [vp, vp]
+        L.i6g_free_model.argtypes = [vp]
+        L.i6g_free_model.restype = None
+        L.i6g_last_error.restype = ctypes.c_char_p
+        L.i6g_plan_windows.argtypes = [i64, i32, i32, vp, vp, vp, vp, i64]
+        L.i6g_set_batch_windows.argtypes = [vp, i32]
+        L.i6g_set_timing.argtypes = [vp, ctypes.c_int, ctypes.c_uint32]
+        L.i6g_get_timing.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != I6G_OK:
+        raise I6GError(rc, lib().i6g_last_error().decode())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def plan_windows(n_tokens, window, stride):
+    """Host-side window plan: arrays (starts, ends, score_from)."""
+    n = ctypes.c_int64(0)
+    _check(lib().i6g_plan_windows(n_tokens, window, stride, ctypes.byref(n), None, None, None, 0))
+    K = n.value
+    st, en, sf = (np.zeros(K, np.int64) for _ in range(3))
+    _check(lib().i6g_plan_windows(n_tokens, window, stride, ctypes.byref(n),
+                                  st.ctypes.data, en.ctypes.data, sf.ctypes.data, K))
+    return st, en, sf
+
+
+def quantize_rows(w, bits, clip_quantile, flags=None):
+    """Row-quantise a device fp32 matrix.  Returns (codes int8, scales) where
+    ``scales`` is an int16 tensor holding binary16 bit patterns
+    (``scales.view(torch.float16)`` reads them)."""
+    import torch
+    if not (w.is_cuda and w.dtype == torch.float32 and w.dim() == 2):
+        raise ValueError("w must be a 2-D float32 CUDA tensor")
+    w = w.contiguous()
+    rows, cols = w.shape
+    codes = torch.empty((rows, cols), dtype=torch.int8, device=w.device)
+    scales = torch.empty((rows,), dtype=torch.int16, device=w.device)
+    _check(lib().i6g_quantize_rows(_ptr(w), rows, cols, bits, float(clip_quantile),
+                                   _ptr(codes), _ptr(scales), _ptr(flags), _stream()))
+    return codes, scales
+
+
+def _dev(x, dtype=None):
+    import torch
+    if isinstance(x, np.ndarray):
+        t = torch.from_numpy(np.ascontiguousarray(x))
+    else:
+        t = x
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to("cuda").contiguous()
+
+
+def _f16_bits(x):
+    import torch
+    if isinstance(x, np.ndarray):
+        x = np.ascontiguousarray(x.astype(np.float16)).view(np.int16)
+        return _dev(x)
+    return _dev(x.to(torch.float16).view(torch.int16))
+
+
+class Model:
+    """A model loaded into library-owned device memory.
+
+    ``arch`` uses the keys of the synthetic configurations (vocab, d_model,
+    n_heads, n_kv_heads, head_dim, d_ff, rope_base, norm_eps, schedule,
+    skip_kind, n_skip, parallel, lora_rank, bigram_buckets, bigram_dim,
+    embed_dtype).  ``qblocks`` is a list of dicts name -> (codes, scales)
+    for q, k, v, o, fc, proj (device or host tensors / arrays)."""
+
+    def __init__(self, arch, qblocks, embed, skip_w=None, lora=None, bigram=None):
+        import torch
+        keep = []
+        blocks = (_Block * len(qblocks))()
+        for i, qb in enumerate(qblocks):
+            for name in ("q", "k", "v", "o", "fc", "proj"):
+                c, s = qb[name]
+                c = _dev(c, torch.int8)
+                s = _dev(s) if not isinstance(s, np.ndarray) else _dev(s.view(np.int16))
+                keep += [c, s]
+                setattr(blocks[i], name, _Matrix(c.data_ptr(), s.data_ptr()))
+        sched = (ctypes.c_int32 * len(arch["schedule"]))(*arch["schedule"])
+        f32 = arch.get("embed_dtype", "fp16") == "fp32"
+        emb = _dev(embed, torch.float32) if f32 else _f16_bits(embed)
+        keep.append(emb)
+        d = _Desc()
+        d.vocab, d.d_model = arch["vocab"], arch["d_model"]
+        d.n_heads, d.n_kv_heads, d.head_dim = arch["n_heads"], arch["n_kv_heads"], arch["head_dim"]
+        d.d_ff = arch["d_ff"]
+        d.rope_base, d.norm_eps = float(arch["rope_base"]), float(arch["norm_eps"])
+        d.n_unique, d.n_eff = len(qblocks), len(arch["schedule"])
+        d.schedule = ctypes.cast(sched, ctypes.c_void_p)
+        d.blocks = ctypes.cast(blocks, ctypes.c_void_p)
+        d.embed_dtype = 1 if f32 else 0
+        d.embed = emb.data_ptr()
+        kind = arch.get("skip_kind", "none")
+        d.skip_kind = SKIP_KINDS[kind] if isinstance(kind, str) else int(kind)
+        d.n_skip = arch.get("n_skip", 0)
+        if skip_w is not None and d.skip_kind != 0:
+            sw = _f16_bits(skip_w); keep.append(sw); d.skip_weights = sw.data_ptr()
+        d.parallel_residual = int(bool(arch.get("parallel", False)))
+        d.lora_rank = arch.get("lora_rank", 0) if lora is not None else 0
+        if d.lora_rank:
+            for n in ("aq", "bq", "av", "bv"):
+                t = _f16_bits(lora[n]); keep.append(t); setattr(d, "lora_" + n, t.data_ptr())
+        if bigram is not None and arch.get("bigram_buckets", 0) > 0:
+            d.bigram_buckets, d.bigram_dim = arch["bigram_buckets"], arch["bigram_dim"]
+            t1, t2 = _f16_bits(bigram["table"]), _f16_bits(bigram["proj"])
+            keep += [t1, t2]
+            d.bigram_table, d.bigram_proj = t1.data_ptr(), t2.data_ptr()
+        torch.cuda.synchronize()
+        h = ctypes.c_void_p(0)
+        _check(lib().i6g_load_model(ctypes.byref(d), _stream(), ctypes.byref(h)))
+        torch.cuda.synchronize()
+        self._h = h
+        self.arch = dict(arch)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and h.value and _lib is not None:
+            _lib.i6g_free_model(h)
+            self._h = None
+
+    def set_batch_windows(self, n):
+        _check(lib().i6g_set_batch_windows(self._h, n))
+
+    def score(self, tokens, nbytes, window, stride, nats=None, totals=None, check=True):
+        """Score a device token stream; returns (nats [N-1] fp32, totals [4] fp64)
+        with totals = (sum nats, sum bytes, scored predictions, bits per byte)."""
+        import torch
+        tokens = _dev(tokens, torch.int32)
+        nbytes = _dev(nbytes, torch.int32)
+        n = tokens.numel()
+        if nbytes.numel() != n:
+            raise ValueError("tokens and byte counts differ in length")
+        if nats is None:
+            nats = torch.empty(max(n - 1, 0), dtype=torch.float32, device=tokens.device)
+        if totals is None:
+            totals = torch.empty(4, dtype=torch.float64, device=tokens.device)
+        _check(lib().i6g_score_tokens(self._h, _ptr(tokens), _ptr(nbytes), n, window, stride,
+                                      _ptr(nats), _ptr(totals), _stream()))
+        if check:
+            self.status()
+        return nats, totals
+
+    def status(self):
+        """Synchronise and raise on a device-side error (bad token or bytes)."""
+        _check(lib().i6g_model_status(self._h, _stream()))
+
+    def set_timing(self, enable, classes=None):
+        mask = 0
+        for c in (classes or KERNEL_CLASSES):
+            mask |= 1 << KERNEL_CLASSES.index(c)
+        _check(lib().i6g_set_timing(self._h, int(enable), mask))
+
+    def timing(self, cls):
+        """(total_ms, launches, flops, bytes) for one kernel class."""
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        fl, by = ctypes.c_double(), ctypes.c_double()
+        _check(lib().i6g_get_timing(self._h, KERNEL_CLASSES.index(cls), ctypes.byref(ms),
+                                    ctypes.byref(n), ctypes.byref(fl), ctypes.byref(by)))
+        return ms.value, n.value, fl.value, by.value
+
+
+def quantize_model(model, flags=None):
+    """Quantise every block matrix of a synthetic model on the GPU; returns
+    a list of dicts name -> (codes, scales) of device tensors."""
+    import torch
+    arch = model["arch"]
+    out = []
+    for blk in model["blocks"]:
+        qb = {}
+        for name, w in blk.items():
+            wt = _dev(w, torch.float32)
+            qb[name] = quantize_rows(wt, arch["bits"], arch["clip_q"], flags)
+        out.append(qb)
+    return out
+
+
+def load(model, qblocks):
+    """Load a synthetic model dict with the given quantised blocks."""
+    return Model(model["arch"], qblocks, model["embed"], model.get("skip_w"),
+                 model.get("lora"), model.get("bigram"))

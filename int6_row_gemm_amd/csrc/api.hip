@@ -1,0 +1,591 @@
+// C ABI of the scoring library: argument validation, model loading, the
+// block-schedule driver and the sliding-window batch loop.
+//
+// Block schedule (pwwt.cn "parameter-golf 16MB 极限压缩实战 …", 架构: U-Net
+// skips -- encoder outputs pushed on a stack, decoder layers pop them in
+// reverse and add skip_weights[i] * skip; kwkr.cn PR #363 write-up:
+// Stem -> Core x R -> Tail with stem outputs added to tail inputs with
+// learned weights; pigsec.cn README mirror: looped layers and parallel
+// attention/MLP lanes): the host walks the effective layers, runs the unique
+// block each one names, and fuses every push and pop into the epilogue of the
+// GEMM that produces the layer's output.
+#include "../../include/i6g.h"
+#include "common.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+using namespace i6g;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                 \
+  do {                                                                                \
+    hipError_t e_ = (expr);                                                           \
+    if (e_ != hipSuccess)                                                             \
+      return fail(e_ == hipErrorOutOfMemory ? I6G_ENOMEM : I6G_EDEVICE, "%s: %s (%s)", \
+                  #expr, hipGetErrorString(e_), __func__);                            \
+  } while (0)
+
+struct DevBuf {
+  void* p = nullptr;
+  size_t bytes = 0;
+  ~DevBuf() { release(); }
+  void release() {
+    if (p) (void)hipFree(p);
+    p = nullptr;
+    bytes = 0;
+  }
+  hipError_t ensure(size_t n) {
+    if (n <= bytes && p) return hipSuccess;
+    release();
+    hipError_t e = hipMalloc(&p, n ? n : 1);
+    if (e == hipSuccess) bytes = n;
+    else p = nullptr;
+    return e;
+  }
+  template <class T> T* as() const { return reinterpret_cast<T*>(p); }
+};
+
+struct BlockDev {
+  DevBuf qkv_codes, qkv_scales, o_codes, o_scales, fc_codes, fc_scales, proj_codes, proj_scales;
+};
+
+struct TimeRec {
+  int cls;
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+
+int64_t window_count(int64_t P, int64_t L, int64_t S) {
+  return (P <= L) ? 1 : 1 + (P - L + S - 1) / S;
+}
+
+int64_t window_end(int64_t k, int64_t P, int64_t L, int64_t S) {
+  return std::min(k * S + L, P);
+}
+
+}  // namespace
+
+struct i6g_model {
+  // architecture
+  int V, d, Hq, Hkv, hd, F, kvd, nqkv;
+  double rope_base, eps;
+  int n_unique, n_eff;
+  std::vector<int> schedule, push_after, pop_before, pop_slot, push_slot;
+  int max_depth = 0;
+  int skip_kind, n_skip, parallel, lora_r, buckets, bigram_dim, embed_f32;
+  int device = 0;
+  // weights
+  std::vector<BlockDev> blocks;
+  DevBuf embed, embed16, skip_w, lora_aq, lora_bq, lora_av, lora_bv, bigram;
+  // tables and scratch
+  DevBuf rope;
+  int rope_L = 0;
+  DevBuf x, xb, ss, q, k, vt, o, h, slots, lora_u, flags, part_n, part_b;
+  int64_t scratch_rows = 0;
+  int batch_windows = 0;
+  // timing
+  bool timing = false;
+  uint32_t timing_mask = 0;
+  std::vector<hipEvent_t> pool;
+  std::vector<TimeRec> recs;
+  hipStream_t timed_stream = nullptr;
+  double t_ms[I6G_K_COUNT] = {}, t_flops[I6G_K_COUNT] = {}, t_bytes[I6G_K_COUNT] = {};
+  int64_t t_n[I6G_K_COUNT] = {};
+
+  hipEvent_t take_event() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  ~i6g_model() {
+    for (auto& r : recs) { pool.push_back(r.a); pool.push_back(r.b); }
+    for (auto e : pool) (void)hipEventDestroy(e);
+  }
+};
+
+namespace {
+
+// Wrap a launch with an event pair when timing is on for its class.
+template <class F>
+int timed(i6g_model* m, int cls, hipStream_t s, double flops, double bytes, F&& launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  const bool on = m->timing && (m->timing_mask >> cls & 1u);
+  if (on) {
+    a = m->take_event();
+    b = m->take_event();
+    if (!a || !b) return fail(I6G_EDEVICE, "hipEventCreate failed");
+    HIP_TRY(hipEventRecord(a, s));
+  }
+  hipError_t e = launch();
+  if (e != hipSuccess) return fail(I6G_EDEVICE, "kernel launch (class %d): %s", cls, hipGetErrorString(e));
+  if (on) {
+    HIP_TRY(hipEventRecord(b, s));
+    m->recs.push_back(TimeRec{cls, a, b, flops, bytes});
+    m->timed_stream = s;
+  }
+  return I6G_OK;
+}
+
+int copy_in(DevBuf& dst, const void* src, size_t bytes, hipStream_t s) {
+  HIP_TRY(dst.ensure(bytes));
+  HIP_TRY(hipMemcpyAsync(dst.p, src, bytes, hipMemcpyDefault, s));
+  return I6G_OK;
+}
+
+int build_plan(i6g_model* m) {
+  const int ne = m->n_eff;
+  m->push_after.assign(ne, 0);
+  m->pop_before.assign(ne, -1);
+  if (m->skip_kind == I6G_SKIP_UNET) {
+    const int n_enc = ne / 2;
+    if (m->n_skip != n_enc)
+      return fail(I6G_EINVAL, "U-Net with %d effective layers needs %d skip weights, got %d", ne, n_enc,
+                  m->n_skip);
+    for (int e = 0; e < n_enc; ++e) m->push_after[e] = 1;
+    for (int i = 0; i < n_enc; ++i) m->pop_before[n_enc + i] = i;
+  } else if (m->skip_kind == I6G_SKIP_STEM_TAIL) {
+    const int n = m->n_skip;
+    if (n < 1 || 2 * n > ne) return fail(I6G_EINVAL, "stem/tail skips: n_skip=%d with n_eff=%d", n, ne);
+    for (int e = 0; e < n; ++e) m->push_after[e] = 1;
+    for (int j = 0; j < n; ++j) m->pop_before[ne - n + j] = j;
+  } else if (m->skip_kind != I6G_SKIP_NONE) {
+    return fail(I6G_EINVAL, "unknown skip_kind %d", m->skip_kind);
+  }
+  // Resolve the LIFO stack into slot indices.
+  m->push_slot.assign(ne, -1);
+  m->pop_slot.assign(ne, -1);
+  int depth = 0;
+  m->max_depth = 0;
+  for (int e = 0; e < ne; ++e) {
+    if (m->pop_before[e] >= 0) {
+      if (depth == 0) return fail(I6G_EINVAL, "skip pop before layer %d with an empty stack", e);
+      m->pop_slot[e] = --depth;
+    }
+    if (m->push_after[e]) {
+      m->push_slot[e] = depth++;
+      m->max_depth = std::max(m->max_depth, depth);
+    }
+  }
+  if (m->pop_before[0] >= 0) return fail(I6G_EINVAL, "pop before the first layer");
+  return I6G_OK;
+}
+
+int ensure_scratch(i6g_model* m, int W, int Lp, hipStream_t s) {
+  const int64_t M = (int64_t)W * Lp;
+  if (M > m->scratch_rows) {
+    const int nt = m->d / 128;
+    HIP_TRY(m->x.ensure(M * m->d * 4));
+    HIP_TRY(m->xb.ensure(M * m->d * 2));
+    HIP_TRY(m->ss.ensure(M * nt * 4));
+    HIP_TRY(m->q.ensure(M * m->d * 2));
+    HIP_TRY(m->k.ensure(M * m->kvd * 2));
+    HIP_TRY(m->vt.ensure(M * m->kvd * 2));
+    HIP_TRY(m->o.ensure(M * m->d * 2));
+    HIP_TRY(m->h.ensure(M * m->F * 2));
+    if (m->max_depth > 0) HIP_TRY(m->slots.ensure((size_t)m->max_depth * M * m->d * 4));
+    if (m->lora_r > 0) HIP_TRY(m->lora_u.ensure(M * 2 * m->lora_r * 4));
+    m->scratch_rows = M;
+  }
+  if (Lp > m->rope_L) {
+    HIP_TRY(m->rope.ensure((size_t)Lp * (m->hd / 2) * sizeof(float2)));
+    HIP_TRY(launch_rope_table(m->rope.as<float2>(), Lp, m->hd, m->rope_base, s));
+    m->rope_L = Lp;
+  }
+  return I6G_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* i6g_last_error(void) { return g_err.c_str(); }
+
+int i6g_plan_windows(int64_t n_tokens, int32_t window, int32_t stride, int64_t* n_windows,
+                     int64_t* starts, int64_t* ends, int64_t* score_from, int64_t capacity) {
+  if (n_tokens < 2 || window < 1 || stride < 1 || stride > window || !n_windows)
+    return fail(I6G_EINVAL, "plan_windows: need n_tokens >= 2, 1 <= stride <= window");
+  const int64_t P = n_tokens - 1;
+  const int64_t K = window_count(P, window, stride);
+  *n_windows = K;
+  int64_t e_prev = 0;
+  for (int64_t k = 0; k < K && k < capacity; ++k) {
+    const int64_t s = k * stride, e = window_end(k, P, window, stride);
+    if (starts) starts[k] = s;
+    if (ends) ends[k] = e;
+    if (score_from) score_from[k] = std::max(s, e_prev);
+    e_prev = e;
+  }
+  return I6G_OK;
+}
+
+int i6g_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int bits, double clip_quantile,
+                      int8_t* codes_dev, uint16_t* scales_dev, int32_t* flags_dev, void* stream) {
+  if (!w_dev || !codes_dev || !scales_dev) return fail(I6G_EINVAL, "quantize_rows: NULL array");
+  if (rows < 1 || cols < 1) return fail(I6G_EINVAL, "quantize_rows: rows and cols must be >= 1");
+  if (bits != 6 && bits != 8) return fail(I6G_EINVAL, "quantize_rows: bits must be 6 or 8");
+  if (!(clip_quantile > 0.0 && clip_quantile <= 1.0))
+    return fail(I6G_EINVAL, "quantize_rows: clip_quantile must be in (0, 1]");
+  if (cols > 65536) return fail(I6G_EUNSUPPORTED, "quantize_rows: cols > 65536");
+  const double pos = clip_quantile * (double)(cols - 1);
+  const int64_t lo = (int64_t)floor(pos);
+  const int64_t topk = cols - lo;
+  if (topk > 8)
+    return fail(I6G_EUNSUPPORTED, "quantize_rows: quantile needs the %lld largest values (max 8)",
+                (long long)topk);
+  QuantArgs a{};
+  a.w = w_dev;
+  a.codes = codes_dev;
+  a.scales = scales_dev;
+  a.flags = flags_dev;
+  a.rows = rows;
+  a.cols = (int32_t)cols;
+  a.bits = bits;
+  a.topk = (int32_t)topk;
+  a.frac = (float)(pos - (double)lo);
+  HIP_TRY(launch_quantize(a, (hipStream_t)stream));
+  return I6G_OK;
+}
+
+int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
+  if (!out) return fail(I6G_EINVAL, "load_model: out is NULL");
+  *out = nullptr;
+  if (!desc) return fail(I6G_EINVAL, "load_model: desc is NULL");
+  const i6g_model_desc& D = *desc;
+  hipStream_t s = (hipStream_t)stream;
+  if (D.vocab < 16 || D.vocab % 16 || D.d_model < 128 || D.n_heads < 1 || D.n_kv_heads < 1 ||
+      D.head_dim < 1 || D.d_ff < 128 || D.n_unique < 1 || D.n_eff < 1 || !D.schedule || !D.blocks ||
+      !D.embed)
+    return fail(I6G_EINVAL, "load_model: bad sizes or NULL tensors");
+  if (D.n_heads * D.head_dim != D.d_model)
+    return fail(I6G_EINVAL, "load_model: n_heads * head_dim != d_model");
+  if (D.head_dim != 32 && D.head_dim != 64 && D.head_dim != 80)
+    return fail(I6G_EUNSUPPORTED, "load_model: head_dim %d (supported: 32, 64, 80)", D.head_dim);
+  if (D.n_heads != 2 * D.n_kv_heads)
+    return fail(I6G_EUNSUPPORTED, "load_model: needs n_heads == 2 * n_kv_heads");
+  if (D.d_model % 128 || D.d_ff % 128 || D.d_model > 640)
+    return fail(I6G_EUNSUPPORTED, "load_model: d_model and d_ff must be multiples of 128, d_model <= 640");
+  if (D.embed_dtype != I6G_DTYPE_F16 && D.embed_dtype != I6G_DTYPE_F32)
+    return fail(I6G_EINVAL, "load_model: embed_dtype");
+  if (D.lora_rank < 0 || D.lora_rank > 8) return fail(I6G_EINVAL, "load_model: lora_rank must be 0..8");
+  if (D.lora_rank > 0 && (!D.lora_aq || !D.lora_bq || !D.lora_av || !D.lora_bv))
+    return fail(I6G_EINVAL, "load_model: LoRA factors missing");
+  if (D.bigram_buckets < 0 || (D.bigram_buckets > 0 && (D.bigram_dim < 1 || !D.bigram_table || !D.bigram_proj)))
+    return fail(I6G_EINVAL, "load_model: bigram tensors");
+  if (D.skip_kind != I6G_SKIP_NONE && (D.n_skip < 1 || !D.skip_weights))
+    return fail(I6G_EINVAL, "load_model: skip weights missing");
+  for (int e = 0; e < D.n_eff; ++e)
+    if (D.schedule[e] < 0 || D.schedule[e] >= D.n_unique)
+      return fail(I6G_EINVAL, "load_model: schedule[%d] = %d out of range", e, D.schedule[e]);
+
+  i6g_model* m = new i6g_model();
+  m->V = D.vocab; m->d = D.d_model; m->Hq = D.n_heads; m->Hkv = D.n_kv_heads; m->hd = D.head_dim;
+  m->F = D.d_ff; m->kvd = D.n_kv_heads * D.head_dim; m->nqkv = m->d + 2 * m->kvd;
+  m->rope_base = D.rope_base; m->eps = D.norm_eps;
+  m->n_unique = D.n_unique; m->n_eff = D.n_eff;
+  m->schedule.assign(D.schedule, D.schedule + D.n_eff);
+  m->skip_kind = D.skip_kind; m->n_skip = D.skip_kind == I6G_SKIP_NONE ? 0 : D.n_skip;
+  m->parallel = D.parallel_residual != 0; m->lora_r = D.lora_rank;
+  m->buckets = D.bigram_buckets; m->bigram_dim = D.bigram_dim;
+  m->embed_f32 = D.embed_dtype == I6G_DTYPE_F32;
+  (void)hipGetDevice(&m->device);
+
+  int rc = build_plan(m);
+  if (rc != I6G_OK) { delete m; return rc; }
+
+  auto cleanup = [&](int code) { delete m; return code; };
+  const int d = m->d, F = m->F, kvd = m->kvd;
+  m->blocks.resize(m->n_unique);
+  for (int b = 0; b < m->n_unique; ++b) {
+    const i6g_block& B = D.blocks[b];
+    const i6g_matrix* mats[6] = {&B.q, &B.k, &B.v, &B.o, &B.fc, &B.proj};
+    for (auto* mt : mats)
+      if (!mt->codes || !mt->scales) return cleanup(fail(I6G_EINVAL, "load_model: block %d has a NULL matrix", b));
+    BlockDev& bd = m->blocks[b];
+    if (bd.qkv_codes.ensure((size_t)m->nqkv * d) != hipSuccess ||
+        bd.qkv_scales.ensure((size_t)m->nqkv * 2) != hipSuccess)
+      return cleanup(fail(I6G_ENOMEM, "load_model: out of device memory"));
+    int8_t* qc = bd.qkv_codes.as<int8_t>();
+    uint16_t* qs = bd.qkv_scales.as<uint16_t>();
+    if (hipMemcpyAsync(qc, B.q.codes, (size_t)d * d, hipMemcpyDefault, s) != hipSuccess ||
+        hipMemcpyAsync(qc + (size_t)d * d, B.k.codes, (size_t)kvd * d, hipMemcpyDefault, s) != hipSuccess ||
+        hipMemcpyAsync(qc + (size_t)(d + kvd) * d, B.v.codes, (size_t)kvd * d, hipMemcpyDefault, s) != hipSuccess ||
+        hipMemcpyAsync(qs, B.q.scales, (size_t)d * 2, hipMemcpyDefault, s) != hipSuccess ||
+        hipMemcpyAsync(qs + d, B.k.scales, (size_t)kvd * 2, hipMemcpyDefault, s) != hipSuccess ||
+        hipMemcpyAsync(qs + d + kvd, B.v.scales, (size_t)kvd * 2, hipMemcpyDefault, s) != hipSuccess)
+      return cleanup(fail(I6G_EDEVICE, "load_model: copy of q/k/v failed"));
+    if ((rc = copy_in(bd.o_codes, B.o.codes, (size_t)d * d, s)) ||
+        (rc = copy_in(bd.o_scales, B.o.scales, (size_t)d * 2, s)) ||
+        (rc = copy_in(bd.fc_codes, B.fc.codes, (size_t)F * d, s)) ||
+        (rc = copy_in(bd.fc_scales, B.fc.scales, (size_t)F * 2, s)) ||
+        (rc = copy_in(bd.proj_codes, B.proj.codes, (size_t)d * F, s)) ||
+        (rc = copy_in(bd.proj_scales, B.proj.scales, (size_t)d * 2, s)))
+      return cleanup(rc);
+  }
+  const size_t esz = m->embed_f32 ? 4 : 2;
+  if ((rc = copy_in(m->embed, D.embed, (size_t)m->V * d * esz, s))) return cleanup(rc);
+  if (m->embed_f32) {
+    if (m->embed16.ensure((size_t)m->V * d * 2) != hipSuccess) return cleanup(fail(I6G_ENOMEM, "embed16"));
+    if (launch_f32_to_f16(m->embed.as<float>(), m->embed16.as<_Float16>(), (int64_t)m->V * d, s) != hipSuccess)
+      return cleanup(fail(I6G_EDEVICE, "embedding conversion failed"));
+  }
+  DevBuf tmp;
+  auto f16_in = [&](DevBuf& dst, const uint16_t* src, int64_t n) -> int {
+    int r = copy_in(tmp, src, (size_t)n * 2, s);
+    if (r) return r;
+    if (dst.ensure((size_t)n * 4) != hipSuccess) return fail(I6G_ENOMEM, "out of device memory");
+    if (launch_f16_to_f32(tmp.as<uint16_t>(), dst.as<float>(), n, s) != hipSuccess)
+      return fail(I6G_EDEVICE, "f16 conversion failed");
+    if (hipStreamSynchronize(s) != hipSuccess) return fail(I6G_EDEVICE, "sync failed");
+    return I6G_OK;
+  };
+  if (m->n_skip > 0 && (rc = f16_in(m->skip_w, D.skip_weights, (int64_t)m->n_skip * d))) return cleanup(rc);
+  if (m->lora_r > 0) {
+    const int64_t ne = m->n_eff, r = m->lora_r;
+    if ((rc = f16_in(m->lora_aq, D.lora_aq, ne * r * d)) || (rc = f16_in(m->lora_bq, D.lora_bq, ne * d * r)) ||
+        (rc = f16_in(m->lora_av, D.lora_av, ne * r * d)) || (rc = f16_in(m->lora_bv, D.lora_bv, ne * kvd * r)))
+      return cleanup(rc);
+  }
+  if (m->buckets > 0) {
+    DevBuf t2;
+    if ((rc = copy_in(tmp, D.bigram_table, (size_t)m->buckets * m->bigram_dim * 2, s)) ||
+        (rc = copy_in(t2, D.bigram_proj, (size_t)d * m->bigram_dim * 2, s)))
+      return cleanup(rc);
+    if (m->bigram.ensure((size_t)m->buckets * d * 4) != hipSuccess) return cleanup(fail(I6G_ENOMEM, "bigram"));
+    if (launch_bigram_table(tmp.as<uint16_t>(), t2.as<uint16_t>(), m->bigram.as<float>(), m->buckets,
+                            m->bigram_dim, d, s) != hipSuccess)
+      return cleanup(fail(I6G_EDEVICE, "bigram table kernel failed"));
+    if (hipStreamSynchronize(s) != hipSuccess) return cleanup(fail(I6G_EDEVICE, "sync failed"));
+  }
+  if (m->flags.ensure(4) != hipSuccess || m->part_n.ensure(256 * 8) != hipSuccess ||
+      m->part_b.ensure(256 * 8) != hipSuccess)
+    return cleanup(fail(I6G_ENOMEM, "out of device memory"));
+  if (hipMemsetAsync(m->flags.p, 0, 4, s) != hipSuccess) return cleanup(fail(I6G_EDEVICE, "memset"));
+  if (hipStreamSynchronize(s) != hipSuccess) return cleanup(fail(I6G_EDEVICE, "sync failed"));
+  *out = m;
+  return I6G_OK;
+}
+
+void i6g_free_model(i6g_model* m) { delete m; }
+
+int i6g_set_batch_windows(i6g_model* m, int32_t windows) {
+  if (!m || windows < 0) return fail(I6G_EINVAL, "set_batch_windows");
+  m->batch_windows = windows;
+  return I6G_OK;
+}
+
+int i6g_model_status(i6g_model* m, void* stream) {
+  if (!m) return fail(I6G_EINVAL, "model_status: NULL model");
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+  int32_t f = 0;
+  HIP_TRY(hipMemcpy(&f, m->flags.p, 4, hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemset(m->flags.p, 0, 4));
+  if (f & I6G_FLAG_TOKEN) return fail(I6G_ETOKEN, "a token id was outside [0, vocab)");
+  if (f & I6G_FLAG_BYTES) return fail(I6G_EBYTES, "negative byte count or zero total bytes");
+  return I6G_OK;
+}
+
+int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* bytes_dev, int64_t n_tokens,
+                     int32_t window, int32_t stride, float* nats_dev, double* totals_dev, void* stream) {
+  if (!m) return fail(I6G_EINVAL, "score_tokens: NULL model");
+  if (!tokens_dev || !bytes_dev || !nats_dev || !totals_dev) return fail(I6G_EINVAL, "score_tokens: NULL array");
+  if (n_tokens < 2 || window < 1 || stride < 1 || stride > window)
+    return fail(I6G_EINVAL, "score_tokens: need n_tokens >= 2 and 1 <= stride <= window");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t P = n_tokens - 1;
+  const int64_t L = window, S = stride;
+  const int64_t K = window_count(P, L, S);
+  const int Lp = (int)((std::min<int64_t>(L, P) + 63) / 64 * 64);
+  int Wb = m->batch_windows > 0 ? m->batch_windows : std::max(1, 32768 / Lp);
+  Wb = (int)std::min<int64_t>(Wb, K);
+  int rc = ensure_scratch(m, Wb, Lp, s);
+  if (rc) return rc;
+
+  const int d = m->d, F = m->F, kvd = m->kvd, nt = d / 128;
+  const float eps = (float)m->eps;
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)m->hd));
+  const int64_t e0 = window_end(0, P, L, S);
+
+  for (int64_t k0 = 0; k0 < K; k0 += Wb) {
+    const int W = (int)std::min<int64_t>(Wb, K - k0);
+    const int M = W * Lp;
+    // real rows of this batch (for algorithmic FLOP counts)
+    double real_rows = 0, attn_pairs = 0;
+    for (int64_t k = k0; k < k0 + W; ++k) {
+      double T = (double)(window_end(k, P, L, S) - k * S);
+      real_rows += T;
+      attn_pairs += T * (T + 1) / 2;
+    }
+
+    EmbedArgs ea{};
+    ea.tokens = tokens_dev; ea.n_tokens = n_tokens; ea.P = P; ea.k0 = k0;
+    ea.W = W; ea.Lp = Lp; ea.L = (int32_t)L; ea.S = (int32_t)S;
+    ea.embed = m->embed.p; ea.embed_f32 = m->embed_f32;
+    ea.bigram = m->buckets > 0 ? m->bigram.as<float>() : nullptr; ea.buckets = m->buckets;
+    ea.vocab = m->V; ea.d = d; ea.nt = nt;
+    ea.x = m->x.as<float>(); ea.xb = m->xb.as<bf16>(); ea.ss = m->ss.as<float>();
+    ea.flags = m->flags.as<int32_t>();
+    if ((rc = timed(m, I6G_K_EMBED, s, 0.0, real_rows * d * 6.0, [&] { return launch_embed(ea, s); })))
+      return rc;
+
+    for (int e = 0; e < m->n_eff; ++e) {
+      const BlockDev& B = m->blocks[m->schedule[e]];
+      const bool last = (e + 1 == m->n_eff);
+      if (m->lora_r > 0) {
+        LoraArgs la{};
+        la.x = m->x.as<float>(); la.M = M; la.d = d; la.r = m->lora_r; la.eps = eps;
+        la.aq = m->lora_aq.as<float>() + (size_t)e * m->lora_r * d;
+        la.av = m->lora_av.as<float>() + (size_t)e * m->lora_r * d;
+        la.u = m->lora_u.as<float>();
+        if ((rc = timed(m, I6G_K_LORA, s, 4.0 * real_rows * m->lora_r * d, real_rows * d * 4.0,
+                        [&] { return launch_lora_down(la, s); })))
+          return rc;
+      }
+      GemmArgs g{};
+      g.A = m->xb.as<bf16>(); g.B = B.qkv_codes.as<int8_t>(); g.scale = B.qkv_scales.as<uint16_t>();
+      g.M = M; g.N = m->nqkv; g.K = d; g.ss_in = m->ss.as<float>(); g.nt_in = nt; g.eps = eps;
+      g.q = m->q.as<bf16>(); g.k = m->k.as<bf16>(); g.vt = m->vt.as<bf16>();
+      g.n_heads = m->Hq; g.n_kv = m->Hkv; g.hd = m->hd; g.Lp = Lp; g.rope = m->rope.as<float2>();
+      if (m->lora_r > 0) {
+        g.lora_u = m->lora_u.as<float>(); g.lora_r = m->lora_r;
+        g.lora_bq = m->lora_bq.as<float>() + (size_t)e * d * m->lora_r;
+        g.lora_bv = m->lora_bv.as<float>() + (size_t)e * kvd * m->lora_r;
+      }
+      const double fl_qkv = 2.0 * real_rows * m->nqkv * d;
+      if ((rc = timed(m, I6G_K_QKV, s, fl_qkv, real_rows * (2.0 * d + 2.0 * m->nqkv) + (double)m->nqkv * d,
+                      [&] { return launch_gemm(EPI_QKV, g, s); })))
+        return rc;
+
+      AttnArgs at{};
+      at.q = m->q.as<bf16>(); at.k = m->k.as<bf16>(); at.vt = m->vt.as<bf16>(); at.o = m->o.as<bf16>();
+      at.W = W; at.n_heads = m->Hq; at.n_kv = m->Hkv; at.hd = m->hd; at.Lp = Lp; at.scale_log2 = scale_log2;
+      if ((rc = timed(m, I6G_K_ATTN, s, 4.0 * m->hd * m->Hq * attn_pairs,
+                      real_rows * (2.0 * d + 4.0 * kvd),
+                      [&] { return launch_attention(at, s); })))
+        return rc;
+
+      // attention output projection, residual add
+      GemmArgs go{};
+      go.A = m->o.as<bf16>(); go.B = B.o_codes.as<int8_t>(); go.scale = B.o_scales.as<uint16_t>();
+      go.M = M; go.N = d; go.K = d; go.x = m->x.as<float>();
+      if (!m->parallel) { go.xb = m->xb.as<bf16>(); go.ss_out = m->ss.as<float>(); }
+
+      GemmArgs gf{};
+      gf.A = m->xb.as<bf16>(); gf.B = B.fc_codes.as<int8_t>(); gf.scale = B.fc_scales.as<uint16_t>();
+      gf.M = M; gf.N = F; gf.K = d; gf.ss_in = m->ss.as<float>(); gf.nt_in = nt; gf.eps = eps;
+      gf.h = m->h.as<bf16>();
+
+      GemmArgs gp{};
+      gp.A = m->h.as<bf16>(); gp.B = B.proj_codes.as<int8_t>(); gp.scale = B.proj_scales.as<uint16_t>();
+      gp.M = M; gp.N = d; gp.K = F; gp.x = m->x.as<float>();
+      if (!last) { gp.xb = m->xb.as<bf16>(); gp.ss_out = m->ss.as<float>(); }
+      if (m->push_after[e]) gp.push_dst = m->slots.as<float>() + (size_t)m->push_slot[e] * M * d;
+      if (!last && m->pop_before[e + 1] >= 0) {
+        gp.pop_src = m->slots.as<float>() + (size_t)m->pop_slot[e + 1] * M * d;
+        gp.pop_w = m->skip_w.as<float>() + (size_t)m->pop_before[e + 1] * d;
+      }
+
+      const double fl_o = 2.0 * real_rows * d * d, fl_fc = 2.0 * real_rows * F * d;
+      const double by_o = real_rows * (2.0 * d + 4.0 * d * 2 + 2.0 * d) + (double)d * d;
+      const double by_fc = real_rows * (2.0 * d + 2.0 * F) + (double)F * d;
+      const double by_p = real_rows * (2.0 * F + 4.0 * d * 2 + 2.0 * d) + (double)F * d;
+      auto run_o = [&] {
+        return timed(m, I6G_K_OPROJ, s, fl_o, by_o, [&] { return launch_gemm(EPI_RES, go, s); });
+      };
+      auto run_fc = [&] {
+        return timed(m, I6G_K_FC, s, fl_fc, by_fc, [&] { return launch_gemm(EPI_RELU2, gf, s); });
+      };
+      if (m->parallel) {
+        if ((rc = run_fc()) || (rc = run_o())) return rc;
+      } else {
+        if ((rc = run_o()) || (rc = run_fc())) return rc;
+      }
+      if ((rc = timed(m, I6G_K_PROJ, s, fl_fc, by_p, [&] { return launch_gemm(EPI_RES, gp, s); })))
+        return rc;
+    }
+
+    HeadArgs ha{};
+    ha.x = m->x.as<float>();
+    ha.E = m->embed_f32 ? m->embed16.as<_Float16>() : m->embed.as<_Float16>();
+    ha.tokens = tokens_dev; ha.nats = nats_dev;
+    ha.p0 = (k0 == 0) ? 0 : window_end(k0 - 1, P, L, S);
+    ha.p1 = window_end(k0 + W - 1, P, L, S);
+    ha.k0 = k0; ha.K = K; ha.e0 = e0; ha.L = (int32_t)L; ha.S = (int32_t)S; ha.Lp = Lp; ha.d = d;
+    ha.vocab = m->V; ha.eps = eps; ha.flags = m->flags.as<int32_t>();
+    const double R = (double)(ha.p1 - ha.p0);
+    if ((rc = timed(m, I6G_K_HEAD, s, 2.0 * R * m->V * d, R * d * 4.0 + (double)m->V * d * 2,
+                    [&] { return launch_head(ha, s); })))
+      return rc;
+  }
+
+  ReduceArgs ra{};
+  ra.nats = nats_dev; ra.bytes = bytes_dev; ra.P = P;
+  ra.part_nats = m->part_n.as<double>(); ra.part_bytes = m->part_b.as<long long>();
+  ra.n_parts = (int32_t)std::min<int64_t>(256, (P + 255) / 256);
+  ra.totals = totals_dev; ra.flags = m->flags.as<int32_t>();
+  if ((rc = timed(m, I6G_K_REDUCE, s, (double)P, (double)P * 8.0, [&] { return launch_reduce(ra, s); })))
+    return rc;
+  return I6G_OK;
+}
+
+int i6g_set_timing(i6g_model* m, int enable, uint32_t class_mask) {
+  if (!m) return fail(I6G_EINVAL, "set_timing: NULL model");
+  if (m->timed_stream) (void)hipStreamSynchronize(m->timed_stream);
+  for (auto& r : m->recs) { m->pool.push_back(r.a); m->pool.push_back(r.b); }
+  m->recs.clear();
+  m->timing = enable != 0;
+  m->timing_mask = class_mask;
+  for (int c = 0; c < I6G_K_COUNT; ++c) { m->t_ms[c] = m->t_flops[c] = m->t_bytes[c] = 0; m->t_n[c] = 0; }
+  return I6G_OK;
+}
+
+int i6g_get_timing(i6g_model* m, int kernel_class, double* total_ms, int64_t* launches, double* flops,
+                   double* bytes) {
+  if (!m || kernel_class < 0 || kernel_class >= I6G_K_COUNT) return fail(I6G_EINVAL, "get_timing");
+  if (!m->recs.empty()) {
+    HIP_TRY(hipStreamSynchronize(m->timed_stream));
+    for (auto& r : m->recs) {
+      float ms = 0.f;
+      HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));
+      m->t_ms[r.cls] += ms;
+      m->t_flops[r.cls] += r.flops;
+      m->t_bytes[r.cls] += r.bytes;
+      m->t_n[r.cls] += 1;
+      m->pool.push_back(r.a);
+      m->pool.push_back(r.b);
+    }
+    m->recs.clear();
+  }
+  if (total_ms) *total_ms = m->t_ms[kernel_class];
+  if (launches) *launches = m->t_n[kernel_class];
+  if (flops) *flops = m->t_flops[kernel_class];
+  if (bytes) *bytes = m->t_bytes[kernel_class];
+  return I6G_OK;
+}
+
+}  // extern "C"

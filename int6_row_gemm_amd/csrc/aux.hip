@@ -1,0 +1,302 @@
+// Embedding gather, LoRA down-projection, tied head + cross-entropy, the
+// bits-per-byte reduction, and the constant tables built at load time.
+#include "common.h"
+
+namespace i6g {
+namespace {
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Embedding: x0 = E[u] (+ bigram row), pwwt.cn "parameter-golf 16MB 极限压缩
+// 实战 …" 架构 (tied embedding) and the kwkr.cn PR #363 write-up (BigramHash:
+// adjacent-token hash into a table, projected to the model width; the
+// table is pre-multiplied by the projection at load time).  Row m of the
+// batch is position j = m % Lp of window k0 + m / Lp; positions past the end
+// of the window's inputs read token 0 and are never scored.  One wave per row;
+// it also writes bf16(x) and the row's sum of squares for the first normed
+// GEMM.
+__global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= (int64_t)a.W * a.Lp) return;
+  const int64_t k = a.k0 + m / a.Lp;
+  const int64_t j = m % a.Lp;
+  const int64_t s = k * a.S;
+  const int64_t e = min(s + (int64_t)a.L, a.P);
+  const bool valid = s + j < e;
+  int tok = valid ? a.tokens[s + j] : 0;
+  if (tok < 0 || tok >= a.vocab) {
+    if (lane == 0) atomicOr(a.flags, 2);
+    tok = 0;
+  }
+  const float* brow = nullptr;
+  if (a.bigram && valid && j >= 1) {
+    int prev = a.tokens[s + j - 1];
+    if (prev < 0 || prev >= a.vocab) prev = 0;
+    int64_t hsh = ((int64_t)prev * 1000003 + (int64_t)tok) % a.buckets;
+    brow = a.bigram + hsh * a.d;
+  }
+  float sq = 0.f;
+  for (int c = lane; c < a.d; c += 64) {
+    float v = a.embed_f32 ? reinterpret_cast<const float*>(a.embed)[(int64_t)tok * a.d + c]
+                          : (float)reinterpret_cast<const _Float16*>(a.embed)[(int64_t)tok * a.d + c];
+    if (brow) v += brow[c];
+    a.x[m * a.d + c] = v;
+    a.xb[m * a.d + c] = (bf16)v;
+    sq += v * v;
+  }
+  sq = wave_sum(sq);
+  if (lane < a.nt) a.ss[m * a.nt + lane] = (lane == 0) ? sq : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// DepthLoRA down-projection (kwkr.cn PR #363 write-up, per-depth low-rank
+// adapter on Q and V): u = N(x) A^T for the q and v adapters.
+__global__ __launch_bounds__(256) void lora_down_kernel(LoraArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= a.M) return;
+  const float* xr = a.x + m * a.d;
+  float sq = 0.f;
+  for (int c = lane; c < a.d; c += 64) sq += xr[c] * xr[c];
+  sq = wave_sum(sq);
+  const float rinv = 1.0f / sqrtf(sq / (float)a.d + a.eps);
+  for (int t = 0; t < 2 * a.r; ++t) {
+    const float* ar = (t < a.r ? a.aq + t * a.d : a.av + (t - a.r) * a.d);
+    float acc = 0.f;
+    for (int c = lane; c < a.d; c += 64) acc += xr[c] * ar[c];
+    acc = wave_sum(acc);
+    if (lane == 0) a.u[m * 2 * a.r + t] = acc * rinv;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tied head + log-softmax cross-entropy on the scored rows of a batch
+// (pwwt.cn "parameter-golf 16MB 极限压缩实战 …": tied input/output embedding;
+// 滑动窗口评估: only the scored positions of a window reach the loss).
+// A workgroup takes 64 scored predictions, 16 per wave.  Each wave normalises
+// its rows into fp16 (final RMSNorm), keeps them as the B operand, and
+// streams the binary16 embedding as the A operand of
+// v_mfma_f32_16x16x32_f16, so logits^T arrive with one row per lane column:
+// the log-sum-exp runs online per lane and is merged over the 4 lane groups
+// at the end.  Logits never reach memory.
+__global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 zs[64 * (640 + 8)];   // [64][d + 8], d <= 640
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int zld = a.d + 8;
+  const int64_t pw = a.p0 + (int64_t)blockIdx.x * 64 + wave * 16;
+
+  for (int rr = 0; rr < 16; ++rr) {
+    const int64_t p = pw + rr;
+    _Float16* zrow = zs + (wave * 16 + rr) * zld;
+    if (p < a.p1) {
+      int64_t k = (p < a.e0) ? 0 : (p - a.L) / a.S + 1;
+      if (k > a.K - 1) k = a.K - 1;
+      const int64_t row = (k - a.k0) * a.Lp + (p - k * a.S);
+      const float* xr = a.x + row * a.d;
+      float sq = 0.f;
+      for (int c = lane; c < a.d; c += 64) sq += xr[c] * xr[c];
+      sq = wave_sum(sq);
+      const float rinv = 1.0f / sqrtf(sq / (float)a.d + a.eps);
+      for (int c = lane; c < a.d; c += 64) zrow[c] = (_Float16)(xr[c] * rinv);
+    } else {
+      for (int c = lane; c < a.d; c += 64) zrow[c] = (_Float16)0.0f;
+    }
+  }
+  __syncthreads();
+
+  const int64_t p_mine = pw + lr;
+  const bool have = p_mine < a.p1;
+  int tgt = have ? a.tokens[p_mine + 1] : -1;
+  if (have && (tgt < 0 || tgt >= a.vocab)) {
+    if (lg == 0) atomicOr(a.flags, 2);
+    tgt = -1;
+  }
+
+  const int nks = a.d / 32;
+  f16x8 zf[20];
+#pragma unroll
+  for (int ks = 0; ks < 20; ++ks)
+    if (ks < nks)
+      zf[ks] = *reinterpret_cast<const f16x8*>(zs + (wave * 16 + lr) * zld + ks * 32 + 8 * lg);
+
+  float mrun = -1e30f, srun = 0.f, tl = 0.f;
+  int got = 0;
+  for (int vb = 0; vb < a.vocab; vb += 16) {
+    const _Float16* er = a.E + (int64_t)(vb + lr) * a.d + 8 * lg;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 20; ++ks)
+      if (ks < nks) {
+        f16x8 ef = *reinterpret_cast<const f16x8*>(er + ks * 32);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ef, zf[ks], acc, 0, 0, 0);
+      }
+    const int vbase = vb + 4 * lg;
+    float mt = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+    float mn = fmaxf(mrun, mt);
+    srun = srun * expf(mrun - mn) + expf(acc[0] - mn) + expf(acc[1] - mn) +
+           expf(acc[2] - mn) + expf(acc[3] - mn);
+    mrun = mn;
+    if (tgt >= vbase && tgt < vbase + 4) {
+      int i = tgt - vbase;
+      tl = (i == 0) ? acc[0] : (i == 1) ? acc[1] : (i == 2) ? acc[2] : acc[3];
+      got = 1;
+    }
+  }
+#pragma unroll
+  for (int off = 16; off < 64; off <<= 1) {
+    float mo = __shfl_xor(mrun, off);
+    float so = __shfl_xor(srun, off);
+    float to = __shfl_xor(tl, off);
+    int go = __shfl_xor(got, off);
+    float mn = fmaxf(mrun, mo);
+    srun = srun * expf(mrun - mn) + so * expf(mo - mn);
+    mrun = mn;
+    if (go) { tl = to; got = 1; }
+  }
+  if (have && lg == 0) a.nats[p_mine] = mrun + logf(srun) - tl;
+}
+
+// ---------------------------------------------------------------------------
+// Bits per byte (pigsec.cn openai/parameter-golf README mirror: the score is
+// tokenizer-agnostic bits per byte): sum of nats over the sum of the byte
+// counts of the predicted tokens, times 1/ln 2.  Two deterministic passes
+// (fixed partition, fixed tree) in fp64 / int64.
+__global__ __launch_bounds__(256) void reduce_part_kernel(ReduceArgs a) {
+  __shared__ double sn[256];
+  __shared__ long long sb[256];
+  const int tid = threadIdx.x;
+  const int64_t per = (a.P + a.n_parts - 1) / a.n_parts;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = min(lo + per, a.P);
+  double n = 0.0;
+  long long b = 0;
+  int bad = 0;
+  for (int64_t p = lo + tid; p < hi; p += 256) {
+    n += (double)a.nats[p];
+    int by = a.bytes[p + 1];
+    if (by < 0) { bad = 1; by = 0; }
+    b += by;
+  }
+  if (bad) atomicOr(a.flags, 4);
+  sn[tid] = n;
+  sb[tid] = b;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st) { sn[tid] += sn[tid + st]; sb[tid] += sb[tid + st]; }
+    __syncthreads();
+  }
+  if (tid == 0) { a.part_nats[blockIdx.x] = sn[0]; a.part_bytes[blockIdx.x] = sb[0]; }
+}
+
+__global__ void reduce_final_kernel(ReduceArgs a) {
+  if (threadIdx.x != 0) return;
+  double n = 0.0;
+  long long b = 0;
+  for (int i = 0; i < a.n_parts; ++i) { n += a.part_nats[i]; b += a.part_bytes[i]; }
+  a.totals[0] = n;
+  a.totals[1] = (double)b;
+  a.totals[2] = (double)a.P;
+  a.totals[3] = (b > 0) ? n / (0.69314718055994530942 * (double)b) : __builtin_nan("");
+  if (b <= 0) atomicOr(a.flags, 4);
+}
+
+// ---------------------------------------------------------------------------
+// RoPE table: (cos, sin) of p * base^(-2i/hd), evaluated in fp64.
+__global__ void rope_table_kernel(float2* tab, int Lmax, int hd, double base) {
+  const int half = hd / 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)Lmax * half) return;
+  const int p = (int)(idx / half), i = (int)(idx % half);
+  const double theta = pow(base, -2.0 * (double)i / (double)hd);
+  const double ang = (double)p * theta;
+  tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+// Bigram table pre-multiplied by its projection: out[b, n] = sum_t table[b, t] * proj[n, t].
+__global__ void bigram_table_kernel(const uint16_t* table, const uint16_t* proj, float* out,
+                                    int buckets, int dim, int d) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)buckets * d) return;
+  const int b = (int)(idx / d), n = (int)(idx % d);
+  double acc = 0.0;
+  for (int t = 0; t < dim; ++t)
+    acc += (double)(float)__builtin_bit_cast(_Float16, table[(int64_t)b * dim + t]) *
+           (double)(float)__builtin_bit_cast(_Float16, proj[(int64_t)n * dim + t]);
+  out[idx] = (float)acc;
+}
+
+__global__ void f16_to_f32_kernel(const uint16_t* in, float* out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (float)__builtin_bit_cast(_Float16, in[i]);
+}
+
+__global__ void f32_to_f16_kernel(const float* in, _Float16* out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (_Float16)in[i];
+}
+
+inline unsigned nblk(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
+
+}  // namespace
+
+hipError_t launch_embed(const EmbedArgs& a, hipStream_t s) {
+  int64_t rows = (int64_t)a.W * a.Lp;
+  hipLaunchKernelGGL(embed_kernel, dim3(nblk(rows, 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_down(const LoraArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(lora_down_kernel, dim3(nblk(a.M, 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_head(const HeadArgs& a, hipStream_t s) {
+  if (a.d % 32 != 0 || a.d > 640 || a.vocab % 16 != 0) return hipErrorInvalidValue;
+  int64_t rows = a.p1 - a.p0;
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(head_kernel, dim3(nblk(rows, 64)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(reduce_part_kernel, dim3(a.n_parts), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(reduce_final_kernel, dim3(1), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float2* tab, int32_t Lmax, int32_t hd, double base, hipStream_t s) {
+  int64_t n = (int64_t)Lmax * (hd / 2);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(nblk(n, 256)), dim3(256), 0, s, tab, Lmax, hd, base);
+  return hipGetLastError();
+}
+
+hipError_t launch_bigram_table(const uint16_t* table, const uint16_t* proj, float* out,
+                               int32_t buckets, int32_t dim, int32_t d, hipStream_t s) {
+  int64_t n = (int64_t)buckets * d;
+  hipLaunchKernelGGL(bigram_table_kernel, dim3(nblk(n, 256)), dim3(256), 0, s, table, proj, out,
+                     buckets, dim, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_f16_to_f32(const uint16_t* in, float* out, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(f16_to_f32_kernel, dim3(nblk(n, 256)), dim3(256), 0, s, in, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_f32_to_f16(const float* in, _Float16* out, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(f32_to_f16_kernel, dim3(nblk(n, 256)), dim3(256), 0, s, in, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace i6g

@@ -1,0 +1,135 @@
+// Internal declarations shared by the HIP kernels and the C-ABI host code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace i6g {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Row quantiser
+struct QuantArgs {
+  const float* w;
+  int8_t* codes;
+  uint16_t* scales;
+  int32_t* flags;
+  int64_t rows;
+  int32_t cols;
+  int32_t bits;
+  int32_t topk;   // number of largest |w| kept per row (cols - lo)
+  float frac;     // fp32 interpolation weight f
+};
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Dequant-fused GEMM: C[m, n] = sum_k A[m, k] * code[n, k], A bf16 [M, K],
+// codes int8 [N, K]; the per-row scale of B (and, for normed inputs, the
+// per-row RMS factor of A) is applied in the epilogue.
+enum EpiKind { EPI_QKV = 0, EPI_RELU2 = 1, EPI_RES = 2 };
+
+struct GemmArgs {
+  const bf16* A;          // [M, K]
+  const int8_t* B;        // [N, K]
+  const uint16_t* scale;  // [N] binary16
+  int32_t M, N, K;
+  // RMS factor of the A rows (EPI_QKV, EPI_RELU2): rinv = 1/sqrt(sum_t ss[m,t]/K + eps)
+  const float* ss_in;     // [M, nt_in]
+  int32_t nt_in;
+  float eps;
+  // EPI_QKV
+  bf16* q; bf16* k; bf16* vt;
+  int32_t n_heads, n_kv, hd, Lp;
+  const float2* rope;     // [Lp, hd/2] (cos, sin)
+  const float* lora_u;    // [M, 2r] or null
+  const float* lora_bq;   // [d, r]
+  const float* lora_bv;   // [Hkv*hd, r]
+  int32_t lora_r;
+  // EPI_RELU2
+  bf16* h;                // [M, N]
+  // EPI_RES
+  float* x;               // [M, N] residual, updated in place
+  bf16* xb;               // [M, N] bf16 copy of the new x (or null)
+  float* ss_out;          // [M, N/128] partial sums of squares (or null)
+  float* push_dst;        // [M, N] skip slot to store the new x into (or null)
+  const float* pop_src;   // [M, N] skip slot to add (or null); may equal push_dst
+  const float* pop_w;     // [N] fp32 skip weight
+};
+hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Causal GQA attention over a batch of windows.
+struct AttnArgs {
+  const bf16* q;   // [W, Hq, Lp, hd]
+  const bf16* k;   // [W, Hkv, Lp, hd]
+  const bf16* vt;  // [W, Hkv, hd, Lp]
+  bf16* o;         // [W*Lp, Hq*hd]
+  int32_t W, n_heads, n_kv, hd, Lp;
+  float scale_log2;  // log2(e) / sqrt(hd)
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Embedding gather (+ bigram), writes x, bf16 x and row sums of squares.
+struct EmbedArgs {
+  const int32_t* tokens;
+  int64_t n_tokens;
+  int64_t P;           // n_tokens - 1
+  int64_t k0;          // first window of the batch
+  int32_t W, Lp, L, S;
+  const void* embed; int32_t embed_f32;
+  const float* bigram; // [buckets, d] fp32 (table * proj^T) or null
+  int32_t buckets;
+  int32_t vocab, d, nt;  // nt partial-sum slots per row
+  float* x; bf16* xb; float* ss;
+  int32_t* flags;
+};
+hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
+
+// LoRA down-projection: u[m, 0:r] = N(x[m]) . aq^T, u[m, r:2r] = N(x[m]) . av^T
+struct LoraArgs {
+  const float* x; int32_t M, d, r; float eps;
+  const float* aq; const float* av;   // [r, d] fp32
+  float* u;                           // [M, 2r]
+};
+hipError_t launch_lora_down(const LoraArgs& a, hipStream_t s);
+
+// Tied head + log-softmax cross-entropy on the scored rows of a batch.
+struct HeadArgs {
+  const float* x;        // [W*Lp, d]
+  const _Float16* E;     // [V, d] binary16
+  const int32_t* tokens;
+  float* nats;           // [P]
+  int64_t p0, p1;        // predictions scored by this batch
+  int64_t k0, K, e0;     // first window, window count, end of window 0
+  int32_t L, S, Lp, d, vocab;
+  float eps;
+  int32_t* flags;
+};
+hipError_t launch_head(const HeadArgs& a, hipStream_t s);
+
+// Totals: sum nats (fp64), sum bytes[p+1] (int64), count, bpb.
+struct ReduceArgs {
+  const float* nats; const int32_t* bytes; int64_t P;
+  double* part_nats; long long* part_bytes; int32_t n_parts;
+  double* totals; int32_t* flags;
+};
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
+
+// Constant tables built at load time on the device.
+hipError_t launch_rope_table(float2* tab, int32_t Lmax, int32_t hd, double base, hipStream_t s);
+hipError_t launch_bigram_table(const uint16_t* table, const uint16_t* proj, float* out,
+                               int32_t buckets, int32_t dim, int32_t d, hipStream_t s);
+hipError_t launch_f16_to_f32(const uint16_t* in, float* out, int64_t n, hipStream_t s);
+hipError_t launch_f32_to_f16(const float* in, _Float16* out, int64_t n, hipStream_t s);
+
+}  // namespace i6g

@@ -1,0 +1,105 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol its header
+declares, plans windows exactly as the oracle does, and rejects invalid
+arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    import int6_row_gemm_amd as g
+    if not os.path.exists(g.LIB_PATH):
+        pytest.skip("libi6g.so not built (run __graft_entry__.build())")
+    return g, g.lib()
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "i6g.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(i6g_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    g, L = _lib()
+    names = _header_functions()
+    assert "i6g_score_tokens" in names and "i6g_quantize_rows" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(g.EXPORTED) == names
+
+
+@pytest.mark.parametrize("n,L,S", [(1025, 256, 256), (1000, 128, 64), (3000, 512, 100), (50, 128, 64),
+                                   (2, 1, 1), (1_048_576, 2048, 64), (4_194_304, 2048, 64),
+                                   (65_537, 2048, 2048), (400, 128, 128), (700, 200, 50)])
+def test_window_plan_matches_oracle(n, L, S):
+    g, _ = _lib()
+    from oracle import windows
+    st, en, sf = g.plan_windows(n, L, S)
+    plan = windows.plan_windows(n, L, S)
+    assert len(plan) == len(st)
+    assert np.array_equal(st, [p[0] for p in plan])
+    assert np.array_equal(en, [p[1] for p in plan])
+    assert np.array_equal(sf, [p[2] for p in plan])
+
+
+def test_argument_validation_without_gpu():
+    g, L = _lib()
+    fake = ctypes.c_void_p(0x1000)     # never dereferenced: validation fails first
+    null = ctypes.c_void_p(0)
+    # bits not in {6, 8}
+    assert L.i6g_quantize_rows(fake, 4, 4, 7, 1.0, fake, fake, null, null) == -1
+    # quantile outside (0, 1]
+    assert L.i6g_quantize_rows(fake, 4, 4, 6, 1.5, fake, fake, null, null) == -1
+    assert L.i6g_quantize_rows(fake, 4, 4, 6, 0.0, fake, fake, null, null) == -1
+    # empty shapes and NULL arrays
+    assert L.i6g_quantize_rows(fake, 0, 4, 6, 1.0, fake, fake, null, null) == -1
+    assert L.i6g_quantize_rows(null, 4, 4, 6, 1.0, fake, fake, null, null) == -1
+    # a quantile needing more than the 8 largest values of a row
+    assert L.i6g_quantize_rows(fake, 4, 100, 6, 0.5, fake, fake, null, null) == -6
+    assert "largest" in L.i6g_last_error().decode()
+    # score_tokens / load_model on bad input
+    assert L.i6g_score_tokens(null, fake, fake, 10, 4, 2, fake, fake, null) == -1
+    out = ctypes.c_void_p(0)
+    assert L.i6g_load_model(null, null, ctypes.byref(out)) == -1
+    assert out.value is None
+    n = ctypes.c_int64(0)
+    assert L.i6g_plan_windows(10, 4, 5, ctypes.byref(n), None, None, None, 0) == -1
+    assert L.i6g_plan_windows(1, 4, 2, ctypes.byref(n), None, None, None, 0) == -1
+
+
+def test_load_model_rejects_bad_descriptors():
+    g, L = _lib()
+    d = g._Desc()
+    d.vocab, d.d_model, d.n_heads, d.n_kv_heads, d.head_dim, d.d_ff = 1024, 512, 8, 4, 64, 1536
+    d.n_unique, d.n_eff = 1, 1
+    out = ctypes.c_void_p(0)
+    # NULL schedule / blocks / embedding
+    assert L.i6g_load_model(ctypes.byref(d), None, ctypes.byref(out)) == -1
+    sched = (ctypes.c_int32 * 1)(0)
+    blocks = (g._Block * 1)()
+    emb = ctypes.c_void_p(0x1000)
+    d.schedule = ctypes.cast(sched, ctypes.c_void_p)
+    d.blocks = ctypes.cast(blocks, ctypes.c_void_p)
+    d.embed = emb
+    d.head_dim = 48
+    d.n_heads = 10
+    d.d_model = 480
+    assert L.i6g_load_model(ctypes.byref(d), None, ctypes.byref(out)) in (-1, -6)
+    d.d_model, d.n_heads, d.head_dim = 512, 8, 64
+    bad = (ctypes.c_int32 * 1)(3)      # schedule names a block that does not exist
+    d.schedule = ctypes.cast(bad, ctypes.c_void_p)
+    assert L.i6g_load_model(ctypes.byref(d), None, ctypes.byref(out)) == -1
+    assert "schedule" in L.i6g_last_error().decode()
+
+
+def test_binding_refuses_missing_library(monkeypatch, tmp_path):
+    import int6_row_gemm_amd as g
+    monkeypatch.setattr(g, "_lib", None)
+    monkeypatch.setattr(g, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        g.lib()

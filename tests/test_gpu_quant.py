@@ -1,0 +1,75 @@
+"""GPU parity of the row quantiser: codes and binary16 scales bit-exact
+against the oracle on every configuration's matrices and on adversarial
+rows."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import quant as oq
+from gpu_common import need_gpu, print_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_quant(g, w, bits, q):
+    import torch
+    codes, scales = g.quantize_rows(torch.from_numpy(w).cuda(), bits, q)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy().view(np.uint16)
+
+
+def _assert_same(g, w, bits, q, label):
+    print_case("quantize", label, w.shape, bits, q)
+    codes, scales = _gpu_quant(g, w, bits, q)
+    rc, rs = oq.quantize_rows(w, bits, q)
+    bad = np.argwhere(codes != rc)
+    assert bad.size == 0, f"{label}: {len(bad)} code mismatches, first {bad[:3].tolist()}"
+    sb = np.argwhere(scales != rs.view(np.uint16))
+    assert sb.size == 0, f"{label}: {len(sb)} scale mismatches, first {sb[:3].tolist()}"
+
+
+@pytest.mark.parametrize("name", ["tiny", "baseline", "11l", "midcycle", "largevocab"])
+def test_config_matrices_bit_exact(name):
+    g = need_gpu()
+    cfg = synth.config(name)
+    model = synth.make_model(cfg["arch"], seed=1337)
+    a = cfg["arch"]
+    for b, blk in enumerate(model["blocks"]):
+        if b > 1 and name != "tiny" and b % 3:
+            continue                     # every third block beyond the first two
+        for mname, w in blk.items():
+            _assert_same(g, w, a["bits"], a["clip_q"], f"{name}/block{b}/{mname}")
+
+
+@pytest.mark.parametrize("cols", [48, 512, 1536, 2048])
+@pytest.mark.parametrize("bits,q", [(6, 0.9999984), (8, 0.9999984), (6, 1.0), (8, 1.0), (6, 0.999)])
+def test_adversarial_rows_bit_exact(cols, bits, q):
+    g = need_gpu()
+    if cols - int(np.floor(q * (cols - 1))) > 8:
+        pytest.skip("quantile outside the kernel's top-8 window")
+    rng = np.random.default_rng(cols + bits)
+    w = synth.adversarial_rows(rng, cols)
+    _assert_same(g, w, bits, q, f"adversarial/{cols}")
+
+
+def test_ragged_rows_and_many_rows():
+    g = need_gpu()
+    rng = np.random.default_rng(5)
+    for rows, cols in [(1, 1), (3, 7), (5, 65), (4097, 130)]:
+        w = rng.normal(0, 0.02, size=(rows, cols)).astype(np.float32)
+        _assert_same(g, w, 6, 0.9999984 if cols > 1 else 1.0, f"ragged/{rows}x{cols}")
+
+
+def test_nonfinite_row_flagged():
+    import torch
+    g = need_gpu()
+    w = np.random.default_rng(6).normal(0, 0.02, size=(4, 64)).astype(np.float32)
+    w[2, 10] = np.inf
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    codes, scales = g.quantize_rows(torch.from_numpy(w).cuda(), 6, 1.0, flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) & 1
+    s = scales.cpu().numpy().view(np.uint16)
+    assert s[2] == 0x7E00 and np.all(codes.cpu().numpy()[2] == 0)
+    rc, rs = oq.quantize_rows(w[[0, 1, 3]], 6, 1.0)
+    assert np.array_equal(codes.cpu().numpy()[[0, 1, 3]], rc)

@@ -1,0 +1,144 @@
+"""GPU parity of the scoring pass against the oracle.
+
+Small cases run the oracle over every window (several tiles, ragged tails,
+short streams, padded windows, every architecture feature, amplified small
+components); full-size cases compare sampled windows one by one and check
+the totals by properties that hold at any size."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import windows as ow
+from gpu_common import (BPB_ATOL, NATS_RTOL, compare_nats, gpu_model, make_case, need_gpu,
+                        oracle_quantized, print_case)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(g, name, L, S, n_tokens, seed=1337, model_kw=None, batch_windows=None, **ov):
+    import torch
+    cfg, model = make_case(name, seed=seed, model_kw=model_kw, **ov)
+    tokens, nbytes = synth.make_stream(cfg, seed=seed, n_tokens=n_tokens)
+    print_case("score", name, ov, "L", L, "S", S, "N", n_tokens, model_kw or "")
+    gm, _ = gpu_model(g, model)
+    if batch_windows:
+        gm.set_batch_windows(batch_windows)
+    nats, totals = gm.score(torch.from_numpy(tokens).cuda(), torch.from_numpy(nbytes).cuda(), L, S)
+    torch.cuda.synchronize()
+    return cfg, model, tokens, nbytes, nats.cpu().numpy(), totals.cpu().numpy()
+
+
+def _full_oracle(model, tokens, nbytes, L, S):
+    qm = oracle_quantized(model)
+    ref, mask = ow.score(qm, tokens, L, S)
+    assert mask.all()
+    return ref, ow.bpb(ref, nbytes)
+
+
+SMALL = [
+    # name, overrides, L, S, N
+    ("tiny", {}, 256, 256, 4 * 256 + 1),
+    ("tiny", {}, 256, 64, 700),
+    ("11l", {}, 256, 64, 1000),
+    ("baseline", {}, 128, 128, 400),
+    ("midcycle", {}, 128, 128, 257),
+    ("largevocab", {}, 200, 50, 700),
+    ("11l", {}, 2048, 64, 100),          # stream shorter than one window
+    ("11l", {"schedule": [0, 1, 2]}, 64, 16, 300),
+]
+
+
+@pytest.mark.parametrize("name,ov,L,S,N", SMALL)
+def test_small_full_parity(name, ov, L, S, N):
+    g = need_gpu()
+    cfg, model, tokens, nbytes, nats, totals = _run(g, name, L, S, N, **ov)
+    ref, ref_bpb = _full_oracle(model, tokens, nbytes, L, S)
+    compare_nats(nats, ref, label=f"{name} L={L} S={S} N={N}")
+    assert totals[2] == N - 1
+    assert totals[1] == float(nbytes[1:].sum())
+    assert abs(totals[3] - ref_bpb) <= BPB_ATOL, (totals[3], ref_bpb)
+
+
+def test_batching_does_not_change_results():
+    g = need_gpu()
+    runs = [_run(g, "11l", 128, 32, 600, batch_windows=b)[4] for b in (1, 3, 64)]
+    np.testing.assert_array_equal(runs[0], runs[1])
+    np.testing.assert_array_equal(runs[0], runs[2])
+
+
+@pytest.mark.parametrize("kw,label", [
+    (dict(lora_b_std=1.0), "lora x100"),
+    (dict(bigram_scale=100.0), "bigram x100"),
+    (dict(skip_scale=3.0), "skip x3"),
+])
+def test_amplified_components(kw, label):
+    """Components whose effect at the configured init is below the tolerance
+    are checked with amplified parameters so a mistake in them would show."""
+    g = need_gpu()
+    cfg, model, tokens, nbytes, nats, totals = _run(g, "midcycle", 128, 128, 257, model_kw=kw)
+    ref, ref_bpb = _full_oracle(model, tokens, nbytes, 128, 128)
+    compare_nats(nats, ref, label=label)
+    assert abs(totals[3] - ref_bpb) <= BPB_ATOL
+
+
+def test_uniform_logits_closed_form():
+    import torch
+    g = need_gpu()
+    cfg, model = make_case("baseline")
+    model["embed"] = np.zeros_like(model["embed"])
+    tokens, nbytes = synth.make_stream(cfg, seed=3, n_tokens=3 * 128 + 1)
+    gm, _ = gpu_model(g, model)
+    nats, totals = gm.score(torch.from_numpy(tokens).cuda(), torch.from_numpy(nbytes).cuda(), 128, 128)
+    nats = nats.cpu().numpy()
+    np.testing.assert_allclose(nats, math.log(1024), rtol=1e-6)
+    want = math.log2(1024) * (len(tokens) - 1) / float(nbytes[1:].sum())
+    assert abs(totals.cpu().numpy()[3] - want) < 1e-6
+
+
+def test_bad_token_is_reported():
+    import torch
+    g = need_gpu()
+    cfg, model = make_case("tiny")
+    tokens, nbytes = synth.make_stream(cfg, seed=4, n_tokens=200)
+    tokens[17] = 5000
+    gm, _ = gpu_model(g, model)
+    with pytest.raises(g.I6GError) as ei:
+        gm.score(torch.from_numpy(tokens).cuda(), torch.from_numpy(nbytes).cuda(), 64, 64)
+    assert "ETOKEN" in str(ei.value)
+    tokens[17] = 3
+    nbytes[5] = -1
+    with pytest.raises(g.I6GError) as ei:
+        gm.score(torch.from_numpy(tokens).cuda(), torch.from_numpy(nbytes).cuda(), 64, 64)
+    assert "EBYTES" in str(ei.value)
+
+
+# ------------------------------------------------------------ full sizes
+FULL = [
+    # name, windows sampled for the oracle
+    ("tiny", None),
+    ("baseline", [0, 37, 63]),
+    ("midcycle", [0, 31]),
+    ("11l", [0, 8191, 16352]),
+]
+
+
+@pytest.mark.parametrize("name,sample", FULL)
+def test_full_size_sampled(name, sample):
+    g = need_gpu()
+    cfg = synth.config(name)
+    L, S = cfg["window"], cfg["stride"]
+    cfg, model, tokens, nbytes, nats, totals = _run(g, name, L, S, cfg["n_tokens"])
+    P = len(tokens) - 1
+    assert totals[2] == P
+    assert totals[1] == float(nbytes[1:].astype(np.int64).sum())
+    # totals agree with the per-token outputs (property at any size)
+    assert abs(totals[0] - nats.astype(np.float64).sum()) <= 1e-9 * abs(totals[0]) + 1e-6
+    assert abs(totals[3] - totals[0] / (math.log(2) * totals[1])) <= 1e-12
+    assert np.all(np.isfinite(nats)) and np.all(nats > 0)
+    qm = oracle_quantized(model)
+    ref, mask = ow.score(qm, tokens, L, S, which=sample)
+    compare_nats(nats, ref, mask=mask, label=f"{name} sampled windows {sample}")
+    if sample is None:
+        assert abs(totals[3] - ow.bpb(ref, nbytes)) <= BPB_ATOL
