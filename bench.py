@@ -1,0 +1,208 @@
+"""Throughput of the int6 per-row scoring pass on one MI355X.
+
+One step = the whole hot path over the 11-layer, d=512 int6 workload:
+row-quantise all 66 block matrices (fp32 weights already in HBM), then score
+the 1,048,576-token synthetic stream with sliding windows of 2048 / stride 64
+(16,353 windows, 1,048,575 scored predictions) down to bits per byte.
+Inputs are resident in HBM before the timed region starts.
+
+Prints one JSON line with scored tokens/s, the roofline of the dominant
+kernel (per-launch HIP-event durations over the timed steps), every kernel
+class's share, and the CPU oracle timed on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="11l")
+    ap.add_argument("--seed", type=int, default=1337)
+    ap.add_argument("--batch-windows", type=int, default=0)
+    ap.add_argument("--cpu-windows", type=int, default=4,
+                    help="full windows the CPU oracle scores for its baseline (0 = skip)")
+    ap.add_argument("--no-timing", action="store_true", help="no per-launch events")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import int6_row_gemm_amd as g
+    import synth
+
+    torch.cuda.set_device(0)
+    cfg = synth.config(args.config)
+    arch = cfg["arch"]
+    L, S = cfg["window"], cfg["stride"]
+    model = synth.make_model(arch, seed=args.seed)
+    tokens_np, nbytes_np = synth.make_stream(cfg, seed=args.seed)
+    N = len(tokens_np)
+    P = N - 1
+
+    # device-resident inputs
+    w_dev = [{k: torch.from_numpy(v).cuda() for k, v in blk.items()} for blk in model["blocks"]]
+    codes = [{k: torch.empty(v.shape, dtype=torch.int8, device="cuda") for k, v in blk.items()}
+             for blk in w_dev]
+    scales = [{k: torch.empty(v.shape[0], dtype=torch.int16, device="cuda") for k, v in blk.items()}
+              for blk in w_dev]
+    tokens = torch.from_numpy(tokens_np).cuda()
+    nbytes = torch.from_numpy(nbytes_np).cuda()
+    nats = torch.empty(P, dtype=torch.float32, device="cuda")
+    totals = torch.empty(4, dtype=torch.float64, device="cuda")
+    lib = g.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def quantize_all():
+        for wb, cb, sb in zip(w_dev, codes, scales):
+            for k, w in wb.items():
+                rc = lib.i6g_quantize_rows(ctypes.c_void_p(w.data_ptr()), w.shape[0], w.shape[1],
+                                           arch["bits"], float(arch["clip_q"]),
+                                           ctypes.c_void_p(cb[k].data_ptr()),
+                                           ctypes.c_void_p(sb[k].data_ptr()), None, stream)
+                if rc != 0:
+                    raise g.I6GError(rc, lib.i6g_last_error().decode())
+
+    quantize_all()
+    torch.cuda.synchronize()
+    qblocks = [{k: (cb[k], sb[k]) for k in cb} for cb, sb in zip(codes, scales)]
+    gm = g.load(model, qblocks)
+    if args.batch_windows:
+        gm.set_batch_windows(args.batch_windows)
+
+    def step():
+        quantize_all()
+        rc = lib.i6g_score_tokens(gm._h, ctypes.c_void_p(tokens.data_ptr()),
+                                  ctypes.c_void_p(nbytes.data_ptr()), N, L, S,
+                                  ctypes.c_void_p(nats.data_ptr()), ctypes.c_void_p(totals.data_ptr()),
+                                  stream)
+        if rc != 0:
+            raise g.I6GError(rc, lib.i6g_last_error().decode())
+
+    for i in range(args.warmup):
+        t0 = time.time()
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup {i} {time.time() - t0:.2f}s", file=sys.stderr, flush=True)
+    gm.status()
+
+    if not args.no_timing:
+        gm.set_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+        print(f"[bench] step {i} enqueued {time.perf_counter() - t0:.2f}s", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gm.status()
+    ms_per_step = 1000.0 * elapsed / args.steps
+    value = P * args.steps / elapsed
+    tot = totals.cpu().numpy()
+
+    kernels = {}
+    if not args.no_timing:
+        for cls in g.KERNEL_CLASSES:
+            ms, n, fl, by = gm.timing(cls)
+            if n:
+                kernels[cls] = {"ms_total": ms / args.steps, "launches": n // args.steps,
+                                "avg_us": 1000.0 * ms / n,
+                                "tflops": fl / (ms * 1e9) if ms > 0 else None,
+                                "gbs": by / (ms * 1e6) if ms > 0 else None}
+        gm.set_timing(False)
+    roofline = None
+    gemm_frac = None
+    if kernels:
+        dom = max(kernels, key=lambda c: kernels[c]["ms_total"])
+        k = kernels[dom]
+        if dom == "reduce" or dom == "embed":
+            ach, peak, unit, bound = k["gbs"], PEAK_HBM_GBS, "GB/s", "hbm"
+        else:
+            ach, peak, unit, bound = k["tflops"], PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
+        roofline = {"kernel": dom, "bound": bound, "achieved": ach, "peak": peak, "unit": unit,
+                    "frac": ach / peak, "traffic": None, "avg_launch_us": k["avg_us"]}
+        gsum_ms = sum(kernels[c]["ms_total"] for c in ("qkv", "oproj", "fc", "proj") if c in kernels)
+        gsum_fl = sum(kernels[c]["tflops"] * kernels[c]["ms_total"] for c in ("qkv", "oproj", "fc", "proj")
+                      if c in kernels)
+        gemm_frac = (gsum_fl / gsum_ms) / PEAK_BF16_TFLOPS if gsum_ms else None
+
+    cpu = None
+    if args.cpu_windows > 0:
+        cpu = cpu_baseline(model, tokens_np, L, S, args.cpu_windows)
+
+    out = {
+        "metric": "scored tokens/sec, 11L-512d int6 sliding-window bpb eval",
+        "value": value,
+        "unit": "scored tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Zipf tokens, uniform byte counts, N(0,0.02) weights)",
+        "config": {"workload": f"{args.config}: {arch['n_eff']} layers d={arch['d_model']} "
+                               f"int{arch['bits']} sliding window {L} stride {S} over {N} tokens",
+                   "tokens": N, "scored": P, "window": L, "stride": S, "seed": args.seed,
+                   "parallelism": "single GPU"},
+        "bpb": float(tot[3]),
+        "gemm_mfma_frac": gemm_frac,
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(model, tokens, L, S, n_windows):
+    """The CPU oracle, as it stands, on full windows from the middle of the
+    stream (each scores `stride` predictions); block quantisation is done once
+    before timing (it is amortised over the whole stream)."""
+    import numpy as np
+    from oracle import quant as oq, windows as ow
+    try:
+        from threadpoolctl import threadpool_info
+    except ImportError:
+        threadpool_info = lambda: []  # noqa: E731
+    qm = oq.quantize_model(model)
+    plan = ow.plan_windows(len(tokens), L, S)
+    mid = len(plan) // 2
+    which = list(range(mid, mid + n_windows))
+    t0 = time.perf_counter()
+    nats, mask = ow.score(qm, tokens, L, S, which=which)
+    dt = time.perf_counter() - t0
+    scored = int(mask.sum())
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    return {"value": scored / dt, "unit": "scored tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_windows} full windows ({scored} scored predictions) from the middle of the "
+                      f"stream, float64 NumPy, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

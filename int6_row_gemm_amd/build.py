@@ -21,6 +21,9 @@ FLAGS = [
     "-Wno-unused-function",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the softmax and epilogues read them
+    # with VALU ops, and AGPR <-> VGPR moves would cost one op per element
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

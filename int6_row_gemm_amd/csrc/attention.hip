@@ -7,18 +7,41 @@
 //
 // One workgroup = (window, KV head, 64 queries) and both query heads of the
 // group, so each K/V tile brought into LDS serves 128 query rows.  Each of
-// the 4 waves owns 32 queries of one head.  The scores are formed transposed,
-// S^T = K Q^T, with v_mfma_f32_16x16x32_bf16: a lane's accumulator then
-// holds one query and 4 keys, so the running max and sum of a query live in
-// one lane group and the softmax needs only two cross-lane steps for the
-// max.  The keys feeding the S^T rows are permuted so that the probabilities
-// a lane holds are exactly the 8 consecutive keys the B operand of
-// O^T += V^T P^T wants; P never leaves registers.  exp is exp2 with the
-// 1/sqrt(hd) * log2(e) factor folded into one multiply-add.
+// the 4 waves owns 32 queries of one head.
+//
+// * The scores are formed transposed, S^T = K Q^T, with
+//   v_mfma_f32_16x16x32_bf16: a lane's accumulator holds one query and 4
+//   keys, so a query's running max lives in one lane group and needs two
+//   cross-lane steps (gfx950 v_permlane16/32_swap, no LDS round trip).
+// * The keys feeding the S^T rows are permuted so that the probabilities a
+//   lane holds are exactly the 8 consecutive keys the B operand of
+//   O^T += V^T P^T wants; P never leaves registers.
+// * The softmax denominator comes out of the same MFMAs: a constant block of
+//   ones appended to V^T makes one extra O^T block equal to sum_k P[q, k]
+//   (of the bf16 P actually used), with no VALU adds.
+// * exp is the hardware exp2 with the 1/sqrt(hd) * log2(e) factor folded
+//   into one multiply-add; the rescale of O is skipped when no running max of
+//   the wave moved (its factor is then exactly 1).
+// * Software pipelining: the MFMAs of the next key tile's S^T are issued
+//   before the softmax of the current one, so the matrix cores and the VALU
+//   work at the same time.  K tiles run one tile ahead of V tiles through two
+//   LDS buffers each, with one barrier per tile; global loads are issued two
+//   tiles ahead into two register sets so their latency spans a whole step.
 #include "common.h"
 
 namespace i6g {
 namespace {
+
+__device__ inline float max_xor16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                            false, false);
+  return __builtin_fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+__device__ inline float max_xor32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                            false, false);
+  return __builtin_fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
 
 template <int HD>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
@@ -35,13 +58,33 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][64 * KLD];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][HD * VLD];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
+  // 1-D grid over (window, KV head, query tile).  The hardware deals
+  // workgroups round-robin over 8 XCDs; remap so that every query tile of a
+  // (window, KV head) pair runs on one XCD and shares its K/V through that
+  // XCD's L2, and hand out the longest (causal) tiles first.
   const int nqt = a.Lp / 64;
-  const int qt = nqt - 1 - (int)blockIdx.x;  // longest rows first
-  const int g = blockIdx.y, w = blockIdx.z;
+  const int npairs = a.W * a.n_kv;
+  int qt, pair;
+  {
+    const int bid = blockIdx.x;
+    const int nblk = npairs * nqt;
+    if ((npairs & 7) == 0) {
+      const int xcd = bid & 7, i = bid >> 3;
+      const int per = npairs >> 3;            // pairs owned by this XCD
+      pair = xcd * per + i % per;
+      qt = nqt - 1 - i / per;
+    } else {
+      pair = bid % npairs;
+      qt = nqt - 1 - bid / npairs;
+    }
+    (void)nblk;
+  }
+  const int g = pair % a.n_kv, w = pair / a.n_kv;
   const int head = 2 * g + (wave >> 1);
   const int qbase = qt * 64 + 32 * (wave & 1);
+  const int nkt = qt + 1;
 
   if constexpr (HDP > HD) {
     for (int i = tid; i < 2 * 64 * (HDP - HD); i += 256) {
@@ -67,150 +110,158 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         qf[qb][ks] = bf16x8{};
     }
 
-  uint4 kreg[KPER], vreg[VPER];
-  auto load_tile = [&](int kt) {
-    const int k0 = kt * 64;
-#pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      int c = tid + 256 * i;
-      if (c < KCH) kreg[i] = *reinterpret_cast<const uint4*>(Kg + (int64_t)k0 * HD + c * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VPER; ++i) {
-      int c = tid + 256 * i;
-      if (c < VCH) {
-        int d = c >> 3, c8 = (c & 7) * 8;
-        vreg[i] = *reinterpret_cast<const uint4*>(Vg + (int64_t)d * a.Lp + k0 + c8);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      int c = tid + 256 * i;
-      if (c < KCH) {
-        int r = c / (HD / 8), c8 = (c % (HD / 8)) * 8;
-        *reinterpret_cast<uint4*>(&Ks[buf][r * KLD + c8]) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VPER; ++i) {
-      int c = tid + 256 * i;
-      if (c < VCH) {
-        int d = c >> 3, c8 = (c & 7) * 8;
-        *reinterpret_cast<uint4*>(&Vs[buf][d * VLD + c8]) = vreg[i];
-      }
-    }
-  };
+  // Register staging, up to three 16-byte chunks per thread and tile, as
+  // named scalars (arrays of them end up in scratch memory).
+  static_assert(KPER <= 3 && VPER <= 3, "staging holds three chunks per thread");
+  uint4 kreg_0, kreg_1, kreg_2, vreg_0, vreg_1, vreg_2, kreg2_0, kreg2_1, kreg2_2, vreg2_0, vreg2_1, vreg2_2;
+  // Chunk indices past the tile are clamped: those threads reload and rewrite
+  // the last chunk with identical data.
+#define ATT_CHUNKS(PER, R, BODY) \
+  { if constexpr ((PER) > 0) { constexpr int i = 0; uint4& r_ = R##_0; BODY } \
+    if constexpr ((PER) > 1) { constexpr int i = 1; uint4& r_ = R##_1; BODY } \
+    if constexpr ((PER) > 2) { constexpr int i = 2; uint4& r_ = R##_2; BODY } }
+#define ATT_LOAD_K(kt, R)                                                             \
+  {                                                                                   \
+    const int64_t k0_ = (int64_t)(kt) * 64;                                           \
+    ATT_CHUNKS(KPER, R, { int c = min(tid + 256 * i, KCH - 1);                           \
+                       r_ = *reinterpret_cast<const uint4*>(Kg + k0_ * HD + c * 8); }) \
+  }
+#define ATT_LOAD_V(kt, R)                                                             \
+  {                                                                                   \
+    const int k0_ = (kt) * 64;                                                        \
+    ATT_CHUNKS(VPER, R, { int c = min(tid + 256 * i, VCH - 1);                           \
+                       r_ = *reinterpret_cast<const uint4*>(Vg + (int64_t)(c >> 3) * a.Lp + k0_ + (c & 7) * 8); }) \
+  }
+#define ATT_STORE_K(buf, R)                                                           \
+  ATT_CHUNKS(KPER, R, { int c = min(tid + 256 * i, KCH - 1);                             \
+                     *reinterpret_cast<uint4*>(&Ks[buf][(c / (HD / 8)) * KLD + (c % (HD / 8)) * 8]) = r_; })
+#define ATT_STORE_V(buf, R)                                                           \
+  ATT_CHUNKS(VPER, R, { int c = min(tid + 256 * i, VCH - 1);                             \
+                     *reinterpret_cast<uint4*>(&Vs[buf][(c >> 3) * VLD + (c & 7) * 8]) = r_; })
+  // S^T for one key tile: row lr of block kb reads physical key pk.
+#define ATT_QK(dst, buf)                                                              \
+  {                                                                                   \
+    _Pragma("unroll") for (int kb = 0; kb < 4; ++kb) {                                \
+      const int pk = 32 * (kb >> 1) + 8 * (lr >> 2) + 4 * (kb & 1) + (lr & 3);        \
+      bf16x8 kf[KS];                                                                  \
+      _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                               \
+        kf[ks] = *reinterpret_cast<const bf16x8*>(&Ks[buf][pk * KLD + ks * 32 + 8 * lg]); \
+      _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                              \
+        f32x4 acc_ = f32x4{0.f, 0.f, 0.f, 0.f};                                       \
+        _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                             \
+          acc_ = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[qb][ks], acc_, 0, 0, 0); \
+        dst[qb][kb] = acc_;                                                           \
+      }                                                                               \
+    }                                                                                 \
+  }
 
   f32x4 o[2][DB];
+  f32x4 osum[2];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    osum[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.0f;
   float mrow[2] = {-1e30f, -1e30f};
-  float lrow[2] = {0.f, 0.f};
   const float c = a.scale_log2;
 
-  const int nkt = qt + 1;
-  load_tile(0);
-  store_tile(0);
+  // prologue: S^T of tile 0; LDS then holds K[1] and V[0]
+  ATT_LOAD_K(0, kreg);
+  ATT_LOAD_V(0, vreg);
+  ATT_STORE_K(0, kreg);
+  ATT_STORE_V(0, vreg);
+  __syncthreads();
+  f32x4 s_cur[2][4], s_nxt[2][4];
+  ATT_QK(s_cur, 0);
+  ATT_LOAD_K(min(1, nkt - 1), kreg);
+  ATT_LOAD_K(min(2, nkt - 1), kreg2);   // stored at the end of step 0
+  ATT_LOAD_V(min(1, nkt - 1), vreg2);
+  ATT_STORE_K(1, kreg);
   __syncthreads();
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) load_tile(kt + 1);
-    const bf16* ks_ = Ks[buf];
-    const bf16* vs_ = Vs[buf];
-
-    f32x4 s[2][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      // S^T row lr of block kb reads physical key pk (see header comment)
-      const int pk = 32 * (kb >> 1) + 8 * (lr >> 2) + 4 * (kb & 1) + (lr & 3);
-      bf16x8 kf[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[ks] = *reinterpret_cast<const bf16x8*>(ks_ + pk * KLD + ks * 32 + 8 * lg);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[qb][ks], acc, 0, 0, 0);
-        s[qb][kb] = acc;
-      }
-    }
-
-    const bool diag = (kt == qt);
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int qabs = qbase + 16 * qb + lr;
-      if (diag) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            int kabs = kt * 64 + 32 * (kb >> 1) + 8 * lg + 4 * (kb & 1) + i;
-            if (kabs > qabs) s[qb][kb][i] = -1e30f;
-          }
-      }
-      float mt = s[qb][0][0];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mt = fmaxf(mt, s[qb][kb][i]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mnew = fmaxf(mrow[qb], mt);
-      const float alpha = exp2f((mrow[qb] - mnew) * c);
-      const float mc = mnew * c;
-      mrow[qb] = mnew;
-      float ls = 0.f;
-      float p[4][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[kb][i] = exp2f(s[qb][kb][i] * c - mc);
-          ls += p[kb][i];
-        }
-      lrow[qb] = lrow[qb] * alpha + ls;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = (bf16)p[2 * kk][i];
-          v[4 + i] = (bf16)p[2 * kk + 1][i];
-        }
-        pf[qb][kk] = v;
-      }
-    }
-
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs_ + (db * 16 + lr) * VLD + 32 * kk + 8 * lg);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb][kk], o[qb][db], 0, 0, 0);
-      }
-
-    if (kt + 1 < nkt) store_tile(buf ^ 1);
-    __syncthreads();
+  // One key tile; SC holds its S^T, SN receives the next tile's.  The
+  // register set RL receives K[kt+3] and V[kt+2]; RS (filled one step
+  // earlier) holds K[kt+2] and V[kt+1], written to LDS at the end.
+#define ATT_STEP(kt, SC, SN, KRL, VRL, KRS, VRS)                                      \
+  {                                                                                   \
+    ATT_LOAD_K(min((kt) + 3, nkt - 1), KRL);                                          \
+    ATT_LOAD_V(min((kt) + 2, nkt - 1), VRL);                                          \
+    if ((kt) + 1 < nkt) ATT_QK(SN, ((kt) + 1) & 1);                                   \
+    if ((kt) == qt) {                                                                 \
+      _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                              \
+        const int qabs = qbase + 16 * qb + lr;                                        \
+        _Pragma("unroll") for (int kb = 0; kb < 4; ++kb)                              \
+          _Pragma("unroll") for (int i = 0; i < 4; ++i) {                             \
+            int kabs = (kt) * 64 + 32 * (kb >> 1) + 8 * lg + 4 * (kb & 1) + i;        \
+            if (kabs > qabs) SC[qb][kb][i] = -1e30f;                                  \
+          }                                                                           \
+      }                                                                               \
+    }                                                                                 \
+    bf16x8 pf[2][2];                                                                  \
+    float alpha[2];                                                                   \
+    bool moved = false;                                                               \
+    _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                                \
+      float mt = SC[qb][0][0];                                                        \
+      _Pragma("unroll") for (int kb = 0; kb < 4; ++kb)                                \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) mt = __builtin_fmaxf(mt, SC[qb][kb][i]); \
+      mt = max_xor16(mt);                                                             \
+      mt = max_xor32(mt);                                                             \
+      const float mnew = __builtin_fmaxf(mrow[qb], mt);                               \
+      moved |= mnew > mrow[qb];                                                       \
+      alpha[qb] = __builtin_amdgcn_exp2f((mrow[qb] - mnew) * c);                      \
+      const float mc = mnew * c;                                                      \
+      mrow[qb] = mnew;                                                                \
+      _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                              \
+        bf16x8 v;                                                                     \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                               \
+          v[i] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(SC[qb][2 * kk][i], c, -mc)); \
+          v[4 + i] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(SC[qb][2 * kk + 1][i], c, -mc)); \
+        }                                                                             \
+        pf[qb][kk] = v;                                                               \
+      }                                                                               \
+    }                                                                                 \
+    if (__any(moved)) {                                                               \
+      _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                              \
+        _Pragma("unroll") for (int db = 0; db < DB; ++db) o[qb][db] *= alpha[qb];     \
+        osum[qb] *= alpha[qb];                                                        \
+      }                                                                               \
+    }                                                                                 \
+    const int vb_ = (kt) & 1;                                                         \
+    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                \
+      _Pragma("unroll") for (int db = 0; db < DB; ++db) {                             \
+        bf16x8 vf = *reinterpret_cast<const bf16x8*>(&Vs[vb_][(db * 16 + lr) * VLD + 32 * kk + 8 * lg]); \
+        _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                              \
+          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb][kk], o[qb][db], 0, 0, 0); \
+      }                                                                               \
+      _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                                \
+        osum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb][kk], osum[qb], 0, 0, 0); \
+    }                                                                                 \
+    /* K[kt+2] replaces K[kt] (read by the previous step), V[kt+1] replaces */        \
+    /* V[kt-1]; the barrier publishes both for the next step. */                      \
+    if ((kt) + 2 < nkt) ATT_STORE_K((kt) & 1, KRS);                                   \
+    if ((kt) + 1 < nkt) ATT_STORE_V(((kt) + 1) & 1, VRS);                             \
+    __syncthreads();                                                                  \
   }
+
+  for (int kt = 0; kt < nkt; kt += 2) {
+    ATT_STEP(kt, s_cur, s_nxt, kreg, vreg, kreg2, vreg2);
+    if (kt + 1 < nkt) ATT_STEP(kt + 1, s_nxt, s_cur, kreg2, vreg2, kreg, vreg);
+  }
+#undef ATT_STEP
+#undef ATT_LOAD_K
+#undef ATT_LOAD_V
+#undef ATT_STORE_K
+#undef ATT_STORE_V
+#undef ATT_CHUNKS
+#undef ATT_QK
 
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float l = lrow[qb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / osum[qb][0];
     const int q = qbase + 16 * qb + lr;
     bf16* dst = a.o + ((int64_t)w * a.Lp + q) * (a.n_heads * HD) + head * HD;
 #pragma unroll
@@ -228,7 +279,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.Lp / 64, a.n_kv, a.W);
+  dim3 grid((unsigned)(a.Lp / 64) * a.n_kv * a.W);
   switch (a.hd) {
     case 32: hipLaunchKernelGGL(attn_kernel<32>, grid, dim3(256), 0, s, a); break;
     case 64: hipLaunchKernelGGL(attn_kernel<64>, grid, dim3(256), 0, s, a); break;

@@ -46,7 +46,7 @@ SMALL = [
     ("midcycle", {}, 128, 128, 257),
     ("largevocab", {}, 200, 50, 700),
     ("11l", {}, 2048, 64, 100),          # stream shorter than one window
-    ("11l", {"schedule": [0, 1, 2]}, 64, 16, 300),
+    ("11l", {"schedule": [0, 1, 2], "n_skip": 1}, 64, 16, 300),
 ]
 
 
