@@ -15,7 +15,10 @@
 //   cross-lane steps (gfx950 v_permlane16/32_swap, no LDS round trip).
 // * The keys feeding the S^T rows are permuted so that the probabilities a
 //   lane holds are exactly the 8 consecutive keys the B operand of
-//   O^T += V^T P^T wants; P never leaves registers.
+//   O^T += V^T P^T wants; P never leaves registers.  The permutation is
+//   applied when K is written to LDS, so fragment reads stay on 16
+//   consecutive rows; all LDS tiles use layouts measured free of bank
+//   conflicts on gfx950.
 // * The softmax denominator comes out of the same MFMAs: a constant block of
 //   ones appended to V^T makes one extra O^T block equal to sum_k P[q, k]
 //   (of the bf16 P actually used), with no VALU adds.
@@ -31,6 +34,18 @@
 
 namespace i6g {
 namespace {
+
+// 16-byte chunk j of a 128-byte LDS row r lives in slot j ^ ((r >> 1) & 7).
+__device__ inline int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+// LDS row of key k inside a 64-key tile: S^T row r of block kb reads key
+// 32(kb>>1) + 8(r>>2) + 4(kb&1) + (r&3), and key k is stored at row 16 kb + r,
+// so every S^T fragment read covers 16 consecutive LDS rows.
+__device__ inline int key_row(int k) {
+  const int kb = 2 * (k >> 5) + ((k >> 2) & 1);
+  const int r = 4 * ((k >> 3) & 3) + (k & 3);
+  return 16 * kb + r;
+}
 
 __device__ inline float max_xor16(float v) {
   auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
@@ -48,8 +63,12 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   constexpr int KS = (HD + 31) / 32;  // 32-wide k steps over the head dim
   constexpr int HDP = KS * 32;
   constexpr int DB = HD / 16;         // 16-row blocks of O^T
-  constexpr int KLD = HDP + 8;
-  constexpr int VLD = 64 + 8;
+  // LDS row strides chosen for conflict-free 16-row fragment reads on gfx950:
+  // 128-byte rows with an XOR swizzle of the 16-byte chunks, or 160 / 224-byte
+  // rows where the padded head dim does not fill 128 bytes exactly.
+  constexpr bool KSWZ = (HDP == 64);
+  constexpr int KLD = KSWZ ? 64 : (HDP == 96 ? 112 : 80);
+  constexpr int VLD = 64;
   constexpr int KCH = 64 * HD / 8;    // 16-byte chunks per K tile
   constexpr int VCH = HD * 64 / 8;    // 16-byte chunks per V^T tile
   constexpr int KPER = (KCH + 255) / 256;
@@ -134,18 +153,22 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 #define ATT_STORE_K(buf, R)                                                           \
   ATT_CHUNKS(KPER, R, { int c = min(tid + 256 * i, KCH - 1);                             \
-                     *reinterpret_cast<uint4*>(&Ks[buf][(c / (HD / 8)) * KLD + (c % (HD / 8)) * 8]) = r_; })
+                     const int kr_ = key_row(c / (HD / 8));                             \
+                     const int kc_ = c % (HD / 8);                                      \
+                     *reinterpret_cast<uint4*>(&Ks[buf][kr_ * KLD + (KSWZ ? swz(kr_, kc_) : kc_) * 8]) = r_; })
 #define ATT_STORE_V(buf, R)                                                           \
   ATT_CHUNKS(VPER, R, { int c = min(tid + 256 * i, VCH - 1);                             \
-                     *reinterpret_cast<uint4*>(&Vs[buf][(c >> 3) * VLD + (c & 7) * 8]) = r_; })
-  // S^T for one key tile: row lr of block kb reads physical key pk.
+                     *reinterpret_cast<uint4*>(&Vs[buf][(c >> 3) * VLD + swz(c >> 3, c & 7) * 8]) = r_; })
+  // S^T for one key tile: row lr of block kb reads LDS row 16 kb + lr.
 #define ATT_QK(dst, buf)                                                              \
   {                                                                                   \
     _Pragma("unroll") for (int kb = 0; kb < 4; ++kb) {                                \
-      const int pk = 32 * (kb >> 1) + 8 * (lr >> 2) + 4 * (kb & 1) + (lr & 3);        \
+      const int kr = 16 * kb + lr;                                                    \
       bf16x8 kf[KS];                                                                  \
-      _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                               \
-        kf[ks] = *reinterpret_cast<const bf16x8*>(&Ks[buf][pk * KLD + ks * 32 + 8 * lg]); \
+      _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                             \
+        const int ch = ks * 4 + lg;                                                   \
+        kf[ks] = *reinterpret_cast<const bf16x8*>(&Ks[buf][kr * KLD + (KSWZ ? swz(kr, ch) : ch) * 8]); \
+      }                                                                               \
       _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                              \
         f32x4 acc_ = f32x4{0.f, 0.f, 0.f, 0.f};                                       \
         _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                             \
@@ -233,7 +256,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const int vb_ = (kt) & 1;                                                         \
     _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                \
       _Pragma("unroll") for (int db = 0; db < DB; ++db) {                             \
-        bf16x8 vf = *reinterpret_cast<const bf16x8*>(&Vs[vb_][(db * 16 + lr) * VLD + 32 * kk + 8 * lg]); \
+        const int vr_ = db * 16 + lr;                                                 \
+        bf16x8 vf = *reinterpret_cast<const bf16x8*>(&Vs[vb_][vr_ * VLD + swz(vr_, 4 * kk + lg) * 8]); \
         _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                              \
           o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb][kk], o[qb][db], 0, 0, 0); \
       }                                                                               \

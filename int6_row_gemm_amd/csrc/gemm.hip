@@ -11,7 +11,8 @@
 // (a per-row factor of C) is applied in the epilogue as well.
 //
 // Tiling: 256 threads = 4 waves in a 2 x 2 grid; workgroup tile BM x BN,
-// K step 64 through double-buffered LDS with register prefetch; each wave
+// K step 64 through double-buffered, XOR-swizzled LDS with register prefetch
+// two K steps ahead; each wave
 // issues v_mfma_f32_16x16x32_bf16 on (BM/2) x (BN/2).  The accumulator tile
 // is staged through LDS so each epilogue can read rows and columns in the
 // order its output layout wants:
@@ -28,7 +29,13 @@ namespace i6g {
 namespace {
 
 constexpr int BK = 64;
-constexpr int LDK = BK + 8;  // LDS row stride in bf16 elements
+constexpr int LDK = BK;      // LDS row stride in bf16 elements (128 bytes)
+
+// LDS tiles keep 128-byte rows of eight 16-byte chunks; chunk j of row r is
+// stored in slot j ^ ((r >> 1) & 7).  Measured on gfx950, this makes both the
+// MFMA fragment reads (16 rows, one chunk each) and the staging writes free of
+// bank conflicts, where a 16-byte row padding costs a two-way conflict.
+__device__ inline int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 __device__ inline float h2f(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
@@ -57,7 +64,7 @@ __device__ inline int xcd_remap(int bid, int nblocks) {
 
 template <int BM, int BN>
 struct Smem {
-  static constexpr int kAB = 2 * (BM + BN) * LDK * 2;
+  static constexpr int kAB = 2 * (BM + BN) * LDK * 2;   // double-buffered A and B tiles
   static constexpr int kC = BM * (BN + 4) * 4;
   static constexpr int kBytes = kAB > kC ? kAB : kC;
 };
@@ -74,11 +81,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 
   __shared__ __attribute__((aligned(16))) char smem[Smem<BM, BN>::kBytes];
   __shared__ float rinv_s[BM];
+  __shared__ float scale_s[BN];
+  __shared__ float popw_s[BN];
   bf16* As = reinterpret_cast<bf16*>(smem);
   bf16* Bs = As + 2 * BM * LDK;
   float* Cs = reinterpret_cast<float*>(smem);
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x & 255;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int ntn = a.N / BN;
@@ -86,6 +95,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   const int tm = tile / ntn, tn = tile % ntn;
   const int m0 = tm * BM, n0 = tn * BN;
 
+  for (int c = tid; c < BN; c += 256) {
+    scale_s[c] = h2f(a.scale[n0 + c]);
+    if constexpr (EPI == EPI_RES) popw_s[c] = a.pop_w ? a.pop_w[n0 + c] : 0.0f;
+  }
   if constexpr (EPI == EPI_QKV || EPI == EPI_RELU2) {
     for (int r = tid; r < BM; r += 256) {
       int m = m0 + r;
@@ -99,66 +112,58 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     }
   }
 
-  uint4 areg[A_PER];
-  uint4 breg[B_PER];
+  // Global -> register staging, prefetched two K tiles ahead into two sets
+  // of named scalars (arrays of them end up in scratch memory).  Chunk
+  // indices past the tile are clamped (those threads reload and rewrite the
+  // last chunk with identical data); A rows past M are clamped to M - 1 and
+  // their results are never stored.
+  static_assert(A_PER <= 4 && B_PER <= 3, "staging holds 4 A and 3 B chunks per thread");
+  uint4 sa0_0, sa0_1, sa0_2, sa0_3, sb0_0, sb0_1, sb0_2;
+  uint4 sa1_0, sa1_1, sa1_2, sa1_3, sb1_0, sb1_1, sb1_2;
   const int nk = a.K / BK;
 
-  auto load_global = [&](int kt) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      int c = tid + i * 256;
-      areg[i] = make_uint4(0, 0, 0, 0);
-      if (c < A_CHUNKS) {
-        int r = c >> 3, cc = (c & 7) * 8;
-        int m = m0 + r;
-        if (m < a.M)
-          areg[i] = *reinterpret_cast<const uint4*>(a.A + (int64_t)m * a.K + k0 + cc);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-      int c = tid + i * 256;
-      if (c < B_CHUNKS) {
-        int r = c >> 2, cc = (c & 3) * 16;
-        breg[i] = *reinterpret_cast<const uint4*>(a.B + (int64_t)(n0 + r) * a.K + k0 + cc);
-      }
-    }
-  };
-
-  auto store_lds = [&](int buf) {
-    bf16* as = As + buf * BM * LDK;
-    bf16* bs = Bs + buf * BN * LDK;
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      int c = tid + i * 256;
-      if (c < A_CHUNKS) {
-        int r = c >> 3, cc = (c & 7) * 8;
-        *reinterpret_cast<uint4*>(as + r * LDK + cc) = areg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-      int c = tid + i * 256;
-      if (c < B_CHUNKS) {
-        int r = c >> 2, cc = (c & 3) * 16;
-        const uint32_t w[4] = {breg[i].x, breg[i].y, breg[i].z, breg[i].w};
-        uint32_t o[8];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          int b0 = (int)(int8_t)(w[j] & 0xff);
-          int b1 = (int)(int8_t)((w[j] >> 8) & 0xff);
-          int b2 = (int)(int8_t)((w[j] >> 16) & 0xff);
-          int b3 = (int)(int8_t)(w[j] >> 24);
-          o[2 * j] = pack_bf16x2_from_int(b0, b1);
-          o[2 * j + 1] = pack_bf16x2_from_int(b2, b3);
-        }
-        uint4* dst = reinterpret_cast<uint4*>(bs + r * LDK + cc);
-        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-      }
-    }
-  };
+#define GM_A(i, R)                                                                    \
+  if constexpr (A_PER > i) {                                                          \
+    int c = min(tid + (i) * 256, A_CHUNKS - 1);                                       \
+    int m = min(m0 + (c >> 3), a.M - 1);                                              \
+    R = *reinterpret_cast<const uint4*>(a.A + (int64_t)m * a.K + k0_ + (c & 7) * 8);  \
+  }
+#define GM_B(i, R)                                                                    \
+  if constexpr (B_PER > i) {                                                          \
+    int c = min(tid + (i) * 256, B_CHUNKS - 1);                                       \
+    R = *reinterpret_cast<const uint4*>(a.B + (int64_t)(n0 + (c >> 2)) * a.K + k0_ + (c & 3) * 16); \
+  }
+#define GM_LOAD(kt, S)                                                                \
+  {                                                                                   \
+    const int k0_ = (kt) * BK;                                                        \
+    GM_A(0, sa##S##_0) GM_A(1, sa##S##_1) GM_A(2, sa##S##_2) GM_A(3, sa##S##_3)       \
+    GM_B(0, sb##S##_0) GM_B(1, sb##S##_1) GM_B(2, sb##S##_2)                          \
+  }
+#define GM_SA(i, R, as)                                                               \
+  if constexpr (A_PER > i) {                                                          \
+    int c = min(tid + (i) * 256, A_CHUNKS - 1);                                       \
+    *reinterpret_cast<uint4*>(as + (c >> 3) * LDK + swz(c >> 3, c & 7) * 8) = R;      \
+  }
+#define GM_SB(i, R, bs)                                                               \
+  if constexpr (B_PER > i) {                                                          \
+    int c = min(tid + (i) * 256, B_CHUNKS - 1);                                       \
+    const uint32_t w_[4] = {R.x, R.y, R.z, R.w};                                      \
+    uint32_t o_[8];                                                                   \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                   \
+      o_[2 * j] = pack_bf16x2_from_int((int)(int8_t)(w_[j] & 0xff), (int)(int8_t)((w_[j] >> 8) & 0xff)); \
+      o_[2 * j + 1] = pack_bf16x2_from_int((int)(int8_t)((w_[j] >> 16) & 0xff), (int)(int8_t)(w_[j] >> 24)); \
+    }                                                                                 \
+    const int r_ = c >> 2, j_ = (c & 3) * 2;                                          \
+    *reinterpret_cast<uint4*>(bs + r_ * LDK + swz(r_, j_) * 8) = make_uint4(o_[0], o_[1], o_[2], o_[3]); \
+    *reinterpret_cast<uint4*>(bs + r_ * LDK + swz(r_, j_ + 1) * 8) = make_uint4(o_[4], o_[5], o_[6], o_[7]); \
+  }
+#define GM_STORE(buf, S)                                                              \
+  {                                                                                   \
+    bf16* as_ = As + (buf) * BM * LDK;                                                \
+    bf16* bs_ = Bs + (buf) * BN * LDK;                                                \
+    GM_SA(0, sa##S##_0, as_) GM_SA(1, sa##S##_1, as_) GM_SA(2, sa##S##_2, as_) GM_SA(3, sa##S##_3, as_) \
+    GM_SB(0, sb##S##_0, bs_) GM_SB(1, sb##S##_1, bs_) GM_SB(2, sb##S##_2, bs_)        \
+  }
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -166,34 +171,52 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-
-  const int lr = lane & 15, lk = (lane >> 4) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_global(kt + 1);
-    const bf16* as = As + buf * BM * LDK;
-    const bf16* bs = Bs + buf * BN * LDK;
-#pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8 af[FM], bfg[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(as + (wm * WM + i * 16 + lr) * LDK + ks * 32 + lk);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfg[j] = *reinterpret_cast<const bf16x8*>(bs + (wn * WN + j * 16 + lr) * LDK + ks * 32 + lk);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfg[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_lds(buf ^ 1);
-    __syncthreads();
+  const int lr = lane & 15, lg = lane >> 4;
+#define GM_COMPUTE(buf)                                                               \
+  {                                                                                   \
+    const bf16* as = As + (buf) * BM * LDK;                                           \
+    const bf16* bs = Bs + (buf) * BN * LDK;                                           \
+    _Pragma("unroll") for (int ks = 0; ks < BK / 32; ++ks) {                          \
+      bf16x8 af[FM], bfg[FN];                                                         \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                \
+        const int r_ = wm * WM + i * 16 + lr;                                         \
+        af[i] = *reinterpret_cast<const bf16x8*>(as + r_ * LDK + swz(r_, ks * 4 + lg) * 8); \
+      }                                                                               \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                \
+        const int r_ = wn * WN + j * 16 + lr;                                         \
+        bfg[j] = *reinterpret_cast<const bf16x8*>(bs + r_ * LDK + swz(r_, ks * 4 + lg) * 8); \
+      }                                                                               \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i)                                  \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j)                                \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfg[j], acc[i][j], 0, 0, 0); \
+    }                                                                                 \
   }
+  // one K tile: load tile kt+2 into set L, compute tile kt, store tile kt+1
+  // (loaded one step earlier into set S) into the other LDS buffer
+#define GM_STEP(kt, L, S)                                                             \
+  {                                                                                   \
+    GM_LOAD(min((kt) + 2, nk - 1), L);                                                \
+    GM_COMPUTE((kt) & 1);                                                             \
+    if ((kt) + 1 < nk) GM_STORE(((kt) + 1) & 1, S);                                   \
+    __syncthreads();                                                                  \
+  }
+
+  GM_LOAD(0, 0);
+  GM_STORE(0, 0);
+  GM_LOAD(min(1, nk - 1), 1);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    GM_STEP(kt, 0, 1);
+    if (kt + 1 < nk) GM_STEP(kt + 1, 1, 0);
+  }
+#undef GM_STEP
+#undef GM_COMPUTE
+#undef GM_STORE
+#undef GM_SB
+#undef GM_SA
+#undef GM_LOAD
+#undef GM_B
+#undef GM_A
 
   // Stage the accumulators: lane holds column (lane & 15), rows 4*(lane>>4)+e.
 #pragma unroll
@@ -208,60 +231,69 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       }
   __syncthreads();
 
+  // Epilogues: each unit of work is 8 consecutive outputs; the unit loops
+  // have compile-time trip counts and are unrolled so their global loads
+  // are all in flight together.
   if constexpr (EPI == EPI_RELU2) {
     constexpr int UPR = BN / 8;
-    for (int u = tid; u < BM * UPR; u += 256) {
-      int r = u / UPR, c8 = (u % UPR) * 8;
-      int m = m0 + r;
+    static_assert((BM * UPR) % 256 == 0, "unit count");
+#pragma unroll
+    for (int it = 0; it < BM * UPR / 256; ++it) {
+      const int u = tid + it * 256;
+      const int r = u / UPR, c8 = (u % UPR) * 8;
+      const int m = m0 + r;
       if (m >= a.M) continue;
-      float ri = rinv_s[r];
+      const float ri = rinv_s[r];
       uint32_t o[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        float v0 = Cs[r * CLD + c8 + e] * h2f(a.scale[n0 + c8 + e]) * ri;
-        float v1 = Cs[r * CLD + c8 + e + 1] * h2f(a.scale[n0 + c8 + e + 1]) * ri;
-        v0 = fmaxf(v0, 0.0f); v1 = fmaxf(v1, 0.0f);
-        v0 = v0 * v0; v1 = v1 * v1;
-        o[e / 2] = (uint32_t)f2bf_bits(v0) | ((uint32_t)f2bf_bits(v1) << 16);
+        float v0 = fmaxf(Cs[r * CLD + c8 + e] * scale_s[c8 + e] * ri, 0.0f);
+        float v1 = fmaxf(Cs[r * CLD + c8 + e + 1] * scale_s[c8 + e + 1] * ri, 0.0f);
+        o[e / 2] = (uint32_t)f2bf_bits(v0 * v0) | ((uint32_t)f2bf_bits(v1 * v1) << 16);
       }
       *reinterpret_cast<uint4*>(a.h + (int64_t)m * a.N + n0 + c8) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   } else if constexpr (EPI == EPI_RES) {
-    constexpr int UPR = BN / 8;   // 16 threads per row for BN = 128
+    constexpr int UPR = BN / 8;   // 16 consecutive lanes hold one row
     static_assert(BN == 128, "residual epilogue assumes 128-column tiles");
-    for (int u = tid; u < BM * UPR; u += 256) {
-      int r = u / UPR, c8 = (u % UPR) * 8;
-      int m = m0 + r;
-      bool ok = m < a.M;
+    const bool push = a.push_dst != nullptr;
+    const bool pop = a.pop_src != nullptr;
+    const bool pop_self = pop && a.pop_src == a.push_dst;
+#pragma unroll
+    for (int it = 0; it < BM * UPR / 256; ++it) {
+      const int u = tid + it * 256;
+      const int r = u / UPR, c8 = (u % UPR) * 8;
+      const int m = min(m0 + r, a.M - 1);     // rows past M recompute row M-1, store nothing
+      const bool ok = m0 + r < a.M;
+      const int64_t off = (int64_t)m * a.N + n0 + c8;
+      const float4* xp = reinterpret_cast<const float4*>(a.x + off);
+      const float4 x0 = xp[0], x1 = xp[1];
+      float xn[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xn[e] += Cs[r * CLD + c8 + e] * scale_s[c8 + e];
+      if (push && ok) {
+        float4* pd = reinterpret_cast<float4*>(a.push_dst + off);
+        pd[0] = make_float4(xn[0], xn[1], xn[2], xn[3]);
+        pd[1] = make_float4(xn[4], xn[5], xn[6], xn[7]);
+      }
+      if (pop) {
+        float pv[8];
+        if (pop_self) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] = xn[e];
+        } else {
+          const float4* pp = reinterpret_cast<const float4*>(a.pop_src + off);
+          const float4 p0 = pp[0], p1 = pp[1];
+          pv[0] = p0.x; pv[1] = p0.y; pv[2] = p0.z; pv[3] = p0.w;
+          pv[4] = p1.x; pv[5] = p1.y; pv[6] = p1.z; pv[7] = p1.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xn[e] += popw_s[c8 + e] * pv[e];
+      }
       float sq = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sq += xn[e] * xn[e];
       if (ok) {
-        int64_t off = (int64_t)m * a.N + n0 + c8;
-        float xn[8];
-        const float4* xp = reinterpret_cast<const float4*>(a.x + off);
-        float4 x0 = xp[0], x1 = xp[1];
-        float xo[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          xn[e] = xo[e] + Cs[r * CLD + c8 + e] * h2f(a.scale[n0 + c8 + e]);
-        if (a.push_dst) {
-          float4* pd = reinterpret_cast<float4*>(a.push_dst + off);
-          pd[0] = make_float4(xn[0], xn[1], xn[2], xn[3]);
-          pd[1] = make_float4(xn[4], xn[5], xn[6], xn[7]);
-        }
-        if (a.pop_src) {
-          float pv[8];
-          if (a.pop_src == a.push_dst) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pv[e] = xn[e];
-          } else {
-            const float4* pp = reinterpret_cast<const float4*>(a.pop_src + off);
-            float4 p0 = pp[0], p1 = pp[1];
-            pv[0] = p0.x; pv[1] = p0.y; pv[2] = p0.z; pv[3] = p0.w;
-            pv[4] = p1.x; pv[5] = p1.y; pv[6] = p1.z; pv[7] = p1.w;
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xn[e] += a.pop_w[n0 + c8 + e] * pv[e];
-        }
         float4* xw = reinterpret_cast<float4*>(a.x + off);
         xw[0] = make_float4(xn[0], xn[1], xn[2], xn[3]);
         xw[1] = make_float4(xn[4], xn[5], xn[6], xn[7]);
@@ -272,95 +304,102 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
             o[e / 2] = (uint32_t)f2bf_bits(xn[e]) | ((uint32_t)f2bf_bits(xn[e + 1]) << 16);
           *reinterpret_cast<uint4*>(a.xb + off) = make_uint4(o[0], o[1], o[2], o[3]);
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sq += xn[e] * xn[e];
       }
-      // 16 consecutive lanes hold one row: reduce their partial sums.
       sq += __shfl_xor(sq, 1);
       sq += __shfl_xor(sq, 2);
       sq += __shfl_xor(sq, 4);
       sq += __shfl_xor(sq, 8);
       if (ok && a.ss_out && (u % UPR) == 0) a.ss_out[(int64_t)m * (a.N / 128) + tn] = sq;
     }
-  } else {  // EPI_QKV
-    const int hd = a.hd, half = hd / 2;
-    const int dq = a.n_heads * hd, dkv = a.n_kv * hd;
+  } else {  // EPI_QKV: BN = 2 * head_dim, so a tile holds two whole heads
+    constexpr int HDT = BN / 2, HALF = HDT / 2;
+    const int dq = a.n_heads * HDT, dkv = a.n_kv * HDT;
     if (n0 < dq + dkv) {
       // q or k heads: units of (row, head in tile, 4 rotation pairs)
       const bool is_q = n0 < dq;
-      const int heads_in_tile = BN / hd;
-      const int cpr = half / 4;                 // pair chunks per head
-      const int upr = heads_in_tile * cpr;      // units per row
-      for (int u = tid; u < BM * upr; u += 256) {
-        int r = u / upr, rem = u % upr;
-        int hh = rem / cpr, i0 = (rem % cpr) * 4;
-        int m = m0 + r;
+      constexpr int CPR = HALF / 4;             // pair chunks per head
+      constexpr int UPR = 2 * CPR;              // units per row
+      static_assert((BM * UPR) % 256 == 0, "unit count");
+      const int head0 = (is_q ? n0 : n0 - dq) / HDT;
+      const int nh = is_q ? a.n_heads : a.n_kv;
+      bf16* const base = is_q ? a.q : a.k;
+      const bool lora = is_q && a.lora_u;
+#pragma unroll
+      for (int it = 0; it < BM * UPR / 256; ++it) {
+        const int u = tid + it * 256;
+        const int r = u / UPR, rem = u % UPR;
+        const int hh = rem / CPR, i0 = (rem % CPR) * 4;
+        const int m = m0 + r;
         if (m >= a.M) continue;
-        float ri = rinv_s[r];
-        int w = m / a.Lp, pos = m % a.Lp;
-        int cbase = hh * hd;
+        const float ri = rinv_s[r];
+        const int w = m / a.Lp, pos = m % a.Lp;
+        const int cbase = hh * HDT;
+        const float4 cs01 = *reinterpret_cast<const float4*>(a.rope + pos * HALF + i0);
+        const float4 cs23 = *reinterpret_cast<const float4*>(a.rope + pos * HALF + i0 + 2);
+        const float cs[8] = {cs01.x, cs01.y, cs01.z, cs01.w, cs23.x, cs23.y, cs23.z, cs23.w};
         float x1[4], x2[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          int c1 = cbase + i0 + e, c2 = c1 + half;
-          x1[e] = Cs[r * CLD + c1] * h2f(a.scale[n0 + c1]) * ri;
-          x2[e] = Cs[r * CLD + c2] * h2f(a.scale[n0 + c2]) * ri;
+          const int c1 = cbase + i0 + e, c2 = c1 + HALF;
+          x1[e] = Cs[r * CLD + c1] * scale_s[c1] * ri;
+          x2[e] = Cs[r * CLD + c2] * scale_s[c2] * ri;
         }
-        if (is_q && a.lora_u) {
+        if (lora) {
           const float* uu = a.lora_u + (int64_t)m * 2 * a.lora_r;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            int g1 = n0 + cbase + i0 + e, g2 = g1 + half;
+            const int g1 = n0 + cbase + i0 + e, g2 = g1 + HALF;
             float s1 = 0.f, s2 = 0.f;
             for (int t = 0; t < a.lora_r; ++t) {
               s1 += uu[t] * a.lora_bq[g1 * a.lora_r + t];
               s2 += uu[t] * a.lora_bq[g2 * a.lora_r + t];
             }
-            x1[e] += s1; x2[e] += s2;
+            x1[e] += s1;
+            x2[e] += s2;
           }
         }
         uint16_t y1[4], y2[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float2 cs = a.rope[pos * half + i0 + e];
-          float a1 = x1[e] * cs.x - x2[e] * cs.y;
-          float a2 = x1[e] * cs.y + x2[e] * cs.x;
-          y1[e] = f2bf_bits(a1);
-          y2[e] = f2bf_bits(a2);
+          const float co = cs[2 * e], si = cs[2 * e + 1];
+          y1[e] = f2bf_bits(x1[e] * co - x2[e] * si);
+          y2[e] = f2bf_bits(x1[e] * si + x2[e] * co);
         }
-        int head = (is_q ? n0 : n0 - dq) / hd + hh;
-        int nh = is_q ? a.n_heads : a.n_kv;
-        bf16* dst = (is_q ? a.q : a.k) + (((int64_t)w * nh + head) * a.Lp + pos) * hd;
-        uint2 p1 = make_uint2((uint32_t)y1[0] | ((uint32_t)y1[1] << 16), (uint32_t)y1[2] | ((uint32_t)y1[3] << 16));
-        uint2 p2 = make_uint2((uint32_t)y2[0] | ((uint32_t)y2[1] << 16), (uint32_t)y2[2] | ((uint32_t)y2[3] << 16));
-        *reinterpret_cast<uint2*>(dst + i0) = p1;
-        *reinterpret_cast<uint2*>(dst + half + i0) = p2;
+        bf16* dst = base + (((int64_t)w * nh + head0 + hh) * a.Lp + pos) * HDT;
+        *reinterpret_cast<uint2*>(dst + i0) =
+            make_uint2((uint32_t)y1[0] | ((uint32_t)y1[1] << 16), (uint32_t)y1[2] | ((uint32_t)y1[3] << 16));
+        *reinterpret_cast<uint2*>(dst + HALF + i0) =
+            make_uint2((uint32_t)y2[0] | ((uint32_t)y2[1] << 16), (uint32_t)y2[2] | ((uint32_t)y2[3] << 16));
       }
     } else {
       // v heads, written transposed: units of (column, 8 consecutive rows)
-      const int rcs = BM / 8;
-      for (int u = tid; u < BN * rcs; u += 256) {
-        int rc = u % rcs, c = u / rcs;
-        int r0 = rc * 8;
-        int m = m0 + r0;
+      constexpr int RCS = BM / 8;
+      static_assert((BN * RCS) % 256 == 0, "unit count");
+      const bool lora = a.lora_u != nullptr;
+#pragma unroll
+      for (int it = 0; it < BN * RCS / 256; ++it) {
+        const int u = tid + it * 256;
+        const int rc = u % RCS, c = u / RCS;
+        const int r0 = rc * 8;
+        const int m = m0 + r0;
         if (m >= a.M) continue;          // M is a multiple of 8
-        int nv = n0 + c - dq - dkv;      // column inside the v block
-        int head = nv / hd, dd = nv % hd;
-        float sc = h2f(a.scale[n0 + c]);
+        const int nv = n0 + c - dq - dkv;      // column inside the v block
+        const int head = nv / HDT, dd = nv % HDT;
+        const float sc = scale_s[c];
         uint16_t y[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float v = Cs[(r0 + e) * CLD + c] * sc * rinv_s[r0 + e];
-          if (a.lora_u) {
+          if (lora) {
             const float* uu = a.lora_u + (int64_t)(m + e) * 2 * a.lora_r + a.lora_r;
-            float s = 0.f;
-            for (int t = 0; t < a.lora_r; ++t) s += uu[t] * a.lora_bv[nv * a.lora_r + t];
-            v += s;
+            float sl = 0.f;
+            for (int t = 0; t < a.lora_r; ++t) sl += uu[t] * a.lora_bv[nv * a.lora_r + t];
+            v += sl;
           }
           y[e] = f2bf_bits(v);
         }
-        int w = m / a.Lp, pos = m % a.Lp;
-        bf16* dst = a.vt + (((int64_t)w * a.n_kv + head) * hd + dd) * a.Lp + pos;
+        const int w = m / a.Lp, pos = m % a.Lp;
+        bf16* dst = a.vt + (((int64_t)w * a.n_kv + head) * HDT + dd) * a.Lp + pos;
         *reinterpret_cast<uint4*>(dst) = make_uint4(
             (uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16),
             (uint32_t)y[4] | ((uint32_t)y[5] << 16), (uint32_t)y[6] | ((uint32_t)y[7] << 16));
@@ -381,6 +420,7 @@ hipError_t run(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   switch (epi) {
     case EPI_QKV:
+      // the epilogue takes the head size from the tile width (BN = 2 * hd)
       if (a.hd == 32) return run<128, 64, EPI_QKV>(a, s);
       if (a.hd == 64) return run<128, 128, EPI_QKV>(a, s);
       if (a.hd == 80) return run<128, 160, EPI_QKV>(a, s);
