@@ -110,7 +110,8 @@ typedef struct {
  * [RM] (parallel attention/MLP lanes, looped layers).
  *
  * vocab, d_model, n_heads, n_kv_heads, head_dim, d_ff   model sizes;
- *     d_model = n_heads * head_dim; n_heads = 2 * n_kv_heads;
+ *     d_model = n_heads * head_dim; n_heads = 2 * n_kv_heads; vocab a
+ *     multiple of 64;
  *     head_dim in {32, 64, 80}; d_model and d_ff multiples of 128.
  * rope_base          RoPE base (pairs (i, i + hd/2), theta_i = base^(-2i/hd)).
  * norm_eps           RMSNorm epsilon (no gain).
@@ -213,9 +214,16 @@ const char* i6g_last_error(void);
 int i6g_plan_windows(int64_t n_tokens, int32_t window, int32_t stride, int64_t* n_windows,
                      int64_t* starts, int64_t* ends, int64_t* score_from, int64_t capacity);
 
-/* Windows processed per batch inside i6g_score_tokens (tuning; default chosen
- * from the window length).  0 restores the default. */
-int i6g_set_batch_windows(i6g_model* m, int32_t windows);
+/* Model options (tuning and testing; results do not depend on them beyond
+ * floating-point rounding):
+ *   I6G_OPT_BATCH_WINDOWS  windows per batch in i6g_score_tokens (0 = the
+ *                          default, about 32768 rows per batch);
+ *   I6G_OPT_PRUNE_LAST     1 (default): the final layer computes queries,
+ *                          the output projection and the MLP only for the
+ *                          scored rows; 0: for every row.
+ * Errors: I6G_EINVAL for an unknown option or a value out of range. */
+enum { I6G_OPT_BATCH_WINDOWS = 0, I6G_OPT_PRUNE_LAST = 1 };
+int i6g_set_option(i6g_model* m, int option, int64_t value);
 
 /* Per-launch kernel timing with HIP events, for measurement.  Kernel
  * classes: */

@@ -23,7 +23,7 @@ KERNEL_CLASSES = ["embed", "qkv", "attn", "oproj", "fc", "proj", "head", "reduce
 
 EXPORTED = [
     "i6g_quantize_rows", "i6g_load_model", "i6g_score_tokens", "i6g_model_status",
-    "i6g_free_model", "i6g_last_error", "i6g_plan_windows", "i6g_set_batch_windows",
+    "i6g_free_model", "i6g_last_error", "i6g_plan_windows", "i6g_set_option",
     "i6g_set_timing", "i6g_get_timing",
 ]
 
@@ -79,7 +79,7 @@ def lib():
         L.i6g_free_model.restype = None
         L.i6g_last_error.restype = ctypes.c_char_p
         L.i6g_plan_windows.argtypes = [i64, i32, i32, vp, vp, vp, vp, i64]
-        L.i6g_set_batch_windows.argtypes = [vp, i32]
+        L.i6g_set_option.argtypes = [vp, ctypes.c_int, i64]
         L.i6g_set_timing.argtypes = [vp, ctypes.c_int, ctypes.c_uint32]
         L.i6g_get_timing.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp]
         _lib = L
@@ -209,7 +209,10 @@ class Model:
             self._h = None
 
     def set_batch_windows(self, n):
-        _check(lib().i6g_set_batch_windows(self._h, n))
+        _check(lib().i6g_set_option(self._h, 0, n))
+
+    def set_prune_last(self, on):
+        _check(lib().i6g_set_option(self._h, 1, int(bool(on))))
 
     def score(self, tokens, nbytes, window, stride, nats=None, totals=None, check=True):
         """Score a device token stream; returns (nats [N-1] fp32, totals [4] fp64)

@@ -104,6 +104,7 @@ struct i6g_model {
   DevBuf x, xb, ss, q, k, vt, o, h, slots, lora_u, flags, part_n, part_b;
   int64_t scratch_rows = 0;
   int batch_windows = 0;
+  int prune_last = 1;
   // timing
   bool timing = false;
   uint32_t timing_mask = 0;
@@ -278,7 +279,7 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
   if (!desc) return fail(I6G_EINVAL, "load_model: desc is NULL");
   const i6g_model_desc& D = *desc;
   hipStream_t s = (hipStream_t)stream;
-  if (D.vocab < 16 || D.vocab % 16 || D.d_model < 128 || D.n_heads < 1 || D.n_kv_heads < 1 ||
+  if (D.vocab < 64 || D.vocab % 64 || D.d_model < 128 || D.n_heads < 1 || D.n_kv_heads < 1 ||
       D.head_dim < 1 || D.d_ff < 128 || D.n_unique < 1 || D.n_eff < 1 || !D.schedule || !D.blocks ||
       !D.embed)
     return fail(I6G_EINVAL, "load_model: bad sizes or NULL tensors");
@@ -393,10 +394,18 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
 
 void i6g_free_model(i6g_model* m) { delete m; }
 
-int i6g_set_batch_windows(i6g_model* m, int32_t windows) {
-  if (!m || windows < 0) return fail(I6G_EINVAL, "set_batch_windows");
-  m->batch_windows = windows;
-  return I6G_OK;
+int i6g_set_option(i6g_model* m, int option, int64_t value) {
+  if (!m) return fail(I6G_EINVAL, "set_option: NULL model");
+  switch (option) {
+    case I6G_OPT_BATCH_WINDOWS:
+      if (value < 0 || value > (1 << 20)) return fail(I6G_EINVAL, "set_option: batch windows %lld", (long long)value);
+      m->batch_windows = (int)value;
+      return I6G_OK;
+    case I6G_OPT_PRUNE_LAST:
+      m->prune_last = value != 0;
+      return I6G_OK;
+  }
+  return fail(I6G_EINVAL, "set_option: unknown option %d", option);
 }
 
 int i6g_model_status(i6g_model* m, void* stream) {
@@ -434,12 +443,21 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
   for (int64_t k0 = 0; k0 < K; k0 += Wb) {
     const int W = (int)std::min<int64_t>(Wb, K - k0);
     const int M = W * Lp;
+    // predictions scored by this batch
+    const int64_t p0 = (k0 == 0) ? 0 : window_end(k0 - 1, P, L, S);
+    const int64_t p1 = window_end(k0 + W - 1, P, L, S);
+    const int R = (int)(p1 - p0);
+    // In the final layer only scored rows need queries, the output
+    // projection and the MLP (K and V still come from every row): exact.
+    const bool prune = m->prune_last && R < M;
     // real rows of this batch (for algorithmic FLOP counts)
-    double real_rows = 0, attn_pairs = 0;
+    double real_rows = 0, attn_pairs = 0, attn_pairs_scored = 0;
     for (int64_t k = k0; k < k0 + W; ++k) {
-      double T = (double)(window_end(k, P, L, S) - k * S);
+      const double T = (double)(window_end(k, P, L, S) - k * S);
+      const double j0 = (double)(std::max(k * S, k == 0 ? (int64_t)0 : window_end(k - 1, P, L, S)) - k * S);
       real_rows += T;
       attn_pairs += T * (T + 1) / 2;
+      attn_pairs_scored += (T * (T + 1) - j0 * (j0 + 1)) / 2;
     }
 
     EmbedArgs ea{};
@@ -481,10 +499,12 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
                       [&] { return launch_gemm(EPI_QKV, g, s); })))
         return rc;
 
+      const bool pr = last && prune;
       AttnArgs at{};
       at.q = m->q.as<bf16>(); at.k = m->k.as<bf16>(); at.vt = m->vt.as<bf16>(); at.o = m->o.as<bf16>();
       at.W = W; at.n_heads = m->Hq; at.n_kv = m->Hkv; at.hd = m->hd; at.Lp = Lp; at.scale_log2 = scale_log2;
-      if ((rc = timed(m, I6G_K_ATTN, s, 4.0 * m->hd * m->Hq * attn_pairs,
+      at.prune = pr; at.k0 = k0; at.P = P; at.L = (int32_t)L; at.S = (int32_t)S;
+      if ((rc = timed(m, I6G_K_ATTN, s, 4.0 * m->hd * m->Hq * (pr ? attn_pairs_scored : attn_pairs),
                       real_rows * (2.0 * d + 4.0 * kvd),
                       [&] { return launch_attention(at, s); })))
         return rc;
@@ -509,11 +529,25 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
         gp.pop_src = m->slots.as<float>() + (size_t)m->pop_slot[e + 1] * M * d;
         gp.pop_w = m->skip_w.as<float>() + (size_t)m->pop_before[e + 1] * d;
       }
+      if (pr) {
+        // GEMM row r = prediction p0 + r; o, xb, ss and x are read and
+        // written at the row the prediction occupies in the batch, h is
+        // compact
+        for (GemmArgs* g2 : {&go, &gf, &gp}) {
+          g2->M = R;
+          g2->p0 = p0; g2->k0 = k0; g2->n_win = K; g2->e0 = e0;
+          g2->L = (int32_t)L; g2->S = (int32_t)S; g2->Lp = Lp;
+        }
+        go.a_map = 1; go.e_map = 1;
+        gf.a_map = 1;
+        gp.e_map = 1;
+      }
 
-      const double fl_o = 2.0 * real_rows * d * d, fl_fc = 2.0 * real_rows * F * d;
-      const double by_o = real_rows * (2.0 * d + 4.0 * d * 2 + 2.0 * d) + (double)d * d;
-      const double by_fc = real_rows * (2.0 * d + 2.0 * F) + (double)F * d;
-      const double by_p = real_rows * (2.0 * F + 4.0 * d * 2 + 2.0 * d) + (double)F * d;
+      const double rows_mlp = pr ? (double)R : real_rows;
+      const double fl_o = 2.0 * rows_mlp * d * d, fl_fc = 2.0 * rows_mlp * F * d;
+      const double by_o = rows_mlp * (2.0 * d + 4.0 * d * 2 + 2.0 * d) + (double)d * d;
+      const double by_fc = rows_mlp * (2.0 * d + 2.0 * F) + (double)F * d;
+      const double by_p = rows_mlp * (2.0 * F + 4.0 * d * 2 + 2.0 * d) + (double)F * d;
       auto run_o = [&] {
         return timed(m, I6G_K_OPROJ, s, fl_o, by_o, [&] { return launch_gemm(EPI_RES, go, s); });
       };
@@ -533,12 +567,12 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
     ha.x = m->x.as<float>();
     ha.E = m->embed_f32 ? m->embed16.as<_Float16>() : m->embed.as<_Float16>();
     ha.tokens = tokens_dev; ha.nats = nats_dev;
-    ha.p0 = (k0 == 0) ? 0 : window_end(k0 - 1, P, L, S);
-    ha.p1 = window_end(k0 + W - 1, P, L, S);
+    ha.p0 = p0;
+    ha.p1 = p1;
     ha.k0 = k0; ha.K = K; ha.e0 = e0; ha.L = (int32_t)L; ha.S = (int32_t)S; ha.Lp = Lp; ha.d = d;
     ha.vocab = m->V; ha.eps = eps; ha.flags = m->flags.as<int32_t>();
-    const double R = (double)(ha.p1 - ha.p0);
-    if ((rc = timed(m, I6G_K_HEAD, s, 2.0 * R * m->V * d, R * d * 4.0 + (double)m->V * d * 2,
+    const double Rd = (double)R;
+    if ((rc = timed(m, I6G_K_HEAD, s, 2.0 * Rd * m->V * d, Rd * d * 4.0 + (double)m->V * d * 2,
                     [&] { return launch_head(ha, s); })))
       return rc;
   }

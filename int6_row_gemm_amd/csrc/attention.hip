@@ -101,6 +101,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     (void)nblk;
   }
   const int g = pair % a.n_kv, w = pair / a.n_kv;
+  if (a.prune) {
+    // final layer: window k's first scored position is 0 for k = 0, else
+    // min(L - S, P - kS); query tiles before it are not needed
+    const int64_t k = a.k0 + w;
+    const int64_t j0 = (k == 0) ? 0 : min((int64_t)(a.L - a.S), a.P - k * a.S);
+    if (qt < (int)(j0 / 64)) return;
+  }
   const int head = 2 * g + (wave >> 1);
   const int qbase = qt * 64 + 32 * (wave & 1);
   const int nkt = qt + 1;

@@ -79,26 +79,37 @@ __global__ __launch_bounds__(256) void lora_down_kernel(LoraArgs a) {
 // Tied head + log-softmax cross-entropy on the scored rows of a batch
 // (pwwt.cn "parameter-golf 16MB 极限压缩实战 …": tied input/output embedding;
 // 滑动窗口评估: only the scored positions of a window reach the loss).
-// A workgroup takes 64 scored predictions, 16 per wave.  Each wave normalises
-// its rows into fp16 (final RMSNorm), keeps them as the B operand, and
-// streams the binary16 embedding as the A operand of
-// v_mfma_f32_16x16x32_f16, so logits^T arrive with one row per lane column:
-// the log-sum-exp runs online per lane and is merged over the 4 lane groups
-// at the end.  Logits never reach memory.
+// A workgroup takes 16 scored predictions.  Their rows are normalised (final
+// RMSNorm) into fp16 in LDS and held by every wave as the B operand; the 4
+// waves split the vocabulary and stream the binary16 embedding as the A
+// operand of v_mfma_f32_16x16x32_f16, so logits^T arrive with one prediction
+// per lane column: each lane keeps an online log-sum-exp and the target
+// logit, merged over lane groups and then over the waves through LDS.
+// Logits never reach memory.
+constexpr int HEAD_ROWS = 16;
+
 __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 zs[64 * (640 + 8)];   // [64][d + 8], d <= 640
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(16))) _Float16 zs[HEAD_ROWS * (640 + 8)];   // d <= 640
+  __shared__ float part_m[4][HEAD_ROWS], part_s[4][HEAD_ROWS], part_t[4][HEAD_ROWS];
+  __shared__ int part_g[4][HEAD_ROWS];
+  const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int zld = a.d + 8;
-  const int64_t pw = a.p0 + (int64_t)blockIdx.x * 64 + wave * 16;
+  const int64_t pb = a.p0 + (int64_t)blockIdx.x * HEAD_ROWS;
 
-  for (int rr = 0; rr < 16; ++rr) {
-    const int64_t p = pw + rr;
-    _Float16* zrow = zs + (wave * 16 + rr) * zld;
+  // final norm of 4 rows per wave
+  for (int rr = wave * 4; rr < wave * 4 + 4; ++rr) {
+    const int64_t p = pb + rr;
+    _Float16* zrow = zs + rr * zld;
     if (p < a.p1) {
-      int64_t k = (p < a.e0) ? 0 : (p - a.L) / a.S + 1;
-      if (k > a.K - 1) k = a.K - 1;
-      const int64_t row = (k - a.k0) * a.Lp + (p - k * a.S);
+      int64_t row;
+      if (a.compact) {
+        row = p - a.p0;
+      } else {
+        int64_t k = (p < a.e0) ? 0 : (p - a.L) / a.S + 1;
+        if (k > a.K - 1) k = a.K - 1;
+        row = (k - a.k0) * a.Lp + (p - k * a.S);
+      }
       const float* xr = a.x + row * a.d;
       float sq = 0.f;
       for (int c = lane; c < a.d; c += 64) sq += xr[c] * xr[c];
@@ -111,11 +122,11 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
   }
   __syncthreads();
 
-  const int64_t p_mine = pw + lr;
+  const int64_t p_mine = pb + lr;
   const bool have = p_mine < a.p1;
   int tgt = have ? a.tokens[p_mine + 1] : -1;
   if (have && (tgt < 0 || tgt >= a.vocab)) {
-    if (lg == 0) atomicOr(a.flags, 2);
+    if (lg == 0 && wave == 0) atomicOr(a.flags, 2);
     tgt = -1;
   }
 
@@ -123,12 +134,13 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
   f16x8 zf[20];
 #pragma unroll
   for (int ks = 0; ks < 20; ++ks)
-    if (ks < nks)
-      zf[ks] = *reinterpret_cast<const f16x8*>(zs + (wave * 16 + lr) * zld + ks * 32 + 8 * lg);
+    if (ks < nks) zf[ks] = *reinterpret_cast<const f16x8*>(zs + lr * zld + ks * 32 + 8 * lg);
 
+  const int vper = a.vocab / 4;
+  const int vlo = wave * vper, vhi = vlo + vper;
   float mrun = -1e30f, srun = 0.f, tl = 0.f;
   int got = 0;
-  for (int vb = 0; vb < a.vocab; vb += 16) {
+  for (int vb = vlo; vb < vhi; vb += 16) {
     const _Float16* er = a.E + (int64_t)(vb + lr) * a.d + 8 * lg;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -138,29 +150,46 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ef, zf[ks], acc, 0, 0, 0);
       }
     const int vbase = vb + 4 * lg;
-    float mt = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
-    float mn = fmaxf(mrun, mt);
-    srun = srun * expf(mrun - mn) + expf(acc[0] - mn) + expf(acc[1] - mn) +
-           expf(acc[2] - mn) + expf(acc[3] - mn);
+    const float mt = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+    const float mn = fmaxf(mrun, mt);
+    srun = srun * expf(mrun - mn) + expf(acc[0] - mn) + expf(acc[1] - mn) + expf(acc[2] - mn) +
+           expf(acc[3] - mn);
     mrun = mn;
     if (tgt >= vbase && tgt < vbase + 4) {
-      int i = tgt - vbase;
+      const int i = tgt - vbase;
       tl = (i == 0) ? acc[0] : (i == 1) ? acc[1] : (i == 2) ? acc[2] : acc[3];
       got = 1;
     }
   }
 #pragma unroll
   for (int off = 16; off < 64; off <<= 1) {
-    float mo = __shfl_xor(mrun, off);
-    float so = __shfl_xor(srun, off);
-    float to = __shfl_xor(tl, off);
-    int go = __shfl_xor(got, off);
-    float mn = fmaxf(mrun, mo);
+    const float mo = __shfl_xor(mrun, off);
+    const float so = __shfl_xor(srun, off);
+    const float to = __shfl_xor(tl, off);
+    const int go = __shfl_xor(got, off);
+    const float mn = fmaxf(mrun, mo);
     srun = srun * expf(mrun - mn) + so * expf(mo - mn);
     mrun = mn;
     if (go) { tl = to; got = 1; }
   }
-  if (have && lg == 0) a.nats[p_mine] = mrun + logf(srun) - tl;
+  if (lg == 0) {
+    part_m[wave][lr] = mrun;
+    part_s[wave][lr] = srun;
+    part_t[wave][lr] = tl;
+    part_g[wave][lr] = got;
+  }
+  __syncthreads();
+  if (wave == 0 && lg == 0 && have) {
+    float m = part_m[0][lr], s = part_s[0][lr], t = got ? tl : 0.f;
+    for (int w2 = 1; w2 < 4; ++w2) {
+      const float mo = part_m[w2][lr];
+      const float mn = fmaxf(m, mo);
+      s = s * expf(m - mn) + part_s[w2][lr] * expf(mo - mn);
+      m = mn;
+      if (part_g[w2][lr]) t = part_t[w2][lr];
+    }
+    a.nats[p_mine] = m + logf(s) - t;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -258,10 +287,10 @@ hipError_t launch_lora_down(const LoraArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_head(const HeadArgs& a, hipStream_t s) {
-  if (a.d % 32 != 0 || a.d > 640 || a.vocab % 16 != 0) return hipErrorInvalidValue;
+  if (a.d % 32 != 0 || a.d > 640 || a.vocab % 64 != 0) return hipErrorInvalidValue;
   int64_t rows = a.p1 - a.p0;
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(head_kernel, dim3(nblk(rows, 64)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(head_kernel, dim3(nblk(rows, HEAD_ROWS)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

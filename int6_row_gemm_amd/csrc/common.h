@@ -63,8 +63,23 @@ struct GemmArgs {
   float* push_dst;        // [M, N] skip slot to store the new x into (or null)
   const float* pop_src;   // [M, N] skip slot to add (or null); may equal push_dst
   const float* pop_w;     // [N] fp32 skip weight
+  // Scored-rows mode (final layer): GEMM row r stands for prediction p0 + r,
+  // whose row in the batch layout is RowMap::row(r).  a_map maps the A rows
+  // (and ss_in); e_map maps the epilogue's x / xb / ss / skip rows.
+  int32_t a_map, e_map;
+  int64_t p0, k0, n_win, e0;
+  int32_t L, S;
 };
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
+
+// Row of prediction p in a batch of windows k0.. laid out Lp rows apart:
+// window k scores p in [max(kS, e_{k-1}), e_k); window 0 ends at e0.
+__host__ __device__ inline int64_t scored_row(int64_t p, int64_t k0, int64_t n_win, int64_t e0,
+                                              int32_t L, int32_t S, int32_t Lp) {
+  int64_t k = (p < e0) ? 0 : (p - L) / S + 1;
+  if (k > n_win - 1) k = n_win - 1;
+  return (k - k0) * Lp + (p - k * S);
+}
 
 // ---------------------------------------------------------------------------
 // Causal GQA attention over a batch of windows.
@@ -75,6 +90,10 @@ struct AttnArgs {
   bf16* o;         // [W*Lp, Hq*hd]
   int32_t W, n_heads, n_kv, hd, Lp;
   float scale_log2;  // log2(e) / sqrt(hd)
+  // final layer: only query tiles holding scored positions are computed
+  int32_t prune;
+  int64_t k0, P;
+  int32_t L, S;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
@@ -114,6 +133,7 @@ struct HeadArgs {
   int32_t L, S, Lp, d, vocab;
   float eps;
   int32_t* flags;
+  int32_t compact;       // 1: row of prediction p is p - p0 (pruned last layer)
 };
 hipError_t launch_head(const HeadArgs& a, hipStream_t s);
 

@@ -104,8 +104,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       int m = m0 + r;
       float v = 0.0f;
       if (m < a.M) {
+        const int64_t mr = a.a_map ? scored_row(a.p0 + m, a.k0, a.n_win, a.e0, a.L, a.S, a.Lp) : m;
         float ss = 0.0f;
-        for (int t = 0; t < a.nt_in; ++t) ss += a.ss_in[(int64_t)m * a.nt_in + t];
+        for (int t = 0; t < a.nt_in; ++t) ss += a.ss_in[mr * a.nt_in + t];
         v = 1.0f / sqrtf(ss / (float)a.K + a.eps);
       }
       rinv_s[r] = v;
@@ -121,12 +122,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   uint4 sa0_0, sa0_1, sa0_2, sa0_3, sb0_0, sb0_1, sb0_2;
   uint4 sa1_0, sa1_1, sa1_2, sa1_3, sb1_0, sb1_1, sb1_2;
   const int nk = a.K / BK;
+  // element offset of each A row this thread loads, for the whole K loop
+  int64_t arow0 = 0, arow1 = 0, arow2 = 0, arow3 = 0;
+#define GM_AROW(i, V)                                                                 \
+  if constexpr (A_PER > i) {                                                          \
+    const int c = min(tid + (i) * 256, A_CHUNKS - 1);                                 \
+    const int m = min(m0 + (c >> 3), a.M - 1);                                        \
+    V = (a.a_map ? scored_row(a.p0 + m, a.k0, a.n_win, a.e0, a.L, a.S, a.Lp) : m) * (int64_t)a.K; \
+  }
+  GM_AROW(0, arow0) GM_AROW(1, arow1) GM_AROW(2, arow2) GM_AROW(3, arow3)
+#undef GM_AROW
 
 #define GM_A(i, R)                                                                    \
   if constexpr (A_PER > i) {                                                          \
     int c = min(tid + (i) * 256, A_CHUNKS - 1);                                       \
-    int m = min(m0 + (c >> 3), a.M - 1);                                              \
-    R = *reinterpret_cast<const uint4*>(a.A + (int64_t)m * a.K + k0_ + (c & 7) * 8);  \
+    R = *reinterpret_cast<const uint4*>(a.A + arow##i + k0_ + (c & 7) * 8);           \
   }
 #define GM_B(i, R)                                                                    \
   if constexpr (B_PER > i) {                                                          \
@@ -265,7 +275,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       const int r = u / UPR, c8 = (u % UPR) * 8;
       const int m = min(m0 + r, a.M - 1);     // rows past M recompute row M-1, store nothing
       const bool ok = m0 + r < a.M;
-      const int64_t off = (int64_t)m * a.N + n0 + c8;
+      const int64_t mr = a.e_map ? scored_row(a.p0 + m, a.k0, a.n_win, a.e0, a.L, a.S, a.Lp) : m;
+      const int64_t off = mr * a.N + n0 + c8;
       const float4* xp = reinterpret_cast<const float4*>(a.x + off);
       const float4 x0 = xp[0], x1 = xp[1];
       float xn[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
@@ -309,7 +320,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       sq += __shfl_xor(sq, 2);
       sq += __shfl_xor(sq, 4);
       sq += __shfl_xor(sq, 8);
-      if (ok && a.ss_out && (u % UPR) == 0) a.ss_out[(int64_t)m * (a.N / 128) + tn] = sq;
+      if (ok && a.ss_out && (u % UPR) == 0) a.ss_out[mr * (a.N / 128) + tn] = sq;
     }
   } else {  // EPI_QKV: BN = 2 * head_dim, so a tile holds two whole heads
     constexpr int HDT = BN / 2, HALF = HDT / 2;

@@ -142,3 +142,23 @@ def test_full_size_sampled(name, sample):
     compare_nats(nats, ref, mask=mask, label=f"{name} sampled windows {sample}")
     if sample is None:
         assert abs(totals[3] - ow.bpb(ref, nbytes)) <= BPB_ATOL
+
+
+@pytest.mark.parametrize("name,L,S,N", [("11l", 256, 64, 1000), ("largevocab", 200, 50, 700),
+                                        ("midcycle", 256, 32, 600), ("tiny", 256, 64, 700)])
+def test_final_layer_pruning_is_exact(name, L, S, N):
+    """Computing queries, output projection and MLP of the final layer only
+    for scored rows must give the same bits as computing every row."""
+    import torch
+    g = need_gpu()
+    cfg, model = make_case(name)
+    tokens, nbytes = synth.make_stream(cfg, seed=7, n_tokens=N)
+    print_case("prune", name, L, S, N)
+    gm, _ = gpu_model(g, model)
+    t, b = torch.from_numpy(tokens).cuda(), torch.from_numpy(nbytes).cuda()
+    gm.set_prune_last(True)
+    a, ta = gm.score(t, b, L, S)
+    gm.set_prune_last(False)
+    c, tc = gm.score(t, b, L, S)
+    np.testing.assert_array_equal(a.cpu().numpy(), c.cpu().numpy())
+    assert float(ta[3]) == float(tc[3])
