@@ -64,13 +64,14 @@ __device__ inline int xcd_remap(int bid, int nblocks) {
 
 template <int BM, int BN>
 struct Smem {
-  static constexpr int kAB = 2 * (BM + BN) * LDK * 2;   // double-buffered A and B tiles
-  static constexpr int kC = BM * (BN + 4) * 4;
+  static constexpr int kAB = (BM + BN) * LDK * 2;        // one A and one B tile
+  static constexpr int kC = (BM / 2) * (BN + 4) * 4;     // half of the accumulator tile
   static constexpr int kBytes = kAB > kC ? kAB : kC;
 };
 
 template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BN <= 128 ? 3 : 2)))
+void gemm_kernel(GemmArgs a) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 16, FN = WN / 16;
   constexpr int A_CHUNKS = BM * BK / 8;       // 16-byte chunks of bf16
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   __shared__ float scale_s[BN];
   __shared__ float popw_s[BN];
   bf16* As = reinterpret_cast<bf16*>(smem);
-  bf16* Bs = As + 2 * BM * LDK;
+  bf16* Bs = As + BM * LDK;
   float* Cs = reinterpret_cast<float*>(smem);
 
   const int tid = threadIdx.x & 255;
@@ -167,10 +168,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     *reinterpret_cast<uint4*>(bs + r_ * LDK + swz(r_, j_) * 8) = make_uint4(o_[0], o_[1], o_[2], o_[3]); \
     *reinterpret_cast<uint4*>(bs + r_ * LDK + swz(r_, j_ + 1) * 8) = make_uint4(o_[4], o_[5], o_[6], o_[7]); \
   }
-#define GM_STORE(buf, S)                                                              \
+#define GM_STORE(S)                                                                   \
   {                                                                                   \
-    bf16* as_ = As + (buf) * BM * LDK;                                                \
-    bf16* bs_ = Bs + (buf) * BN * LDK;                                                \
+    bf16* as_ = As;                                                                   \
+    bf16* bs_ = Bs;                                                                   \
     GM_SA(0, sa##S##_0, as_) GM_SA(1, sa##S##_1, as_) GM_SA(2, sa##S##_2, as_) GM_SA(3, sa##S##_3, as_) \
     GM_SB(0, sb##S##_0, bs_) GM_SB(1, sb##S##_1, bs_) GM_SB(2, sb##S##_2, bs_)        \
   }
@@ -182,10 +183,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int lr = lane & 15, lg = lane >> 4;
-#define GM_COMPUTE(buf)                                                               \
+#define GM_COMPUTE()                                                                  \
   {                                                                                   \
-    const bf16* as = As + (buf) * BM * LDK;                                           \
-    const bf16* bs = Bs + (buf) * BN * LDK;                                           \
+    const bf16* as = As;                                                              \
+    const bf16* bs = Bs;                                                              \
     _Pragma("unroll") for (int ks = 0; ks < BK / 32; ++ks) {                          \
       bf16x8 af[FM], bfg[FN];                                                         \
       _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                \
@@ -201,18 +202,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfg[j], acc[i][j], 0, 0, 0); \
     }                                                                                 \
   }
-  // one K tile: load tile kt+2 into set L, compute tile kt, store tile kt+1
-  // (loaded one step earlier into set S) into the other LDS buffer
+  // One K tile: issue the loads of tile kt+2 into register set L, multiply
+  // tile kt out of LDS, then replace it with tile kt+1 (set S, loaded one
+  // step earlier).  A single LDS tile keeps the footprint small enough for
+  // three workgroups per CU, whose epilogue stores then overlap the others'
+  // MFMA work.
 #define GM_STEP(kt, L, S)                                                             \
   {                                                                                   \
     GM_LOAD(min((kt) + 2, nk - 1), L);                                                \
-    GM_COMPUTE((kt) & 1);                                                             \
-    if ((kt) + 1 < nk) GM_STORE(((kt) + 1) & 1, S);                                   \
-    __syncthreads();                                                                  \
+    GM_COMPUTE();                                                                     \
+    if ((kt) + 1 < nk) {                                                              \
+      __syncthreads();                                                                \
+      GM_STORE(S);                                                                    \
+      __syncthreads();                                                                \
+    }                                                                                 \
   }
 
   GM_LOAD(0, 0);
-  GM_STORE(0, 0);
+  GM_STORE(0);
   GM_LOAD(min(1, nk - 1), 1);
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
@@ -228,17 +235,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #undef GM_B
 #undef GM_A
 
-  // Stage the accumulators: lane holds column (lane & 15), rows 4*(lane>>4)+e.
+  // The accumulator tile goes through LDS in two halves of BM/2 rows (the
+  // rows of wave row wm == h); lane holds column (lane & 15) and rows
+  // 4*(lane>>4)+e of each 16 x 16 block.
+  constexpr int HR = BM / 2;
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int h = 0; h < 2; ++h) {
+  const int hr0 = h * HR;
+  if (wm == h) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        int r = wm * WM + i * 16 + (lane >> 4) * 4 + e;
-        int c = wn * WN + j * 16 + (lane & 15);
-        Cs[r * CLD + c] = acc[i][j][e];
-      }
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          int r = i * 16 + (lane >> 4) * 4 + e;
+          int c = wn * WN + j * 16 + (lane & 15);
+          Cs[r * CLD + c] = acc[i][j][e];
+        }
+  }
   __syncthreads();
 
   // Epilogues: each unit of work is 8 consecutive outputs; the unit loops
@@ -246,14 +262,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   // are all in flight together.
   if constexpr (EPI == EPI_RELU2) {
     constexpr int UPR = BN / 8;
-    static_assert((BM * UPR) % 256 == 0, "unit count");
+    static_assert((HR * UPR) % 256 == 0, "unit count");
 #pragma unroll
-    for (int it = 0; it < BM * UPR / 256; ++it) {
+    for (int it = 0; it < HR * UPR / 256; ++it) {
       const int u = tid + it * 256;
       const int r = u / UPR, c8 = (u % UPR) * 8;
-      const int m = m0 + r;
+      const int m = m0 + hr0 + r;
       if (m >= a.M) continue;
-      const float ri = rinv_s[r];
+      const float ri = rinv_s[hr0 + r];
       uint32_t o[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
@@ -270,11 +286,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     const bool pop = a.pop_src != nullptr;
     const bool pop_self = pop && a.pop_src == a.push_dst;
 #pragma unroll
-    for (int it = 0; it < BM * UPR / 256; ++it) {
+    for (int it = 0; it < HR * UPR / 256; ++it) {
       const int u = tid + it * 256;
       const int r = u / UPR, c8 = (u % UPR) * 8;
-      const int m = min(m0 + r, a.M - 1);     // rows past M recompute row M-1, store nothing
-      const bool ok = m0 + r < a.M;
+      const int m = min(m0 + hr0 + r, a.M - 1);  // rows past M recompute row M-1, store nothing
+      const bool ok = m0 + hr0 + r < a.M;
       const int64_t mr = a.e_map ? scored_row(a.p0 + m, a.k0, a.n_win, a.e0, a.L, a.S, a.Lp) : m;
       const int64_t off = mr * a.N + n0 + c8;
       const float4* xp = reinterpret_cast<const float4*>(a.x + off);
@@ -330,19 +346,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       const bool is_q = n0 < dq;
       constexpr int CPR = HALF / 4;             // pair chunks per head
       constexpr int UPR = 2 * CPR;              // units per row
-      static_assert((BM * UPR) % 256 == 0, "unit count");
+      static_assert((HR * UPR) % 256 == 0, "unit count");
       const int head0 = (is_q ? n0 : n0 - dq) / HDT;
       const int nh = is_q ? a.n_heads : a.n_kv;
       bf16* const base = is_q ? a.q : a.k;
       const bool lora = is_q && a.lora_u;
 #pragma unroll
-      for (int it = 0; it < BM * UPR / 256; ++it) {
+      for (int it = 0; it < HR * UPR / 256; ++it) {
         const int u = tid + it * 256;
         const int r = u / UPR, rem = u % UPR;
         const int hh = rem / CPR, i0 = (rem % CPR) * 4;
-        const int m = m0 + r;
+        const int m = m0 + hr0 + r;
         if (m >= a.M) continue;
-        const float ri = rinv_s[r];
+        const float ri = rinv_s[hr0 + r];
         const int w = m / a.Lp, pos = m % a.Lp;
         const int cbase = hh * HDT;
         const float4 cs01 = *reinterpret_cast<const float4*>(a.rope + pos * HALF + i0);
@@ -384,7 +400,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       }
     } else {
       // v heads, written transposed: units of (column, 8 consecutive rows)
-      constexpr int RCS = BM / 8;
+      constexpr int RCS = HR / 8;
       static_assert((BN * RCS) % 256 == 0, "unit count");
       const bool lora = a.lora_u != nullptr;
 #pragma unroll
@@ -392,7 +408,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         const int u = tid + it * 256;
         const int rc = u % RCS, c = u / RCS;
         const int r0 = rc * 8;
-        const int m = m0 + r0;
+        const int m = m0 + hr0 + r0;
         if (m >= a.M) continue;          // M is a multiple of 8
         const int nv = n0 + c - dq - dkv;      // column inside the v block
         const int head = nv / HDT, dd = nv % HDT;
@@ -400,7 +416,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         uint16_t y[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float v = Cs[(r0 + e) * CLD + c] * sc * rinv_s[r0 + e];
+          float v = Cs[(r0 + e) * CLD + c] * sc * rinv_s[hr0 + r0 + e];
           if (lora) {
             const float* uu = a.lora_u + (int64_t)(m + e) * 2 * a.lora_r + a.lora_r;
             float sl = 0.f;
@@ -417,6 +433,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
       }
     }
   }
+  __syncthreads();
+  }  // halves
 }
 
 template <int BM, int BN, int EPI>
