@@ -39,6 +39,12 @@ def parse():
     ap.add_argument("--cpu-windows", type=int, default=4,
                     help="full windows the CPU oracle scores for its baseline (0 = skip)")
     ap.add_argument("--no-timing", action="store_true", help="no per-launch events")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="score a shorter stream (counter runs only; 0 = the full workload)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (to scale the HBM byte counters)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic_11l.md"),
+                    help="summary of the FETCH_SIZE / WRITE_SIZE counter runs (key: value lines)")
     return ap.parse_args()
 
 
@@ -56,11 +62,21 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 4 * n, "launches": 3}), flush=True)
+        return
     cfg = synth.config(args.config)
     arch = cfg["arch"]
     L, S = cfg["window"], cfg["stride"]
     model = synth.make_model(arch, seed=args.seed)
-    tokens_np, nbytes_np = synth.make_stream(cfg, seed=args.seed)
+    tokens_np, nbytes_np = synth.make_stream(cfg, seed=args.seed,
+                                             n_tokens=args.tokens if args.tokens else None)
     N = len(tokens_np)
     P = N - 1
 
@@ -143,8 +159,11 @@ def main():
             ach, peak, unit, bound = k["gbs"], PEAK_HBM_GBS, "GB/s", "hbm"
         else:
             ach, peak, unit, bound = k["tflops"], PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
+        traffic = counter_traffic(args.traffic, dom)
         roofline = {"kernel": dom, "bound": bound, "achieved": ach, "peak": peak, "unit": unit,
-                    "frac": ach / peak, "traffic": None, "avg_launch_us": k["avg_us"]}
+                    "frac": ach / peak, "traffic": traffic, "avg_launch_us": k["avg_us"],
+                    "algorithmic_per_launch": (k["tflops"] * 1e12 * k["avg_us"] * 1e-6)
+                    if unit == "TFLOP/s" else k["gbs"] * 1e9 * k["avg_us"] * 1e-6}
         gsum_ms = sum(kernels[c]["ms_total"] for c in ("qkv", "oproj", "fc", "proj") if c in kernels)
         gsum_fl = sum(kernels[c]["tflops"] * kernels[c]["ms_total"] for c in ("qkv", "oproj", "fc", "proj")
                       if c in kernels)
@@ -178,6 +197,32 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+KERNEL_SOURCES = {"attn": "attention.hip", "qkv": "gemm.hip", "oproj": "gemm.hip", "fc": "gemm.hip",
+                  "proj": "gemm.hip", "head": "aux.hip", "embed": "aux.hip", "reduce": "aux.hip"}
+
+
+def counter_traffic(path, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    import hashlib
+    if not path or not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", "`")):
+            k, v = line.split(":", 1)
+            kv[k.strip().lstrip("- ")] = v.strip().strip("`")
+    src = os.path.join(ROOT, "int6_row_gemm_amd", "csrc", KERNEL_SOURCES.get(kernel, ""))
+    if kv.get("kernel") != kernel or not os.path.exists(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("source_sha256"):
+        return None
+    try:
+        return float(kv["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(model, tokens, L, S, n_windows):

@@ -121,6 +121,7 @@ FULL = [
     ("baseline", [0, 37, 63]),
     ("midcycle", [0, 31]),
     ("11l", [0, 8191, 16352]),
+    ("largevocab", [0, 40000, 65504]),
 ]
 
 
