@@ -23,8 +23,10 @@
 //   ones appended to V^T makes one extra O^T block equal to sum_k P[q, k]
 //   (of the bf16 P actually used), with no VALU adds.
 // * exp is the hardware exp2 with the 1/sqrt(hd) * log2(e) factor folded
-//   into one multiply-add; the rescale of O is skipped when no running max of
-//   the wave moved (its factor is then exactly 1).
+//   into one multiply-add.  Probabilities are taken relative to a reference
+//   max that only moves when a tile max exceeds it by more than 2^8, so the
+//   rescale of O is rare; the causal mask is applied only on the last
+//   (diagonal) tile, which is peeled off the loop.
 // * Software pipelining: the MFMAs of the next key tile's S^T are issued
 //   before the softmax of the current one, so the matrix cores and the VALU
 //   work at the same time.  K tiles run one tile ahead of V tiles through two
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   bf16x8 ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.0f;
-  float mrow[2] = {-1e30f, -1e30f};
+  float mref[2] = {-1e30f, -1e30f};
   const float c = a.scale_log2;
 
   // prologue: S^T of tile 0; LDS then holds K[1] and V[0]
@@ -215,13 +217,20 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 
   // One key tile; SC holds its S^T, SN receives the next tile's.  The
   // register set RL receives K[kt+3] and V[kt+2]; RS (filled one step
-  // earlier) holds K[kt+2] and V[kt+1], written to LDS at the end.
-#define ATT_STEP(kt, SC, SN, KRL, VRL, KRS, VRS)                                      \
+  // earlier) holds K[kt+2] and V[kt+1], written to LDS at the end.  DIAG is
+  // true only for the last tile, the one that straddles the causal diagonal.
+  //
+  // The probabilities use a per-query reference max mref that is only moved
+  // when the tile max exceeds it by more than 2^8 in the exp2 domain (or on
+  // the first tile); otherwise p <= 256 and O, the denominator and the final
+  // O / denominator are unchanged by the choice of reference, so the rescale
+  // of O (and its multiplies) is skipped on almost every tile.
+#define ATT_STEP(kt, SC, SN, KRL, VRL, KRS, VRS, DIAG)                                \
   {                                                                                   \
     ATT_LOAD_K(min((kt) + 3, nkt - 1), KRL);                                          \
     ATT_LOAD_V(min((kt) + 2, nkt - 1), VRL);                                          \
-    if ((kt) + 1 < nkt) ATT_QK(SN, ((kt) + 1) & 1);                                   \
-    if ((kt) == qt) {                                                                 \
+    if (!(DIAG)) ATT_QK(SN, ((kt) + 1) & 1);                                          \
+    if (DIAG) {                                                                       \
       _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                              \
         const int qabs = qbase + 16 * qb + lr;                                        \
         _Pragma("unroll") for (int kb = 0; kb < 4; ++kb)                              \
@@ -231,20 +240,28 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
           }                                                                           \
       }                                                                               \
     }                                                                                 \
-    bf16x8 pf[2][2];                                                                  \
-    float alpha[2];                                                                   \
-    bool moved = false;                                                               \
+    float mt[2];                                                                      \
+    bool grow = false;                                                                \
     _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                                \
-      float mt = SC[qb][0][0];                                                        \
+      float m_ = SC[qb][0][0];                                                        \
       _Pragma("unroll") for (int kb = 0; kb < 4; ++kb)                                \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) mt = __builtin_fmaxf(mt, SC[qb][kb][i]); \
-      mt = max_xor16(mt);                                                             \
-      mt = max_xor32(mt);                                                             \
-      const float mnew = __builtin_fmaxf(mrow[qb], mt);                               \
-      moved |= mnew > mrow[qb];                                                       \
-      alpha[qb] = __builtin_amdgcn_exp2f((mrow[qb] - mnew) * c);                      \
-      const float mc = mnew * c;                                                      \
-      mrow[qb] = mnew;                                                                \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) m_ = __builtin_fmaxf(m_, SC[qb][kb][i]); \
+      m_ = max_xor16(m_);                                                             \
+      mt[qb] = max_xor32(m_);                                                         \
+      grow |= (mt[qb] - mref[qb]) * c > 8.0f;                                         \
+    }                                                                                 \
+    if (__any(grow)) {                                                                \
+      _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                              \
+        const float mnew = __builtin_fmaxf(mref[qb], mt[qb]);                         \
+        const float alpha = __builtin_amdgcn_exp2f((mref[qb] - mnew) * c);            \
+        mref[qb] = mnew;                                                              \
+        _Pragma("unroll") for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;         \
+        osum[qb] *= alpha;                                                            \
+      }                                                                               \
+    }                                                                                 \
+    bf16x8 pf[2][2];                                                                  \
+    _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                                \
+      const float mc = mref[qb] * c;                                                  \
       _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                              \
         bf16x8 v;                                                                     \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                               \
@@ -252,12 +269,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
           v[4 + i] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(SC[qb][2 * kk + 1][i], c, -mc)); \
         }                                                                             \
         pf[qb][kk] = v;                                                               \
-      }                                                                               \
-    }                                                                                 \
-    if (__any(moved)) {                                                               \
-      _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                              \
-        _Pragma("unroll") for (int db = 0; db < DB; ++db) o[qb][db] *= alpha[qb];     \
-        osum[qb] *= alpha[qb];                                                        \
       }                                                                               \
     }                                                                                 \
     const int vb_ = (kt) & 1;                                                         \
@@ -271,16 +282,26 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                                \
         osum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb][kk], osum[qb], 0, 0, 0); \
     }                                                                                 \
-    /* K[kt+2] replaces K[kt] (read by the previous step), V[kt+1] replaces */        \
-    /* V[kt-1]; the barrier publishes both for the next step. */                      \
-    if ((kt) + 2 < nkt) ATT_STORE_K((kt) & 1, KRS);                                   \
-    if ((kt) + 1 < nkt) ATT_STORE_V(((kt) + 1) & 1, VRS);                             \
-    __syncthreads();                                                                  \
+    if (!(DIAG)) {                                                                    \
+      /* K[kt+2] replaces K[kt] (read by the previous step), V[kt+1] */               \
+      /* replaces V[kt-1]; the barrier publishes both for the next step. */           \
+      if ((kt) + 2 < nkt) ATT_STORE_K((kt) & 1, KRS);                                 \
+      ATT_STORE_V(((kt) + 1) & 1, VRS);                                               \
+      __syncthreads();                                                                \
+    }                                                                                 \
   }
 
-  for (int kt = 0; kt < nkt; kt += 2) {
-    ATT_STEP(kt, s_cur, s_nxt, kreg, vreg, kreg2, vreg2);
-    if (kt + 1 < nkt) ATT_STEP(kt + 1, s_nxt, s_cur, kreg2, vreg2, kreg, vreg);
+  // the diagonal tile is the last one (kt = qt): peel it off the loop
+  int kt = 0;
+  for (; kt + 2 < nkt; kt += 2) {
+    ATT_STEP(kt, s_cur, s_nxt, kreg, vreg, kreg2, vreg2, false);
+    ATT_STEP(kt + 1, s_nxt, s_cur, kreg2, vreg2, kreg, vreg, false);
+  }
+  if (nkt - kt == 2) {
+    ATT_STEP(kt, s_cur, s_nxt, kreg, vreg, kreg2, vreg2, false);
+    ATT_STEP(kt + 1, s_nxt, s_cur, kreg2, vreg2, kreg, vreg, true);
+  } else {
+    ATT_STEP(kt, s_cur, s_nxt, kreg, vreg, kreg2, vreg2, true);
   }
 #undef ATT_STEP
 #undef ATT_LOAD_K
