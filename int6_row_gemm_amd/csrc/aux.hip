@@ -88,6 +88,7 @@ __global__ __launch_bounds__(256) void lora_down_kernel(LoraArgs a) {
 // Logits never reach memory.
 constexpr int HEAD_ROWS = 16;
 
+template <int NKS>   // d / 32
 __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 zs[HEAD_ROWS * (640 + 8)];   // d <= 640
   __shared__ float part_m[4][HEAD_ROWS], part_s[4][HEAD_ROWS], part_t[4][HEAD_ROWS];
@@ -130,25 +131,26 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
     tgt = -1;
   }
 
-  const int nks = a.d / 32;
-  f16x8 zf[20];
+  f16x8 zf[NKS];
 #pragma unroll
-  for (int ks = 0; ks < 20; ++ks)
-    if (ks < nks) zf[ks] = *reinterpret_cast<const f16x8*>(zs + lr * zld + ks * 32 + 8 * lg);
+  for (int ks = 0; ks < NKS; ++ks) zf[ks] = *reinterpret_cast<const f16x8*>(zs + lr * zld + ks * 32 + 8 * lg);
 
   const int vper = a.vocab / 4;
   const int vlo = wave * vper, vhi = vlo + vper;
   float mrun = -1e30f, srun = 0.f, tl = 0.f;
   int got = 0;
-  for (int vb = vlo; vb < vhi; vb += 16) {
+  // Embedding fragments of the next vocabulary block are loaded while the
+  // current block is multiplied (two register sets, 16 vocab rows each).
+  f16x8 ea[NKS], eb[NKS];
+  auto load_e = [&](f16x8 (&dst)[NKS], int vb) {
     const _Float16* er = a.E + (int64_t)(vb + lr) * a.d + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) dst[ks] = *reinterpret_cast<const f16x8*>(er + ks * 32);
+  };
+  auto block = [&](const f16x8 (&ef)[NKS], int vb) {
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 20; ++ks)
-      if (ks < nks) {
-        f16x8 ef = *reinterpret_cast<const f16x8*>(er + ks * 32);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ef, zf[ks], acc, 0, 0, 0);
-      }
+    for (int ks = 0; ks < NKS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ef[ks], zf[ks], acc, 0, 0, 0);
     const int vbase = vb + 4 * lg;
     const float mt = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
     const float mn = fmaxf(mrun, mt);
@@ -159,6 +161,15 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
       const int i = tgt - vbase;
       tl = (i == 0) ? acc[0] : (i == 1) ? acc[1] : (i == 2) ? acc[2] : acc[3];
       got = 1;
+    }
+  };
+  load_e(ea, vlo);
+  for (int vb = vlo; vb < vhi; vb += 32) {
+    if (vb + 16 < vhi) load_e(eb, vb + 16);
+    block(ea, vb);
+    if (vb + 16 < vhi) {
+      if (vb + 32 < vhi) load_e(ea, vb + 32);
+      block(eb, vb + 16);
     }
   }
 #pragma unroll
@@ -290,7 +301,15 @@ hipError_t launch_head(const HeadArgs& a, hipStream_t s) {
   if (a.d % 32 != 0 || a.d > 640 || a.vocab % 64 != 0) return hipErrorInvalidValue;
   int64_t rows = a.p1 - a.p0;
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(head_kernel, dim3(nblk(rows, HEAD_ROWS)), dim3(256), 0, s, a);
+  const dim3 grid(nblk(rows, HEAD_ROWS));
+  switch (a.d) {
+    case 128: hipLaunchKernelGGL(head_kernel<4>, grid, dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(head_kernel<8>, grid, dim3(256), 0, s, a); break;
+    case 384: hipLaunchKernelGGL(head_kernel<12>, grid, dim3(256), 0, s, a); break;
+    case 512: hipLaunchKernelGGL(head_kernel<16>, grid, dim3(256), 0, s, a); break;
+    case 640: hipLaunchKernelGGL(head_kernel<20>, grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
