@@ -289,6 +289,9 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
     return fail(I6G_EUNSUPPORTED, "load_model: head_dim %d (supported: 32, 64, 80)", D.head_dim);
   if (D.n_heads != 2 * D.n_kv_heads)
     return fail(I6G_EUNSUPPORTED, "load_model: needs n_heads == 2 * n_kv_heads");
+  if (D.n_kv_heads % 2)
+    return fail(I6G_EUNSUPPORTED, "load_model: needs an even number of kv heads (the v block of the "
+                                  "q/k/v projection starts on a two-head tile boundary)");
   if (D.d_model % 128 || D.d_ff % 128 || D.d_model > 640)
     return fail(I6G_EUNSUPPORTED, "load_model: d_model and d_ff must be multiples of 128, d_model <= 640");
   if (D.embed_dtype != I6G_DTYPE_F16 && D.embed_dtype != I6G_DTYPE_F32)

@@ -11,11 +11,14 @@
 // (a per-row factor of C) is applied in the epilogue as well.
 //
 // Tiling: 256 threads = 4 waves in a 2 x 2 grid; workgroup tile BM x BN,
-// K step 64 through double-buffered, XOR-swizzled LDS with register prefetch
-// two K steps ahead; each wave
-// issues v_mfma_f32_16x16x32_bf16 on (BM/2) x (BN/2).  The accumulator tile
-// is staged through LDS so each epilogue can read rows and columns in the
-// order its output layout wants:
+// K step 64 through one XOR-swizzled LDS tile with register prefetch two K
+// steps ahead; each wave issues v_mfma_f32_16x16x32_bf16 on (BM/2) x (BN/2).
+// Rows are placed in LDS so that every lane ends up owning runs of
+// consecutive output columns of one row (C^T accumulation: two runs of 8,
+// or whole rotation pairs of a q/k head), or, for the transposed V output,
+// 16 consecutive rows of one column (C accumulation); the epilogues then
+// work straight from the accumulator registers with 16- or 32-byte global
+// accesses and no LDS round trip:
 //   EPI_QKV   q/k/v projection: * scale * rinv (+ rank-r LoRA), RoPE on the
 //             q and k heads, writes Q [W,Hq,Lp,hd], K [W,Hkv,Lp,hd] and
 //             V transposed [W,Hkv,hd,Lp] in bf16;
@@ -62,57 +65,75 @@ __device__ inline int xcd_remap(int bid, int nblocks) {
   return xcd * q + min(xcd, r) + idx;
 }
 
+// Rows of the LDS tiles are placed so that each lane's share of the
+// accumulator is a run of consecutive rows or columns (see the epilogues).
+// Within a 64-row slice, row u is stored at perm16(u), which swaps the two
+// 2-bit fields u[5:4] and u[3:2] (so perm16 is its own inverse): the MFMA
+// fragment of block b, lane row r (physical row 16b + r) then holds logical
+// row 16 * (r >> 2) + 4b + (r & 3).
+__device__ inline int perm16(int u) {
+  return ((u & 12) << 2) | ((u >> 4) & 3) << 2 | (u & 3);
+}
+
+// Placement of the weight rows of a 64-column slice for the row-major
+// epilogues: output rows 4g + e of fragment j (lane group g) are columns
+// 32*(j>>1) + 8g + 4*(j&1) + e, so a lane holds two runs of 8 consecutive
+// columns and the four lanes of a row cover 32 consecutive columns of each
+// half (one 128-byte line of fp32, or 64 bytes of bf16, per instruction).
+__device__ inline int pair_phys(int u) {
+  return 16 * (2 * (u >> 5) + ((u >> 2) & 1)) + 4 * ((u >> 3) & 3) + (u & 3);
+}
+
+// Placement of the rows of one q or k head (HD rows) for the rotary
+// epilogue: the output rows 4g + e of fragment j (lane group g) are the
+// values t = 4j + e of that lane, and value t < HD/8 is rotation index
+// g * HD/8 + t while value t + HD/8 is its partner HD/2 further on, so a
+// lane holds whole rotation pairs.
+template <int HD>
+__device__ inline int rope_phys(int u) {
+  constexpr int HALF = HD / 2, Q8 = HD / 8;
+  const int g = (u < HALF ? u : u - HALF) / Q8;
+  const int t = (u < HALF ? 0 : Q8) + (u < HALF ? u : u - HALF) % Q8;
+  return 16 * (t >> 2) + 4 * g + (t & 3);
+}
+
 template <int BM, int BN>
 struct Smem {
-  static constexpr int kAB = (BM + BN) * LDK * 2;        // one A and one B tile
-  static constexpr int kC = (BM / 2) * (BN + 4) * 4;     // half of the accumulator tile
-  static constexpr int kBytes = kAB > kC ? kAB : kC;
+  static constexpr int kBytes = (BM + BN) * LDK * 2;   // one A and one B tile
 };
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BN <= 128 ? 3 : 2)))
-void gemm_kernel(GemmArgs a) {
+template <int N>
+__device__ inline void store_bf16_run(bf16* dst, const uint16_t (&y)[N]) {
+  if constexpr (N == 8) {
+    *reinterpret_cast<uint4*>(dst) = make_uint4(
+        (uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16),
+        (uint32_t)y[4] | ((uint32_t)y[5] << 16), (uint32_t)y[6] | ((uint32_t)y[7] << 16));
+  } else if constexpr (N == 4) {
+    *reinterpret_cast<uint2*>(dst) =
+        make_uint2((uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16));
+  } else {
+    static_assert(N % 2 == 0, "pairs");
+#pragma unroll
+    for (int e = 0; e < N; e += 2)
+      reinterpret_cast<uint32_t*>(dst)[e / 2] = (uint32_t)y[e] | ((uint32_t)y[e + 1] << 16);
+  }
+}
+
+// Main loop and epilogue of one tile.  CT: accumulate C^T (every epilogue
+// except the V heads of the q/k/v projection, which keep C).
+template <int BM, int BN, int EPI, bool CT>
+__device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs, float* rinv_s,
+                                          float* scale_s, float* popw_s, float (*ss_part)[BM],
+                                          int tid, int wave, int m0, int n0, int tn) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 16, FN = WN / 16;
   constexpr int A_CHUNKS = BM * BK / 8;       // 16-byte chunks of bf16
   constexpr int B_CHUNKS = BN * BK / 16;      // 16-byte chunks of int8
   constexpr int A_PER = (A_CHUNKS + 255) / 256;
   constexpr int B_PER = (B_CHUNKS + 255) / 256;
-  constexpr int CLD = BN + 4;
-
-  __shared__ __attribute__((aligned(16))) char smem[Smem<BM, BN>::kBytes];
-  __shared__ float rinv_s[BM];
-  __shared__ float scale_s[BN];
-  __shared__ float popw_s[BN];
-  bf16* As = reinterpret_cast<bf16*>(smem);
-  bf16* Bs = As + BM * LDK;
-  float* Cs = reinterpret_cast<float*>(smem);
-
-  const int tid = threadIdx.x & 255;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  const int ntn = a.N / BN;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int tm = tile / ntn, tn = tile % ntn;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  for (int c = tid; c < BN; c += 256) {
-    scale_s[c] = h2f(a.scale[n0 + c]);
-    if constexpr (EPI == EPI_RES) popw_s[c] = a.pop_w ? a.pop_w[n0 + c] : 0.0f;
-  }
-  if constexpr (EPI == EPI_QKV || EPI == EPI_RELU2) {
-    for (int r = tid; r < BM; r += 256) {
-      int m = m0 + r;
-      float v = 0.0f;
-      if (m < a.M) {
-        const int64_t mr = a.a_map ? scored_row(a.p0 + m, a.k0, a.n_win, a.e0, a.L, a.S, a.Lp) : m;
-        float ss = 0.0f;
-        for (int t = 0; t < a.nt_in; ++t) ss += a.ss_in[mr * a.nt_in + t];
-        v = 1.0f / sqrtf(ss / (float)a.K + a.eps);
-      }
-      rinv_s[r] = v;
-    }
-  }
+  const int dq = a.n_heads * WN, dkv = a.n_kv * WN;
 
   // Global -> register staging, prefetched two K tiles ahead into two sets
   // of named scalars (arrays of them end up in scratch memory).  Chunk
@@ -123,16 +144,36 @@ void gemm_kernel(GemmArgs a) {
   uint4 sa0_0, sa0_1, sa0_2, sa0_3, sb0_0, sb0_1, sb0_2;
   uint4 sa1_0, sa1_1, sa1_2, sa1_3, sb1_0, sb1_1, sb1_2;
   const int nk = a.K / BK;
-  // element offset of each A row this thread loads, for the whole K loop
+  // per thread, for the whole K loop: the element offset of each A row it
+  // loads, and the LDS offsets its A and B chunks go to
   int64_t arow0 = 0, arow1 = 0, arow2 = 0, arow3 = 0;
-#define GM_AROW(i, V)                                                                 \
+  int aso0 = 0, aso1 = 0, aso2 = 0, aso3 = 0;
+  int bso0a = 0, bso0b = 0, bso1a = 0, bso1b = 0, bso2a = 0, bso2b = 0;
+#define GM_AROW(i, V, O)                                                              \
   if constexpr (A_PER > i) {                                                          \
     const int c = min(tid + (i) * 256, A_CHUNKS - 1);                                 \
     const int m = min(m0 + (c >> 3), a.M - 1);                                        \
     V = (a.a_map ? scored_row(a.p0 + m, a.k0, a.n_win, a.e0, a.L, a.S, a.Lp) : m) * (int64_t)a.K; \
+    const int pr = ((c >> 3) & ~63) | perm16((c >> 3) & 63);                          \
+    O = pr * LDK + swz(pr, c & 7) * 8;                                                \
   }
-  GM_AROW(0, arow0) GM_AROW(1, arow1) GM_AROW(2, arow2) GM_AROW(3, arow3)
+  GM_AROW(0, arow0, aso0) GM_AROW(1, arow1, aso1) GM_AROW(2, arow2, aso2) GM_AROW(3, arow3, aso3)
 #undef GM_AROW
+#define GM_BROW(i, OA, OB)                                                            \
+  if constexpr (B_PER > i) {                                                          \
+    const int c = min(tid + (i) * 256, B_CHUNKS - 1);                                 \
+    const int r = c >> 2, j2 = (c & 3) * 2;                                           \
+    int pr;                                                                           \
+    if constexpr (EPI == EPI_QKV) {                                                   \
+      pr = CT ? (r / WN) * WN + rope_phys<WN>(r % WN) : r;                            \
+    } else {                                                                          \
+      pr = (r & ~63) | pair_phys(r & 63);                                             \
+    }                                                                                 \
+    OA = pr * LDK + swz(pr, j2) * 8;                                                  \
+    OB = pr * LDK + swz(pr, j2 + 1) * 8;                                              \
+  }
+  GM_BROW(0, bso0a, bso0b) GM_BROW(1, bso1a, bso1b) GM_BROW(2, bso2a, bso2b)
+#undef GM_BROW
 
 #define GM_A(i, R)                                                                    \
   if constexpr (A_PER > i) {                                                          \
@@ -150,30 +191,23 @@ void gemm_kernel(GemmArgs a) {
     GM_A(0, sa##S##_0) GM_A(1, sa##S##_1) GM_A(2, sa##S##_2) GM_A(3, sa##S##_3)       \
     GM_B(0, sb##S##_0) GM_B(1, sb##S##_1) GM_B(2, sb##S##_2)                          \
   }
-#define GM_SA(i, R, as)                                                               \
-  if constexpr (A_PER > i) {                                                          \
-    int c = min(tid + (i) * 256, A_CHUNKS - 1);                                       \
-    *reinterpret_cast<uint4*>(as + (c >> 3) * LDK + swz(c >> 3, c & 7) * 8) = R;      \
-  }
-#define GM_SB(i, R, bs)                                                               \
+#define GM_SA(i, R)                                                                   \
+  if constexpr (A_PER > i) *reinterpret_cast<uint4*>(As + aso##i) = R;
+#define GM_SB(i, R)                                                                   \
   if constexpr (B_PER > i) {                                                          \
-    int c = min(tid + (i) * 256, B_CHUNKS - 1);                                       \
     const uint32_t w_[4] = {R.x, R.y, R.z, R.w};                                      \
     uint32_t o_[8];                                                                   \
     _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                   \
       o_[2 * j] = pack_bf16x2_from_int((int)(int8_t)(w_[j] & 0xff), (int)(int8_t)((w_[j] >> 8) & 0xff)); \
       o_[2 * j + 1] = pack_bf16x2_from_int((int)(int8_t)((w_[j] >> 16) & 0xff), (int)(int8_t)(w_[j] >> 24)); \
     }                                                                                 \
-    const int r_ = c >> 2, j_ = (c & 3) * 2;                                          \
-    *reinterpret_cast<uint4*>(bs + r_ * LDK + swz(r_, j_) * 8) = make_uint4(o_[0], o_[1], o_[2], o_[3]); \
-    *reinterpret_cast<uint4*>(bs + r_ * LDK + swz(r_, j_ + 1) * 8) = make_uint4(o_[4], o_[5], o_[6], o_[7]); \
+    *reinterpret_cast<uint4*>(Bs + bso##i##a) = make_uint4(o_[0], o_[1], o_[2], o_[3]); \
+    *reinterpret_cast<uint4*>(Bs + bso##i##b) = make_uint4(o_[4], o_[5], o_[6], o_[7]); \
   }
 #define GM_STORE(S)                                                                   \
   {                                                                                   \
-    bf16* as_ = As;                                                                   \
-    bf16* bs_ = Bs;                                                                   \
-    GM_SA(0, sa##S##_0, as_) GM_SA(1, sa##S##_1, as_) GM_SA(2, sa##S##_2, as_) GM_SA(3, sa##S##_3, as_) \
-    GM_SB(0, sb##S##_0, bs_) GM_SB(1, sb##S##_1, bs_) GM_SB(2, sb##S##_2, bs_)        \
+    GM_SA(0, sa##S##_0) GM_SA(1, sa##S##_1) GM_SA(2, sa##S##_2) GM_SA(3, sa##S##_3)   \
+    GM_SB(0, sb##S##_0) GM_SB(1, sb##S##_1) GM_SB(2, sb##S##_2)                       \
   }
 
   f32x4 acc[FM][FN];
@@ -183,24 +217,29 @@ void gemm_kernel(GemmArgs a) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int lr = lane & 15, lg = lane >> 4;
-#define GM_COMPUTE()                                                                  \
+  // MF_C: acc block (i, j) = C (A rows x weight rows); MF_T: its transpose.
+#define MF_C(x, w, c) __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, w, c, 0, 0, 0)
+#define MF_T(x, w, c) __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, x, c, 0, 0, 0)
+#define GM_COMPUTE(MF)                                                                \
   {                                                                                   \
-    const bf16* as = As;                                                              \
-    const bf16* bs = Bs;                                                              \
     _Pragma("unroll") for (int ks = 0; ks < BK / 32; ++ks) {                          \
       bf16x8 af[FM], bfg[FN];                                                         \
       _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                \
         const int r_ = wm * WM + i * 16 + lr;                                         \
-        af[i] = *reinterpret_cast<const bf16x8*>(as + r_ * LDK + swz(r_, ks * 4 + lg) * 8); \
+        af[i] = *reinterpret_cast<const bf16x8*>(As + r_ * LDK + swz(r_, ks * 4 + lg) * 8); \
       }                                                                               \
       _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                \
         const int r_ = wn * WN + j * 16 + lr;                                         \
-        bfg[j] = *reinterpret_cast<const bf16x8*>(bs + r_ * LDK + swz(r_, ks * 4 + lg) * 8); \
+        bfg[j] = *reinterpret_cast<const bf16x8*>(Bs + r_ * LDK + swz(r_, ks * 4 + lg) * 8); \
       }                                                                               \
       _Pragma("unroll") for (int i = 0; i < FM; ++i)                                  \
         _Pragma("unroll") for (int j = 0; j < FN; ++j)                                \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfg[j], acc[i][j], 0, 0, 0); \
+          acc[i][j] = MF(af[i], bfg[j], acc[i][j]);                                   \
     }                                                                                 \
+  }
+#define GM_COMPUTE_ANY()                                                              \
+  {                                                                                   \
+    if constexpr (CT) GM_COMPUTE(MF_T) else GM_COMPUTE(MF_C)                          \
   }
   // One K tile: issue the loads of tile kt+2 into register set L, multiply
   // tile kt out of LDS, then replace it with tile kt+1 (set S, loaded one
@@ -210,7 +249,7 @@ void gemm_kernel(GemmArgs a) {
 #define GM_STEP(kt, L, S)                                                             \
   {                                                                                   \
     GM_LOAD(min((kt) + 2, nk - 1), L);                                                \
-    GM_COMPUTE();                                                                     \
+    GM_COMPUTE_ANY();                                                                 \
     if ((kt) + 1 < nk) {                                                              \
       __syncthreads();                                                                \
       GM_STORE(S);                                                                    \
@@ -219,15 +258,42 @@ void gemm_kernel(GemmArgs a) {
   }
 
   GM_LOAD(0, 0);
-  GM_STORE(0);
   GM_LOAD(min(1, nk - 1), 1);
+  {
+    // the per-column weight scales and per-row RMS factors (read by the
+    // epilogue only) load while the first two K tiles are in flight
+    static_assert(BN <= 256 && BM <= 256, "one factor per thread");
+    float sc_r = 0.0f, pw_r = 0.0f, ri_r = 0.0f;
+    if (tid < BN) {
+      sc_r = h2f(a.scale[n0 + tid]);
+      if constexpr (EPI == EPI_RES) pw_r = a.pop_w ? a.pop_w[n0 + tid] : 0.0f;
+    }
+    if constexpr (EPI == EPI_QKV || EPI == EPI_RELU2) {
+      const int m = m0 + tid;
+      if (tid < BM && m < a.M) {
+        const int64_t mr = a.a_map ? scored_row(a.p0 + m, a.k0, a.n_win, a.e0, a.L, a.S, a.Lp) : m;
+        float ss = 0.0f;
+        for (int t = 0; t < a.nt_in; ++t) ss += a.ss_in[mr * a.nt_in + t];
+        ri_r = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+      }
+    }
+    GM_STORE(0);
+    if (tid < BN) {
+      scale_s[tid] = sc_r;
+      if constexpr (EPI == EPI_RES) popw_s[tid] = pw_r;
+    }
+    if (tid < BM) rinv_s[tid] = ri_r;
+  }
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
     GM_STEP(kt, 0, 1);
     if (kt + 1 < nk) GM_STEP(kt + 1, 1, 0);
   }
 #undef GM_STEP
+#undef GM_COMPUTE_ANY
 #undef GM_COMPUTE
+#undef MF_T
+#undef MF_C
 #undef GM_STORE
 #undef GM_SB
 #undef GM_SA
@@ -235,206 +301,274 @@ void gemm_kernel(GemmArgs a) {
 #undef GM_B
 #undef GM_A
 
-  // The accumulator tile goes through LDS in two halves of BM/2 rows (the
-  // rows of wave row wm == h); lane holds column (lane & 15) and rows
-  // 4*(lane>>4)+e of each 16 x 16 block.
-  constexpr int HR = BM / 2;
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-  const int hr0 = h * HR;
-  if (wm == h) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          int r = i * 16 + (lane >> 4) * 4 + e;
-          int c = wn * WN + j * 16 + (lane & 15);
-          Cs[r * CLD + c] = acc[i][j][e];
-        }
-  }
-  __syncthreads();
-
-  // Epilogues: each unit of work is 8 consecutive outputs; the unit loops
-  // have compile-time trip counts and are unrolled so their global loads
-  // are all in flight together.
+  // Epilogues straight from the accumulators.  In the C^T orientation lane
+  // (lr, lg) of block (i, j) holds A row wm*WM + 16*(lr>>2) + 4i + (lr&3)
+  // and the 4 weight rows the placement above gives output rows 4lg..4lg+3
+  // of fragment j; in the C orientation (v heads) it holds weight row
+  // wn*WN + 16j + lr and the 16 consecutive A rows wm*WM + 16*lg + 4i + e.
+  const int lrow = 16 * (lr >> 2) + (lr & 3);   // + 4i: the lane's A row in C^T blocks
   if constexpr (EPI == EPI_RELU2) {
-    constexpr int UPR = BN / 8;
-    static_assert((HR * UPR) % 256 == 0, "unit count");
 #pragma unroll
-    for (int it = 0; it < HR * UPR / 256; ++it) {
-      const int u = tid + it * 256;
-      const int r = u / UPR, c8 = (u % UPR) * 8;
-      const int m = m0 + hr0 + r;
+    for (int i = 0; i < FM; ++i) {
+      const int ml = wm * WM + lrow + 4 * i;
+      const int m = m0 + ml;
       if (m >= a.M) continue;
-      const float ri = rinv_s[hr0 + r];
-      uint32_t o[4];
+      const float ri = rinv_s[ml];
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        float v0 = fmaxf(Cs[r * CLD + c8 + e] * scale_s[c8 + e] * ri, 0.0f);
-        float v1 = fmaxf(Cs[r * CLD + c8 + e + 1] * scale_s[c8 + e + 1] * ri, 0.0f);
-        o[e / 2] = (uint32_t)f2bf_bits(v0 * v0) | ((uint32_t)f2bf_bits(v1 * v1) << 16);
+      for (int p = 0; p < FN / 2; ++p) {
+        const int cl = wn * WN + 32 * p + 8 * lg;   // 8 consecutive columns: blocks 2p, 2p+1
+        uint32_t o[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float4 s4 = reinterpret_cast<const float4*>(scale_s + cl)[h];
+          const f32x4 c = acc[i][2 * p + h];
+          const float v0 = fmaxf(c[0] * s4.x * ri, 0.0f), v1 = fmaxf(c[1] * s4.y * ri, 0.0f);
+          const float v2 = fmaxf(c[2] * s4.z * ri, 0.0f), v3 = fmaxf(c[3] * s4.w * ri, 0.0f);
+          o[2 * h] = (uint32_t)f2bf_bits(v0 * v0) | ((uint32_t)f2bf_bits(v1 * v1) << 16);
+          o[2 * h + 1] = (uint32_t)f2bf_bits(v2 * v2) | ((uint32_t)f2bf_bits(v3 * v3) << 16);
+        }
+        *reinterpret_cast<uint4*>(a.h + (int64_t)m * a.N + n0 + cl) = make_uint4(o[0], o[1], o[2], o[3]);
       }
-      *reinterpret_cast<uint4*>(a.h + (int64_t)m * a.N + n0 + c8) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   } else if constexpr (EPI == EPI_RES) {
-    constexpr int UPR = BN / 8;   // 16 consecutive lanes hold one row
-    static_assert(BN == 128, "residual epilogue assumes 128-column tiles");
+    static_assert(BN == 128, "partial sums of squares cover 128 columns");
     const bool push = a.push_dst != nullptr;
     const bool pop = a.pop_src != nullptr;
     const bool pop_self = pop && a.pop_src == a.push_dst;
+    // the lane's columns: block j holds the 4 starting at colj(j)
+    auto colj = [&](int j) { return wn * WN + 32 * (j >> 1) + 8 * lg + 4 * (j & 1); };
+    int64_t off[FM];
+    bool ok[FM];
 #pragma unroll
-    for (int it = 0; it < HR * UPR / 256; ++it) {
-      const int u = tid + it * 256;
-      const int r = u / UPR, c8 = (u % UPR) * 8;
-      const int m = min(m0 + hr0 + r, a.M - 1);  // rows past M recompute row M-1, store nothing
-      const bool ok = m0 + hr0 + r < a.M;
-      const int64_t mr = a.e_map ? scored_row(a.p0 + m, a.k0, a.n_win, a.e0, a.L, a.S, a.Lp) : m;
-      const int64_t off = mr * a.N + n0 + c8;
-      const float4* xp = reinterpret_cast<const float4*>(a.x + off);
-      const float4 x0 = xp[0], x1 = xp[1];
-      float xn[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xn[e] += Cs[r * CLD + c8 + e] * scale_s[c8 + e];
-      if (push && ok) {
-        float4* pd = reinterpret_cast<float4*>(a.push_dst + off);
-        pd[0] = make_float4(xn[0], xn[1], xn[2], xn[3]);
-        pd[1] = make_float4(xn[4], xn[5], xn[6], xn[7]);
-      }
-      if (pop) {
-        float pv[8];
-        if (pop_self) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pv[e] = xn[e];
-        } else {
-          const float4* pp = reinterpret_cast<const float4*>(a.pop_src + off);
-          const float4 p0 = pp[0], p1 = pp[1];
-          pv[0] = p0.x; pv[1] = p0.y; pv[2] = p0.z; pv[3] = p0.w;
-          pv[4] = p1.x; pv[5] = p1.y; pv[6] = p1.z; pv[7] = p1.w;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xn[e] += popw_s[c8 + e] * pv[e];
-      }
-      float sq = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sq += xn[e] * xn[e];
-      if (ok) {
-        float4* xw = reinterpret_cast<float4*>(a.x + off);
-        xw[0] = make_float4(xn[0], xn[1], xn[2], xn[3]);
-        xw[1] = make_float4(xn[4], xn[5], xn[6], xn[7]);
-        if (a.xb) {
-          uint32_t o[4];
-#pragma unroll
-          for (int e = 0; e < 8; e += 2)
-            o[e / 2] = (uint32_t)f2bf_bits(xn[e]) | ((uint32_t)f2bf_bits(xn[e + 1]) << 16);
-          *reinterpret_cast<uint4*>(a.xb + off) = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-      }
-      sq += __shfl_xor(sq, 1);
-      sq += __shfl_xor(sq, 2);
-      sq += __shfl_xor(sq, 4);
-      sq += __shfl_xor(sq, 8);
-      if (ok && a.ss_out && (u % UPR) == 0) a.ss_out[mr * (a.N / 128) + tn] = sq;
+    for (int i = 0; i < FM; ++i) {
+      const int m = m0 + wm * WM + lrow + 4 * i;
+      ok[i] = m < a.M;
+      const int mm = min(m, a.M - 1);   // rows past M recompute row M-1 and store nothing
+      const int64_t mr = a.e_map ? scored_row(a.p0 + mm, a.k0, a.n_win, a.e0, a.L, a.S, a.Lp) : mm;
+      off[i] = mr * a.N + n0;
     }
-  } else {  // EPI_QKV: BN = 2 * head_dim, so a tile holds two whole heads
-    constexpr int HDT = BN / 2, HALF = HDT / 2;
-    const int dq = a.n_heads * HDT, dkv = a.n_kv * HDT;
-    if (n0 < dq + dkv) {
-      // q or k heads: units of (row, head in tile, 4 rotation pairs)
-      const bool is_q = n0 < dq;
-      constexpr int CPR = HALF / 4;             // pair chunks per head
-      constexpr int UPR = 2 * CPR;              // units per row
-      static_assert((HR * UPR) % 256 == 0, "unit count");
-      const int head0 = (is_q ? n0 : n0 - dq) / HDT;
+    // the residual rows first, so that all their loads are in flight together
+    float4 xv[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) xv[i][j] = *reinterpret_cast<const float4*>(a.x + off[i] + colj(j));
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const float4 s4 = *reinterpret_cast<const float4*>(scale_s + colj(j));
+        xv[i][j].x += acc[i][j][0] * s4.x;
+        xv[i][j].y += acc[i][j][1] * s4.y;
+        xv[i][j].z += acc[i][j][2] * s4.z;
+        xv[i][j].w += acc[i][j][3] * s4.w;
+      }
+    if (push) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        if (ok[i]) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) *reinterpret_cast<float4*>(a.push_dst + off[i] + colj(j)) = xv[i][j];
+        }
+    }
+    if (pop) {
+      if (pop_self) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const float4 w4 = *reinterpret_cast<const float4*>(popw_s + colj(j));
+            xv[i][j].x += w4.x * xv[i][j].x;
+            xv[i][j].y += w4.y * xv[i][j].y;
+            xv[i][j].z += w4.z * xv[i][j].z;
+            xv[i][j].w += w4.w * xv[i][j].w;
+          }
+      } else {
+        float4 pv[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) pv[i][j] = *reinterpret_cast<const float4*>(a.pop_src + off[i] + colj(j));
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const float4 w4 = *reinterpret_cast<const float4*>(popw_s + colj(j));
+            xv[i][j].x += w4.x * pv[i][j].x;
+            xv[i][j].y += w4.y * pv[i][j].y;
+            xv[i][j].z += w4.z * pv[i][j].z;
+            xv[i][j].w += w4.w * pv[i][j].w;
+          }
+      }
+    }
+    float sq[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      float t = 0.0f;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        t += xv[i][j].x * xv[i][j].x + xv[i][j].y * xv[i][j].y + xv[i][j].z * xv[i][j].z +
+             xv[i][j].w * xv[i][j].w;
+      sq[i] = t;
+      if (ok[i]) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) *reinterpret_cast<float4*>(a.x + off[i] + colj(j)) = xv[i][j];
+        if (a.xb) {
+#pragma unroll
+          for (int p = 0; p < FN / 2; ++p) {
+            const f32x4 u0 = {xv[i][2 * p].x, xv[i][2 * p].y, xv[i][2 * p].z, xv[i][2 * p].w};
+            const f32x4 u1 = {xv[i][2 * p + 1].x, xv[i][2 * p + 1].y, xv[i][2 * p + 1].z, xv[i][2 * p + 1].w};
+            *reinterpret_cast<uint4*>(a.xb + off[i] + colj(2 * p)) = make_uint4(
+                (uint32_t)f2bf_bits(u0[0]) | ((uint32_t)f2bf_bits(u0[1]) << 16),
+                (uint32_t)f2bf_bits(u0[2]) | ((uint32_t)f2bf_bits(u0[3]) << 16),
+                (uint32_t)f2bf_bits(u1[0]) | ((uint32_t)f2bf_bits(u1[1]) << 16),
+                (uint32_t)f2bf_bits(u1[2]) | ((uint32_t)f2bf_bits(u1[3]) << 16));
+          }
+        }
+      }
+    }
+    if (a.ss_out) {
+      // the four lane groups of a row, then the two waves of a tile row
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        sq[i] += __shfl_xor(sq[i], 16);
+        sq[i] += __shfl_xor(sq[i], 32);
+        if (lg == 0) ss_part[wn][wm * WM + lrow + 4 * i] = sq[i];
+      }
+      __syncthreads();
+      for (int r = tid; r < BM; r += 256) {
+        const int m = m0 + r;
+        if (m >= a.M) continue;
+        const int64_t mr = a.e_map ? scored_row(a.p0 + m, a.k0, a.n_win, a.e0, a.L, a.S, a.Lp) : m;
+        a.ss_out[mr * (a.N / 128) + tn] = ss_part[0][r] + ss_part[1][r];
+      }
+    }
+  } else {  // EPI_QKV: BN = 2 * head_dim, each wave holds one whole head
+    constexpr int HD = WN, HALF = HD / 2, Q8 = HD / 8;
+    const int colbase = n0 + wn * HD;
+    if constexpr (CT) {
+      // q or k head, C^T: lane holds rotation indices c1 = lg*Q8 + t and
+      // their partners c1 + HALF, t < Q8
+      const bool is_q = colbase < dq;
+      const int head = (is_q ? colbase : colbase - dq) / HD;
       const int nh = is_q ? a.n_heads : a.n_kv;
       bf16* const base = is_q ? a.q : a.k;
       const bool lora = is_q && a.lora_u;
+      const int c1b = lg * Q8;
+      float sc1[Q8], sc2[Q8];
 #pragma unroll
-      for (int it = 0; it < HR * UPR / 256; ++it) {
-        const int u = tid + it * 256;
-        const int r = u / UPR, rem = u % UPR;
-        const int hh = rem / CPR, i0 = (rem % CPR) * 4;
-        const int m = m0 + hr0 + r;
+      for (int t = 0; t < Q8; ++t) {
+        sc1[t] = scale_s[wn * HD + c1b + t];
+        sc2[t] = scale_s[wn * HD + HALF + c1b + t];
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int ml = wm * WM + lrow + 4 * i;
+        const int m = m0 + ml;
         if (m >= a.M) continue;
-        const float ri = rinv_s[hr0 + r];
+        const float ri = rinv_s[ml];
         const int w = m / a.Lp, pos = m % a.Lp;
-        const int cbase = hh * HDT;
-        const float4 cs01 = *reinterpret_cast<const float4*>(a.rope + pos * HALF + i0);
-        const float4 cs23 = *reinterpret_cast<const float4*>(a.rope + pos * HALF + i0 + 2);
-        const float cs[8] = {cs01.x, cs01.y, cs01.z, cs01.w, cs23.x, cs23.y, cs23.z, cs23.w};
-        float x1[4], x2[4];
+        const float4* csp = reinterpret_cast<const float4*>(a.rope + pos * HALF + c1b);
+        float x1[Q8], x2[Q8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c1 = cbase + i0 + e, c2 = c1 + HALF;
-          x1[e] = Cs[r * CLD + c1] * scale_s[c1] * ri;
-          x2[e] = Cs[r * CLD + c2] * scale_s[c2] * ri;
+        for (int t = 0; t < Q8; ++t) {
+          x1[t] = acc[i][t >> 2][t & 3] * sc1[t] * ri;
+          x2[t] = acc[i][(t + Q8) >> 2][(t + Q8) & 3] * sc2[t] * ri;
         }
         if (lora) {
           const float* uu = a.lora_u + (int64_t)m * 2 * a.lora_r;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int g1 = n0 + cbase + i0 + e, g2 = g1 + HALF;
+          for (int t = 0; t < Q8; ++t) {
+            const int g1 = colbase + c1b + t, g2 = g1 + HALF;
             float s1 = 0.f, s2 = 0.f;
-            for (int t = 0; t < a.lora_r; ++t) {
-              s1 += uu[t] * a.lora_bq[g1 * a.lora_r + t];
-              s2 += uu[t] * a.lora_bq[g2 * a.lora_r + t];
+            for (int r = 0; r < a.lora_r; ++r) {
+              s1 += uu[r] * a.lora_bq[g1 * a.lora_r + r];
+              s2 += uu[r] * a.lora_bq[g2 * a.lora_r + r];
             }
-            x1[e] += s1;
-            x2[e] += s2;
+            x1[t] += s1;
+            x2[t] += s2;
           }
         }
-        uint16_t y1[4], y2[4];
+        uint16_t y1[Q8], y2[Q8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float co = cs[2 * e], si = cs[2 * e + 1];
-          y1[e] = f2bf_bits(x1[e] * co - x2[e] * si);
-          y2[e] = f2bf_bits(x1[e] * si + x2[e] * co);
+        for (int t = 0; t < Q8; t += 2) {
+          const float4 cs = csp[t / 2];   // (cos, sin) of indices c1b + t and c1b + t + 1
+          y1[t] = f2bf_bits(x1[t] * cs.x - x2[t] * cs.y);
+          y2[t] = f2bf_bits(x1[t] * cs.y + x2[t] * cs.x);
+          y1[t + 1] = f2bf_bits(x1[t + 1] * cs.z - x2[t + 1] * cs.w);
+          y2[t + 1] = f2bf_bits(x1[t + 1] * cs.w + x2[t + 1] * cs.z);
         }
-        bf16* dst = base + (((int64_t)w * nh + head0 + hh) * a.Lp + pos) * HDT;
-        *reinterpret_cast<uint2*>(dst + i0) =
-            make_uint2((uint32_t)y1[0] | ((uint32_t)y1[1] << 16), (uint32_t)y1[2] | ((uint32_t)y1[3] << 16));
-        *reinterpret_cast<uint2*>(dst + HALF + i0) =
-            make_uint2((uint32_t)y2[0] | ((uint32_t)y2[1] << 16), (uint32_t)y2[2] | ((uint32_t)y2[3] << 16));
+        bf16* dst = base + (((int64_t)w * nh + head) * a.Lp + pos) * HD;
+        store_bf16_run<Q8>(dst + c1b, y1);
+        store_bf16_run<Q8>(dst + HALF + c1b, y2);
       }
     } else {
-      // v heads, written transposed: units of (column, 8 consecutive rows)
-      constexpr int RCS = HR / 8;
-      static_assert((BN * RCS) % 256 == 0, "unit count");
-      const bool lora = a.lora_u != nullptr;
+      // v head, C orientation, written transposed: the lane's 16 rows are
+      // consecutive positions of one window (windows are 64-row aligned)
+      const int head = (colbase - dq - dkv) / HD;
+      const int mb = m0 + wm * WM + 16 * lg;
+      if (mb < a.M) {
+        const bool lora = a.lora_u != nullptr;
+        float ri[16];
 #pragma unroll
-      for (int it = 0; it < BN * RCS / 256; ++it) {
-        const int u = tid + it * 256;
-        const int rc = u % RCS, c = u / RCS;
-        const int r0 = rc * 8;
-        const int m = m0 + hr0 + r0;
-        if (m >= a.M) continue;          // M is a multiple of 8
-        const int nv = n0 + c - dq - dkv;      // column inside the v block
-        const int head = nv / HDT, dd = nv % HDT;
-        const float sc = scale_s[c];
-        uint16_t y[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float v = Cs[(r0 + e) * CLD + c] * sc * rinv_s[hr0 + r0 + e];
-          if (lora) {
-            const float* uu = a.lora_u + (int64_t)(m + e) * 2 * a.lora_r + a.lora_r;
-            float sl = 0.f;
-            for (int t = 0; t < a.lora_r; ++t) sl += uu[t] * a.lora_bv[nv * a.lora_r + t];
-            v += sl;
-          }
-          y[e] = f2bf_bits(v);
+        for (int q = 0; q < 4; ++q) {
+          const float4 r4 = reinterpret_cast<const float4*>(rinv_s + wm * WM + 16 * lg)[q];
+          ri[4 * q] = r4.x; ri[4 * q + 1] = r4.y; ri[4 * q + 2] = r4.z; ri[4 * q + 3] = r4.w;
         }
-        const int w = m / a.Lp, pos = m % a.Lp;
-        bf16* dst = a.vt + (((int64_t)w * a.n_kv + head) * HDT + dd) * a.Lp + pos;
-        *reinterpret_cast<uint4*>(dst) = make_uint4(
-            (uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16),
-            (uint32_t)y[4] | ((uint32_t)y[5] << 16), (uint32_t)y[6] | ((uint32_t)y[7] << 16));
+        const int w = mb / a.Lp, pos = mb % a.Lp;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int dd = 16 * j + lr;
+          const float sc = scale_s[wn * HD + dd];
+          uint16_t y[16];
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            float v = acc[t >> 2][j][t & 3] * sc * ri[t];
+            if (lora) {
+              const float* uu = a.lora_u + (int64_t)(mb + t) * 2 * a.lora_r + a.lora_r;
+              float sl = 0.f;
+              for (int r = 0; r < a.lora_r; ++r) sl += uu[r] * a.lora_bv[(head * HD + dd) * a.lora_r + r];
+              v += sl;
+            }
+            y[t] = f2bf_bits(v);
+          }
+          uint4* dst = reinterpret_cast<uint4*>(a.vt + (((int64_t)w * a.n_kv + head) * HD + dd) * a.Lp + pos);
+          dst[0] = make_uint4((uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16),
+                              (uint32_t)y[4] | ((uint32_t)y[5] << 16), (uint32_t)y[6] | ((uint32_t)y[7] << 16));
+          dst[1] = make_uint4((uint32_t)y[8] | ((uint32_t)y[9] << 16), (uint32_t)y[10] | ((uint32_t)y[11] << 16),
+                              (uint32_t)y[12] | ((uint32_t)y[13] << 16), (uint32_t)y[14] | ((uint32_t)y[15] << 16));
+        }
       }
     }
   }
-  __syncthreads();
-  }  // halves
+}
+
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BN <= 128 ? 3 : 2)))
+void gemm_kernel(GemmArgs a) {
+  static_assert(BM / 2 == 64, "the row placement works on 64-row slices");
+  static_assert(EPI == EPI_QKV || BN / 2 == 64, "the column placement works on 64-column slices");
+  __shared__ __attribute__((aligned(16))) char smem[Smem<BM, BN>::kBytes];
+  __shared__ __attribute__((aligned(16))) float rinv_s[BM];
+  __shared__ __attribute__((aligned(16))) float scale_s[BN];
+  __shared__ __attribute__((aligned(16))) float popw_s[BN];
+  __shared__ float ss_part[2][BM];
+  bf16* As = reinterpret_cast<bf16*>(smem);
+  bf16* Bs = As + BM * LDK;
+
+  const int tid = threadIdx.x & 255;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ntn = a.N / BN;
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int tm = tile / ntn, tn = tile % ntn;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // q/k/v projection: BN = 2 * head_dim and the v block starts on a tile
+  // boundary (an even number of kv heads), so a tile is all q/k or all v
+  if (EPI == EPI_QKV && n0 >= (a.n_heads + a.n_kv) * (BN / 2))
+    gemm_body<BM, BN, EPI, false>(a, As, Bs, rinv_s, scale_s, popw_s, ss_part, tid, wave, m0, n0, tn);
+  else
+    gemm_body<BM, BN, EPI, true>(a, As, Bs, rinv_s, scale_s, popw_s, ss_part, tid, wave, m0, n0, tn);
 }
 
 template <int BM, int BN, int EPI>

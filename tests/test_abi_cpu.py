@@ -90,7 +90,10 @@ def test_load_model_rejects_bad_descriptors():
     d.n_heads = 10
     d.d_model = 480
     assert L.i6g_load_model(ctypes.byref(d), None, ctypes.byref(out)) in (-1, -6)
-    d.d_model, d.n_heads, d.head_dim = 512, 8, 64
+    d.d_model, d.n_heads, d.n_kv_heads, d.head_dim = 384, 6, 3, 64   # odd number of kv heads
+    assert L.i6g_load_model(ctypes.byref(d), None, ctypes.byref(out)) == -6
+    assert "kv heads" in L.i6g_last_error().decode()
+    d.d_model, d.n_heads, d.n_kv_heads, d.head_dim = 512, 8, 4, 64
     bad = (ctypes.c_int32 * 1)(3)      # schedule names a block that does not exist
     d.schedule = ctypes.cast(bad, ctypes.c_void_p)
     assert L.i6g_load_model(ctypes.byref(d), None, ctypes.byref(out)) == -1
