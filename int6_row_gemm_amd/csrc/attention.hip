@@ -27,11 +27,13 @@
 //   max that only moves when a tile max exceeds it by more than 2^8, so the
 //   rescale of O is rare; the causal mask is applied only on the last
 //   (diagonal) tile, which is peeled off the loop.
-// * Software pipelining: the MFMAs of the next key tile's S^T are issued
-//   before the softmax of the current one, so the matrix cores and the VALU
-//   work at the same time.  K tiles run one tile ahead of V tiles through two
-//   LDS buffers each, with one barrier per tile; global loads are issued two
-//   tiles ahead into two register sets so their latency spans a whole step.
+// * Pipelining: K and V tiles go through two LDS buffers each with one
+//   barrier per key tile; the global loads of tile kt+1 are issued at the
+//   start of step kt and written to LDS at its end.  One score set and one
+//   staging set per wave keep head_dim 64 within 168 VGPRs, so three
+//   workgroups share a CU and overlap each other's softmax, MFMA and
+//   barrier phases (measured faster on gfx950 than keeping the next tile's
+//   scores in flight at two workgroups per CU).
 #include "common.h"
 
 namespace i6g {
@@ -60,8 +62,11 @@ __device__ inline float max_xor32(float v) {
   return __builtin_fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
 }
 
+// Three workgroups per CU where the registers allow it (head_dim <= 64):
+// the waves of the other workgroups then fill the MFMA pipe while one waits
+// on its softmax or barrier.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD <= 64 ? 3 : 2))) void attn_kernel(AttnArgs a) {
   constexpr int KS = (HD + 31) / 32;  // 32-wide k steps over the head dim
   constexpr int HDP = KS * 32;
   constexpr int DB = HD / 16;         // 16-row blocks of O^T
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   // Register staging, up to three 16-byte chunks per thread and tile, as
   // named scalars (arrays of them end up in scratch memory).
   static_assert(KPER <= 3 && VPER <= 3, "staging holds three chunks per thread");
-  uint4 kreg_0, kreg_1, kreg_2, vreg_0, vreg_1, vreg_2, kreg2_0, kreg2_1, kreg2_2, vreg2_0, vreg2_1, vreg2_2;
+  uint4 kreg_0, kreg_1, kreg_2, vreg_0, vreg_1, vreg_2;
   // Chunk indices past the tile are clamped: those threads reload and rewrite
   // the last chunk with identical data.
 #define ATT_CHUNKS(PER, R, BODY) \
@@ -201,35 +206,30 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   float mref[2] = {-1e30f, -1e30f};
   const float c = a.scale_log2;
 
-  // prologue: S^T of tile 0; LDS then holds K[1] and V[0]
+  // prologue: LDS holds K[0] and V[0]
   ATT_LOAD_K(0, kreg);
   ATT_LOAD_V(0, vreg);
   ATT_STORE_K(0, kreg);
   ATT_STORE_V(0, vreg);
   __syncthreads();
-  f32x4 s_cur[2][4], s_nxt[2][4];
-  ATT_QK(s_cur, 0);
-  ATT_LOAD_K(min(1, nkt - 1), kreg);
-  ATT_LOAD_K(min(2, nkt - 1), kreg2);   // stored at the end of step 0
-  ATT_LOAD_V(min(1, nkt - 1), vreg2);
-  ATT_STORE_K(1, kreg);
-  __syncthreads();
+  f32x4 s_cur[2][4];
 
-  // One key tile; SC holds its S^T, SN receives the next tile's.  The
-  // register set RL receives K[kt+3] and V[kt+2]; RS (filled one step
-  // earlier) holds K[kt+2] and V[kt+1], written to LDS at the end.  DIAG is
-  // true only for the last tile, the one that straddles the causal diagonal.
+  // One key tile: S^T of tile kt into SC, softmax, O^T += V^T P^T.  The
+  // registers KR/VR receive K[kt+1] and V[kt+1], written to LDS at the end
+  // into the buffers tile kt-1 used (read before the previous barrier).
+  // DIAG is true only for the last tile, the one that straddles the causal
+  // diagonal.
   //
   // The probabilities use a per-query reference max mref that is only moved
   // when the tile max exceeds it by more than 2^8 in the exp2 domain (or on
   // the first tile); otherwise p <= 256 and O, the denominator and the final
   // O / denominator are unchanged by the choice of reference, so the rescale
   // of O (and its multiplies) is skipped on almost every tile.
-#define ATT_STEP(kt, SC, SN, KRL, VRL, KRS, VRS, DIAG)                                \
+#define ATT_STEP(kt, SC, KR, VR, DIAG)                                                 \
   {                                                                                   \
-    ATT_LOAD_K(min((kt) + 3, nkt - 1), KRL);                                          \
-    ATT_LOAD_V(min((kt) + 2, nkt - 1), VRL);                                          \
-    if (!(DIAG)) ATT_QK(SN, ((kt) + 1) & 1);                                          \
+    ATT_LOAD_K(min((kt) + 1, nkt - 1), KR);                                           \
+    ATT_LOAD_V(min((kt) + 1, nkt - 1), VR);                                           \
+    ATT_QK(SC, (kt) & 1);                                                             \
     if (DIAG) {                                                                       \
       _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                              \
         const int qabs = qbase + 16 * qb + lr;                                        \
@@ -283,10 +283,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         osum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb][kk], osum[qb], 0, 0, 0); \
     }                                                                                 \
     if (!(DIAG)) {                                                                    \
-      /* K[kt+2] replaces K[kt] (read by the previous step), V[kt+1] */               \
-      /* replaces V[kt-1]; the barrier publishes both for the next step. */           \
-      if ((kt) + 2 < nkt) ATT_STORE_K((kt) & 1, KRS);                                 \
-      ATT_STORE_V(((kt) + 1) & 1, VRS);                                               \
+      /* K[kt+1] and V[kt+1] replace tile kt-1's; the barrier publishes */            \
+      /* them for the next step. */                                                   \
+      ATT_STORE_K(((kt) + 1) & 1, KR);                                                \
+      ATT_STORE_V(((kt) + 1) & 1, VR);                                                \
       __syncthreads();                                                                \
     }                                                                                 \
   }
@@ -294,14 +294,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   // the diagonal tile is the last one (kt = qt): peel it off the loop
   int kt = 0;
   for (; kt + 2 < nkt; kt += 2) {
-    ATT_STEP(kt, s_cur, s_nxt, kreg, vreg, kreg2, vreg2, false);
-    ATT_STEP(kt + 1, s_nxt, s_cur, kreg2, vreg2, kreg, vreg, false);
+    ATT_STEP(kt, s_cur, kreg, vreg, false);
+    ATT_STEP(kt + 1, s_cur, kreg, vreg, false);
   }
   if (nkt - kt == 2) {
-    ATT_STEP(kt, s_cur, s_nxt, kreg, vreg, kreg2, vreg2, false);
-    ATT_STEP(kt + 1, s_nxt, s_cur, kreg2, vreg2, kreg, vreg, true);
+    ATT_STEP(kt, s_cur, kreg, vreg, false);
+    ATT_STEP(kt + 1, s_cur, kreg, vreg, true);
   } else {
-    ATT_STEP(kt, s_cur, s_nxt, kreg, vreg, kreg2, vreg2, true);
+    ATT_STEP(kt, s_cur, kreg, vreg, true);
   }
 #undef ATT_STEP
 #undef ATT_LOAD_K
