@@ -217,7 +217,7 @@ int i6g_plan_windows(int64_t n_tokens, int32_t window, int32_t stride, int64_t* 
 /* Model options (tuning and testing; results do not depend on them beyond
  * floating-point rounding):
  *   I6G_OPT_BATCH_WINDOWS  windows per batch in i6g_score_tokens (0 = the
- *                          default, about 32768 rows per batch);
+ *                          default, about 49152 rows per batch);
  *   I6G_OPT_PRUNE_LAST     1 (default): the final layer computes queries,
  *                          the output projection and the MLP only for the
  *                          scored rows; 0: for every row.

@@ -433,7 +433,9 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
   const int64_t L = window, S = stride;
   const int64_t K = window_count(P, L, S);
   const int Lp = (int)((std::min<int64_t>(L, P) + 63) / 64 * 64);
-  int Wb = m->batch_windows > 0 ? m->batch_windows : std::max(1, 32768 / Lp);
+  // default batch: 49152 rows (24 windows of 2048), which splits the GEMM
+  // tiles evenly over the workgroups the device holds at once
+  int Wb = m->batch_windows > 0 ? m->batch_windows : std::max(1, 49152 / Lp);
   Wb = (int)std::min<int64_t>(Wb, K);
   int rc = ensure_scratch(m, Wb, Lp, s);
   if (rc) return rc;

@@ -135,8 +135,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
   const int wm = wave >> 1, wn = wave & 1;
   const int dq = a.n_heads * WN, dkv = a.n_kv * WN;
 
-  // Global -> register staging, prefetched two K tiles ahead into two sets
-  // of named scalars (arrays of them end up in scratch memory).  Chunk
+  // Global -> register staging into one or two sets of named scalars
+  // (arrays of them end up in scratch memory).  Chunk
   // indices past the tile are clamped (those threads reload and rewrite the
   // last chunk with identical data); A rows past M are clamped to M - 1 and
   // their results are never stored.
@@ -241,11 +241,19 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
   {                                                                                   \
     if constexpr (CT) GM_COMPUTE(MF_T) else GM_COMPUTE(MF_C)                          \
   }
-  // One K tile: issue the loads of tile kt+2 into register set L, multiply
-  // tile kt out of LDS, then replace it with tile kt+1 (set S, loaded one
-  // step earlier).  A single LDS tile keeps the footprint small enough for
-  // three workgroups per CU, whose epilogue stores then overlap the others'
-  // MFMA work.
+  // Two ways through K, both with a single LDS tile (small enough for
+  // several workgroups per CU, whose epilogues then overlap the others'
+  // MFMA work):
+  //  * DEEP (residual epilogue, 3 workgroups per CU): the loads of K tile
+  //    kt+2 go into register set L while tile kt is multiplied out of LDS,
+  //    then tile kt+1 (set S, loaded one step earlier) replaces it;
+  //  * otherwise (4 workgroups per CU, whose waves hide the latency): the
+  //    loads of tile kt+1 go into set 0 and replace tile kt after its
+  //    multiply.
+  // Measured on gfx950: one-deep staging at four workgroups per CU is the
+  // faster of the two for the K = 512 q/k/v and MLP-up GEMMs, two-deep at
+  // three for the residual GEMMs (whose epilogue needs more registers).
+  constexpr bool DEEP = EPI == EPI_RES;
 #define GM_STEP(kt, L, S)                                                             \
   {                                                                                   \
     GM_LOAD(min((kt) + 2, nk - 1), L);                                                \
@@ -256,12 +264,22 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
       __syncthreads();                                                                \
     }                                                                                 \
   }
+#define GM_STEP1(kt)                                                                  \
+  {                                                                                   \
+    GM_LOAD(min((kt) + 1, nk - 1), 0);                                                \
+    GM_COMPUTE_ANY();                                                                 \
+    if ((kt) + 1 < nk) {                                                              \
+      __syncthreads();                                                                \
+      GM_STORE(0);                                                                    \
+      __syncthreads();                                                                \
+    }                                                                                 \
+  }
 
   GM_LOAD(0, 0);
-  GM_LOAD(min(1, nk - 1), 1);
+  if constexpr (DEEP) GM_LOAD(min(1, nk - 1), 1);
   {
     // the per-column weight scales and per-row RMS factors (read by the
-    // epilogue only) load while the first two K tiles are in flight
+    // epilogue only) load while the first K tiles are in flight
     static_assert(BN <= 256 && BM <= 256, "one factor per thread");
     float sc_r = 0.0f, pw_r = 0.0f, ri_r = 0.0f;
     if (tid < BN) {
@@ -285,10 +303,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
     if (tid < BM) rinv_s[tid] = ri_r;
   }
   __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    GM_STEP(kt, 0, 1);
-    if (kt + 1 < nk) GM_STEP(kt + 1, 1, 0);
+  if constexpr (DEEP) {
+    for (int kt = 0; kt < nk; kt += 2) {
+      GM_STEP(kt, 0, 1);
+      if (kt + 1 < nk) GM_STEP(kt + 1, 1, 0);
+    }
+  } else {
+    for (int kt = 0; kt < nk; ++kt) GM_STEP1(kt);
   }
+#undef GM_STEP1
 #undef GM_STEP
 #undef GM_COMPUTE_ANY
 #undef GM_COMPUTE
@@ -544,7 +567,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
 }
 
 template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BN <= 128 ? 3 : 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BN > 128 ? 2 : EPI == EPI_RES ? 3 : 4)))
 void gemm_kernel(GemmArgs a) {
   static_assert(BM / 2 == 64, "the row placement works on 64-row slices");
   static_assert(EPI == EPI_QKV || BN / 2 == 64, "the column placement works on 64-column slices");
