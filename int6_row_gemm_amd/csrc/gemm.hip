@@ -11,8 +11,8 @@
 // (a per-row factor of C) is applied in the epilogue as well.
 //
 // Tiling: 256 threads = 4 waves in a 2 x 2 grid; workgroup tile BM x BN,
-// K step 64 through one XOR-swizzled LDS tile with register prefetch two K
-// steps ahead; each wave issues v_mfma_f32_16x16x32_bf16 on (BM/2) x (BN/2).
+// K step 64 through one XOR-swizzled LDS tile with register prefetch one K
+// step ahead; each wave issues v_mfma_f32_16x16x32_bf16 on (BM/2) x (BN/2).
 // Rows are placed in LDS so that every lane ends up owning runs of
 // consecutive output columns of one row (C^T accumulation: two runs of 8,
 // or whole rotation pairs of a q/k head), or, for the transposed V output,
@@ -135,14 +135,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
   const int wm = wave >> 1, wn = wave & 1;
   const int dq = a.n_heads * WN, dkv = a.n_kv * WN;
 
-  // Global -> register staging into one or two sets of named scalars
-  // (arrays of them end up in scratch memory).  Chunk
+  // Global -> register staging into named scalars (arrays of them end up
+  // in scratch memory).  Chunk
   // indices past the tile are clamped (those threads reload and rewrite the
   // last chunk with identical data); A rows past M are clamped to M - 1 and
   // their results are never stored.
   static_assert(A_PER <= 4 && B_PER <= 3, "staging holds 4 A and 3 B chunks per thread");
   uint4 sa0_0, sa0_1, sa0_2, sa0_3, sb0_0, sb0_1, sb0_2;
-  uint4 sa1_0, sa1_1, sa1_2, sa1_3, sb1_0, sb1_1, sb1_2;
   const int nk = a.K / BK;
   // per thread, for the whole K loop: the element offset of each A row it
   // loads, and the LDS offsets its A and B chunks go to
@@ -241,30 +240,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
   {                                                                                   \
     if constexpr (CT) GM_COMPUTE(MF_T) else GM_COMPUTE(MF_C)                          \
   }
-  // Two ways through K, both with a single LDS tile (small enough for
-  // several workgroups per CU, whose epilogues then overlap the others'
-  // MFMA work):
-  //  * DEEP (residual epilogue, 3 workgroups per CU): the loads of K tile
-  //    kt+2 go into register set L while tile kt is multiplied out of LDS,
-  //    then tile kt+1 (set S, loaded one step earlier) replaces it;
-  //  * otherwise (4 workgroups per CU, whose waves hide the latency): the
-  //    loads of tile kt+1 go into set 0 and replace tile kt after its
-  //    multiply.
-  // Measured on gfx950: one-deep staging at four workgroups per CU is the
-  // faster of the two for the K = 512 q/k/v and MLP-up GEMMs, two-deep at
-  // three for the residual GEMMs (whose epilogue needs more registers).
-  constexpr bool DEEP = EPI == EPI_RES;
-#define GM_STEP(kt, L, S)                                                             \
-  {                                                                                   \
-    GM_LOAD(min((kt) + 2, nk - 1), L);                                                \
-    GM_COMPUTE_ANY();                                                                 \
-    if ((kt) + 1 < nk) {                                                              \
-      __syncthreads();                                                                \
-      GM_STORE(S);                                                                    \
-      __syncthreads();                                                                \
-    }                                                                                 \
-  }
-#define GM_STEP1(kt)                                                                  \
+  // One K tile: the loads of tile kt+1 go into the staging registers while
+  // tile kt is multiplied out of the single LDS tile, then replace it.  One
+  // staging set and one LDS tile keep the kernel within 128 VGPRs and 34 KB
+  // of LDS, so four workgroups share a CU and their waves hide the load
+  // latency (measured on gfx950 to beat two-deep register prefetch at three
+  // workgroups per CU); their epilogues overlap the others' MFMA work.
+#define GM_STEP(kt)                                                                   \
   {                                                                                   \
     GM_LOAD(min((kt) + 1, nk - 1), 0);                                                \
     GM_COMPUTE_ANY();                                                                 \
@@ -276,10 +258,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
   }
 
   GM_LOAD(0, 0);
-  if constexpr (DEEP) GM_LOAD(min(1, nk - 1), 1);
   {
     // the per-column weight scales and per-row RMS factors (read by the
-    // epilogue only) load while the first K tiles are in flight
+    // epilogue only) load while the first K tile is in flight
     static_assert(BN <= 256 && BM <= 256, "one factor per thread");
     float sc_r = 0.0f, pw_r = 0.0f, ri_r = 0.0f;
     if (tid < BN) {
@@ -303,15 +284,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
     if (tid < BM) rinv_s[tid] = ri_r;
   }
   __syncthreads();
-  if constexpr (DEEP) {
-    for (int kt = 0; kt < nk; kt += 2) {
-      GM_STEP(kt, 0, 1);
-      if (kt + 1 < nk) GM_STEP(kt + 1, 1, 0);
-    }
-  } else {
-    for (int kt = 0; kt < nk; ++kt) GM_STEP1(kt);
-  }
-#undef GM_STEP1
+  for (int kt = 0; kt < nk; ++kt) GM_STEP(kt);
 #undef GM_STEP
 #undef GM_COMPUTE_ANY
 #undef GM_COMPUTE
@@ -370,82 +343,87 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
       const int64_t mr = a.e_map ? scored_row(a.p0 + mm, a.k0, a.n_win, a.e0, a.L, a.S, a.Lp) : mm;
       off[i] = mr * a.N + n0;
     }
-    // the residual rows first, so that all their loads are in flight together
-    float4 xv[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) xv[i][j] = *reinterpret_cast<const float4*>(a.x + off[i] + colj(j));
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const float4 s4 = *reinterpret_cast<const float4*>(scale_s + colj(j));
-        xv[i][j].x += acc[i][j][0] * s4.x;
-        xv[i][j].y += acc[i][j][1] * s4.y;
-        xv[i][j].z += acc[i][j][2] * s4.z;
-        xv[i][j].w += acc[i][j][3] * s4.w;
-      }
-    if (push) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        if (ok[i]) {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) *reinterpret_cast<float4*>(a.push_dst + off[i] + colj(j)) = xv[i][j];
-        }
-    }
-    if (pop) {
-      if (pop_self) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const float4 w4 = *reinterpret_cast<const float4*>(popw_s + colj(j));
-            xv[i][j].x += w4.x * xv[i][j].x;
-            xv[i][j].y += w4.y * xv[i][j].y;
-            xv[i][j].z += w4.z * xv[i][j].z;
-            xv[i][j].w += w4.w * xv[i][j].w;
-          }
-      } else {
-        float4 pv[FM][FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) pv[i][j] = *reinterpret_cast<const float4*>(a.pop_src + off[i] + colj(j));
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const float4 w4 = *reinterpret_cast<const float4*>(popw_s + colj(j));
-            xv[i][j].x += w4.x * pv[i][j].x;
-            xv[i][j].y += w4.y * pv[i][j].y;
-            xv[i][j].z += w4.z * pv[i][j].z;
-            xv[i][j].w += w4.w * pv[i][j].w;
-          }
-      }
-    }
+    // the residual rows in two halves of FM/2 row blocks, each half's loads
+    // in flight together
     float sq[FM];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      float t = 0.0f;
+    for (int hh = 0; hh < 2; ++hh) {
+      constexpr int FH = FM / 2;
+      float4 xv[FH][FN];
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        t += xv[i][j].x * xv[i][j].x + xv[i][j].y * xv[i][j].y + xv[i][j].z * xv[i][j].z +
-             xv[i][j].w * xv[i][j].w;
-      sq[i] = t;
-      if (ok[i]) {
+      for (int ii = 0; ii < FH; ++ii)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) *reinterpret_cast<float4*>(a.x + off[i] + colj(j)) = xv[i][j];
-        if (a.xb) {
+        for (int j = 0; j < FN; ++j) xv[ii][j] = *reinterpret_cast<const float4*>(a.x + off[hh * FH + ii] + colj(j));
 #pragma unroll
-          for (int p = 0; p < FN / 2; ++p) {
-            const f32x4 u0 = {xv[i][2 * p].x, xv[i][2 * p].y, xv[i][2 * p].z, xv[i][2 * p].w};
-            const f32x4 u1 = {xv[i][2 * p + 1].x, xv[i][2 * p + 1].y, xv[i][2 * p + 1].z, xv[i][2 * p + 1].w};
-            *reinterpret_cast<uint4*>(a.xb + off[i] + colj(2 * p)) = make_uint4(
-                (uint32_t)f2bf_bits(u0[0]) | ((uint32_t)f2bf_bits(u0[1]) << 16),
-                (uint32_t)f2bf_bits(u0[2]) | ((uint32_t)f2bf_bits(u0[3]) << 16),
-                (uint32_t)f2bf_bits(u1[0]) | ((uint32_t)f2bf_bits(u1[1]) << 16),
-                (uint32_t)f2bf_bits(u1[2]) | ((uint32_t)f2bf_bits(u1[3]) << 16));
+      for (int ii = 0; ii < FH; ++ii) {
+        const int i = hh * FH + ii;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const float4 s4 = *reinterpret_cast<const float4*>(scale_s + colj(j));
+          xv[ii][j].x += acc[i][j][0] * s4.x;
+          xv[ii][j].y += acc[i][j][1] * s4.y;
+          xv[ii][j].z += acc[i][j][2] * s4.z;
+          xv[ii][j].w += acc[i][j][3] * s4.w;
+        }
+        if (push && ok[i]) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) *reinterpret_cast<float4*>(a.push_dst + off[i] + colj(j)) = xv[ii][j];
+        }
+      }
+      if (pop) {
+        if (pop_self) {
+#pragma unroll
+          for (int ii = 0; ii < FH; ++ii)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const float4 w4 = *reinterpret_cast<const float4*>(popw_s + colj(j));
+              xv[ii][j].x += w4.x * xv[ii][j].x;
+              xv[ii][j].y += w4.y * xv[ii][j].y;
+              xv[ii][j].z += w4.z * xv[ii][j].z;
+              xv[ii][j].w += w4.w * xv[ii][j].w;
+            }
+        } else {
+          float4 pv[FH][FN];
+#pragma unroll
+          for (int ii = 0; ii < FH; ++ii)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              pv[ii][j] = *reinterpret_cast<const float4*>(a.pop_src + off[hh * FH + ii] + colj(j));
+#pragma unroll
+          for (int ii = 0; ii < FH; ++ii)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const float4 w4 = *reinterpret_cast<const float4*>(popw_s + colj(j));
+              xv[ii][j].x += w4.x * pv[ii][j].x;
+              xv[ii][j].y += w4.y * pv[ii][j].y;
+              xv[ii][j].z += w4.z * pv[ii][j].z;
+              xv[ii][j].w += w4.w * pv[ii][j].w;
+            }
+        }
+      }
+#pragma unroll
+      for (int ii = 0; ii < FH; ++ii) {
+        const int i = hh * FH + ii;
+        float t = 0.0f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          t += xv[ii][j].x * xv[ii][j].x + xv[ii][j].y * xv[ii][j].y + xv[ii][j].z * xv[ii][j].z +
+               xv[ii][j].w * xv[ii][j].w;
+        sq[i] = t;
+        if (ok[i]) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) *reinterpret_cast<float4*>(a.x + off[i] + colj(j)) = xv[ii][j];
+          if (a.xb) {
+#pragma unroll
+            for (int p = 0; p < FN / 2; ++p) {
+              const f32x4 u0 = {xv[ii][2 * p].x, xv[ii][2 * p].y, xv[ii][2 * p].z, xv[ii][2 * p].w};
+              const f32x4 u1 = {xv[ii][2 * p + 1].x, xv[ii][2 * p + 1].y, xv[ii][2 * p + 1].z, xv[ii][2 * p + 1].w};
+              *reinterpret_cast<uint4*>(a.xb + off[i] + colj(2 * p)) = make_uint4(
+                  (uint32_t)f2bf_bits(u0[0]) | ((uint32_t)f2bf_bits(u0[1]) << 16),
+                  (uint32_t)f2bf_bits(u0[2]) | ((uint32_t)f2bf_bits(u0[3]) << 16),
+                  (uint32_t)f2bf_bits(u1[0]) | ((uint32_t)f2bf_bits(u1[1]) << 16),
+                  (uint32_t)f2bf_bits(u1[2]) | ((uint32_t)f2bf_bits(u1[3]) << 16));
+            }
           }
         }
       }
@@ -567,7 +545,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
 }
 
 template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BN > 128 ? 2 : EPI == EPI_RES ? 3 : 4)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BN > 128 ? 2 : 4)))
 void gemm_kernel(GemmArgs a) {
   static_assert(BM / 2 == 64, "the row placement works on 64-row slices");
   static_assert(EPI == EPI_QKV || BN / 2 == 64, "the column placement works on 64-column slices");
