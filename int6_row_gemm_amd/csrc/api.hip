@@ -550,9 +550,18 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
 
       const double rows_mlp = pr ? (double)R : real_rows;
       const double fl_o = 2.0 * rows_mlp * d * d, fl_fc = 2.0 * rows_mlp * F * d;
-      const double by_o = rows_mlp * (2.0 * d + 4.0 * d * 2 + 2.0 * d) + (double)d * d;
+      // algorithmic HBM bytes: A read, fp32 residual read + write, bf16 copy,
+      // skip slot written / read, codes (scales and sums of squares are small)
+      auto res_bytes = [&](const GemmArgs& g, double a_cols) {
+        double per_row = 2.0 * a_cols + 8.0 * d;
+        if (g.xb) per_row += 2.0 * d;
+        if (g.push_dst) per_row += 4.0 * d;
+        if (g.pop_src && g.pop_src != g.push_dst) per_row += 4.0 * d;
+        return rows_mlp * per_row + a_cols * d;
+      };
+      const double by_o = res_bytes(go, d);
       const double by_fc = rows_mlp * (2.0 * d + 2.0 * F) + (double)F * d;
-      const double by_p = rows_mlp * (2.0 * F + 4.0 * d * 2 + 2.0 * d) + (double)F * d;
+      const double by_p = res_bytes(gp, F);
       auto run_o = [&] {
         return timed(m, I6G_K_OPROJ, s, fl_o, by_o, [&] { return launch_gemm(EPI_RES, go, s); });
       };
