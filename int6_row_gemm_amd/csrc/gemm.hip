@@ -46,10 +46,11 @@ __device__ inline float h2f(uint16_t h) {
 
 __device__ inline uint32_t pack_bf16x2_from_int(int lo, int hi) {
   // integers of magnitude <= 128 are exact in fp32 and keep only 8
-  // significant bits, so the upper half of the fp32 pattern is the bf16.
-  uint32_t a = __builtin_bit_cast(uint32_t, (float)lo);
-  uint32_t b = __builtin_bit_cast(uint32_t, (float)hi);
-  return (a >> 16) | (b & 0xffff0000u);
+  // significant bits, so the upper half of the fp32 pattern is the bf16;
+  // one byte permute takes both upper halves (bytes 2, 3 of lo, then of hi)
+  const uint32_t a = __builtin_bit_cast(uint32_t, (float)lo);
+  const uint32_t b = __builtin_bit_cast(uint32_t, (float)hi);
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
 __device__ inline uint16_t f2bf_bits(float f) {
