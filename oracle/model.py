@@ -13,6 +13,11 @@ Sources (page, section):
   * pigsec.cn openai/parameter-golf README mirror, leaderboard entries:
     parallel attention/MLP residual lanes; layers 4-5 looped.
 
+Evaluation variants from the PR #363 write-up (off by default): logits
+divided by a temperature; LeakyReLU(slope)^2 in place of ReLU^2; RoPE on the
+first R dims of each head; exclusive self attention on the last N effective
+layers.
+
 Readings (listed in the design doc): pre-norm RMSNorm without gain, eps 1e-6, and a
 final norm before the tied head; attention scale 1/sqrt(head_dim), no other
 logit transforms; query head h reads KV head floor(h*Hkv/Hq); RoPE on all
@@ -36,19 +41,45 @@ def rms_norm(z: np.ndarray, eps: float) -> np.ndarray:
     return z / np.sqrt(np.mean(z * z, axis=-1, keepdims=True) + eps)
 
 
-def rope(x: np.ndarray, base: float, positions=None) -> np.ndarray:
-    """Rotary embedding of x [T, H, hd]: pairs (i, i + hd/2) rotated by
-    angle p * base^(-2i/hd) at position p."""
+def rope(x: np.ndarray, base: float, positions=None, dims=None) -> np.ndarray:
+    """Rotary embedding of x [T, H, hd]: pairs (i, i + R/2) rotated by angle
+    p * base^(-2i/R) at position p, for the first R = dims dims of each head
+    (all of them when dims is None); the other hd - R dims pass unchanged
+    (partial RoPE, kwkr.cn PR #363 write-up, "Partial RoPE 16/64")."""
     T, _, hd = x.shape
-    half = hd // 2
+    R = hd if dims is None else int(dims)
+    half = R // 2
     if positions is None:
         positions = np.arange(T, dtype=F64)
-    theta = base ** (-2.0 * np.arange(half, dtype=F64) / hd)
+    theta = base ** (-2.0 * np.arange(half, dtype=F64) / R)
     ang = np.asarray(positions, dtype=F64)[:, None] * theta[None, :]
     cos = np.cos(ang)[:, None, :]
     sin = np.sin(ang)[:, None, :]
-    x1, x2 = x[..., :half], x[..., half:]
-    return np.concatenate([x1 * cos - x2 * sin, x1 * sin + x2 * cos], axis=-1)
+    x1, x2 = x[..., :half], x[..., half:R]
+    return np.concatenate([x1 * cos - x2 * sin, x1 * sin + x2 * cos, x[..., R:]], axis=-1)
+
+
+def exclusive_self_attention(o: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """XSA (kwkr.cn PR #363 write-up, XSA paragraph): remove from each query
+    head's attention output o_h[j] its component along the value vector of
+    the same position, v_g[j] (g = the head's KV head); a zero value vector
+    leaves o unchanged.  o [T, Hq, hd], v [T, Hkv, hd]."""
+    T, Hq, hd = o.shape
+    Hkv = v.shape[1]
+    out = o.copy()
+    for h in range(Hq):
+        g = (h * Hkv) // Hq
+        vv = v[:, g, :]
+        nn = np.sum(vv * vv, axis=1)
+        dot = np.sum(o[:, h, :] * vv, axis=1)
+        coef = np.where(nn > 0, dot / np.where(nn > 0, nn, 1.0), 0.0)
+        out[:, h, :] = o[:, h, :] - coef[:, None] * vv
+    return out
+
+
+def mlp_act(z: np.ndarray, slope: float) -> np.ndarray:
+    """(leaky_relu(z, slope))^2; slope 0 is the ReLU^2 of [11L] 架构."""
+    return np.square(np.where(z >= 0.0, z, slope * z))
 
 
 def causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
@@ -76,11 +107,12 @@ def dense_weights(qblock: dict) -> dict:
     return {name: dequantize(*cs) for name, cs in qblock.items()}
 
 
-def block_forward(x, W, arch, lora=None):
+def block_forward(x, W, arch, lora=None, xsa=False):
     """One transformer block on x [T, d] (float64).
 
     ``W`` holds dequantised [out, in] matrices q, k, v, o, fc, proj.
     ``lora`` is None or (Aq [r,d], Bq [d,r], Av [r,kvd], Bv [kvd,r]) as float64.
+    ``xsa`` applies exclusive self attention to this layer's attention output.
     """
     T, d = x.shape
     Hq, Hkv, hd = arch["n_heads"], arch["n_kv_heads"], arch["head_dim"]
@@ -93,17 +125,21 @@ def block_forward(x, W, arch, lora=None):
         aq, bq, av, bv = lora
         q = q + (a @ aq.T) @ bq.T
         v = v + (a @ av.T) @ bv.T
-    q = rope(q.reshape(T, Hq, hd), arch["rope_base"])
-    k = rope(k.reshape(T, Hkv, hd), arch["rope_base"])
+    rd = arch.get("rope_dims")
+    q = rope(q.reshape(T, Hq, hd), arch["rope_base"], dims=rd)
+    k = rope(k.reshape(T, Hkv, hd), arch["rope_base"], dims=rd)
     v = v.reshape(T, Hkv, hd)
-    o = causal_attention(q, k, v).reshape(T, Hq * hd)
-    attn_out = o @ W["o"].T
+    o = causal_attention(q, k, v)
+    if xsa:
+        o = exclusive_self_attention(o, v)
+    attn_out = o.reshape(T, Hq * hd) @ W["o"].T
+    slope = arch.get("leaky_slope", 0.0)
     if arch["parallel"]:
-        mlp_out = np.square(np.maximum(a @ W["fc"].T, 0.0)) @ W["proj"].T
+        mlp_out = mlp_act(a @ W["fc"].T, slope) @ W["proj"].T
         return x + attn_out + mlp_out
     x = x + attn_out
     a2 = rms_norm(x, eps)
-    return x + np.square(np.maximum(a2 @ W["fc"].T, 0.0)) @ W["proj"].T
+    return x + mlp_act(a2 @ W["fc"].T, slope) @ W["proj"].T
 
 
 def skip_plan(arch):
@@ -158,17 +194,21 @@ def window_logits(qmodel: dict, u: np.ndarray, dense=None) -> np.ndarray:
     skip_w = None if qmodel.get("skip_w") is None else qmodel["skip_w"].astype(F64)
     stack = []
     lora = qmodel.get("lora")
+    n_eff = len(arch["schedule"])
+    xsa_from = n_eff - arch.get("xsa_last_n", 0)
     for e, b in enumerate(arch["schedule"]):
         if pop[e] >= 0:
             x = x + skip_w[pop[e]] * stack.pop()
         lo = None
         if lora is not None:
             lo = tuple(lora[n][e].astype(F64) for n in ("aq", "bq", "av", "bv"))
-        x = block_forward(x, dense[b], arch, lo)
+        x = block_forward(x, dense[b], arch, lo, xsa=e >= xsa_from)
         if push[e]:
             stack.append(x)
     z = rms_norm(x, eps)
-    return z @ E.T
+    # evaluation temperature (kwkr.cn PR #363 write-up, EVAL_TEMPERATURE):
+    # the logits the softmax sees are divided by T
+    return (z @ E.T) / arch.get("temperature", 1.0)
 
 
 def log_softmax_nll(logits: np.ndarray, targets: np.ndarray) -> np.ndarray:

@@ -47,6 +47,14 @@ _BASE = dict(
     embed_dtype="fp16",
     bits=6,
     clip_q=0.9999984,
+    # evaluation variants (off by default): logits divided by the
+    # temperature, MLP activation leaky_relu(x, slope)^2, RoPE on the first
+    # rope_dims dims of each head (None = all), exclusive self attention on
+    # the last xsa_last_n effective layers
+    temperature=1.0,
+    leaky_slope=0.0,
+    rope_dims=None,
+    xsa_last_n=0,
 )
 
 
@@ -83,6 +91,16 @@ CONFIGS = {
                    skip_kind=SKIP_STEM_TAIL, n_skip=3, lora_rank=4,
                    bigram_buckets=4096, bigram_dim=128),
         n_tokens=32 * 2048 + 1, zipf=1.1, bytes_max=8, window=2048, stride=2048,
+    ),
+    # the 11-layer model with the evaluation variants the pages list next:
+    # temperature 0.90, LeakyReLU(0.5)^2, partial RoPE 16/64, XSA on the last
+    # 4 effective layers, and a cyclic schedule i % 4 over 11 effective
+    # layers with U-Net skips over the effective depth
+    "11l_next": dict(
+        arch=_arch(vocab=1024, d_model=512, n_heads=8, n_kv_heads=4, mlp_mult=3,
+                   schedule=[i % 4 for i in range(11)], skip_kind=SKIP_UNET, n_skip=5,
+                   temperature=0.90, leaky_slope=0.5, rope_dims=16, xsa_last_n=4),
+        n_tokens=1_048_576, zipf=1.1, bytes_max=8, window=2048, stride=64,
     ),
     "largevocab": dict(
         arch=_arch(vocab=8192, d_model=512, n_heads=8, n_kv_heads=4, mlp_mult=4,

@@ -25,6 +25,7 @@ import pytest
 from scipy.special import logsumexp
 
 import synth
+from oracle import quant as oq
 from oracle import quant, model as om, windows as ow
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -325,3 +326,146 @@ def test_stride_one_is_per_prediction_context():
         lg = om.window_logits(qm, ctx)
         want = om.log_softmax_nll(lg[-1:], tokens[p + 1: p + 2])[0]
         assert abs(nats[p] - want) < 1e-12, p
+
+
+# ---------------------------------------------------------------------------
+# Evaluation variants (kwkr.cn PR #363 write-up: EVAL_TEMPERATURE, LeakyReLU,
+# Partial RoPE 16/64, XSA on the last layers, cyclic block schedule)
+# ---------------------------------------------------------------------------
+
+def test_partial_rope_hand_example_and_passthrough():
+    # hd = 6, R = 4: pairs (0, 2) and (1, 3) with theta = 1 and 10000^(-1/2);
+    # dims 4, 5 unrotated
+    x = np.arange(1.0, 7.0).reshape(1, 1, 6) * np.ones((2, 1, 6))
+    y = om.rope(x, 10000.0, dims=4)
+    assert np.array_equal(y[0], x[0])                 # position 0: identity
+    a0, a1 = 1.0, 0.01
+    x1 = np.array([1.0, 2.0]); x2 = np.array([3.0, 4.0])
+    c = np.cos([a0, a1]); s = np.sin([a0, a1])
+    want = np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c, [5.0, 6.0]])
+    np.testing.assert_allclose(y[1, 0], want, rtol=0, atol=1e-15)
+
+
+def test_partial_rope_reduces_to_full_rope_on_its_dims():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((9, 2, 64))
+    full = om.rope(x, 10000.0)
+    assert np.array_equal(om.rope(x, 10000.0, dims=64), full)
+    part = om.rope(x, 10000.0, dims=16)
+    np.testing.assert_array_equal(part[..., 16:], x[..., 16:])
+    np.testing.assert_allclose(part[..., :16], om.rope(x[..., :16].copy(), 10000.0), rtol=0, atol=1e-14)
+
+
+def test_partial_rope_scores_depend_on_relative_position_only():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal(64); k = rng.standard_normal(64)
+    def score(m, n):
+        qq = om.rope(np.tile(q, (max(m, n) + 1, 1, 1)), 10000.0, dims=16)[m, 0]
+        kk = om.rope(np.tile(k, (max(m, n) + 1, 1, 1)), 10000.0, dims=16)[n, 0]
+        return qq @ kk
+    assert abs(score(7, 3) - score(14, 10)) < 1e-12
+    assert abs(score(5, 5) - q @ k) < 1e-12
+
+
+def test_xsa_removes_the_own_value_component():
+    rng = np.random.default_rng(5)
+    T, Hq, Hkv, hd = 6, 4, 2, 8
+    o = rng.standard_normal((T, Hq, hd)); v = rng.standard_normal((T, Hkv, hd))
+    y = om.exclusive_self_attention(o, v)
+    for h in range(Hq):
+        g = (h * Hkv) // Hq
+        # orthogonal to the own-position value vector ...
+        np.testing.assert_allclose(np.sum(y[:, h] * v[:, g], axis=1), 0.0, atol=1e-12)
+        # ... and o minus y is parallel to it
+        d = o[:, h] - y[:, h]
+        cross = d[:, :, None] * v[:, g, None, :] - d[:, None, :] * v[:, g, :, None]
+        np.testing.assert_allclose(cross, 0.0, atol=1e-12)
+    # o along v -> 0; o orthogonal to v -> unchanged; zero v -> unchanged
+    vv = rng.standard_normal((1, 1, hd))
+    assert np.allclose(om.exclusive_self_attention(3.0 * vv, vv), 0.0)
+    w = rng.standard_normal(hd); w -= (w @ vv[0, 0]) / (vv[0, 0] @ vv[0, 0]) * vv[0, 0]
+    np.testing.assert_allclose(om.exclusive_self_attention(w.reshape(1, 1, hd), vv), w.reshape(1, 1, hd), atol=1e-13)
+    assert np.array_equal(om.exclusive_self_attention(o[:1, :1], np.zeros((1, 1, hd))), o[:1, :1])
+
+
+def test_xsa_single_token_window_cancels_attention():
+    # one position: attention returns the value itself, so XSA leaves only
+    # the MLP branch of the block
+    rng = np.random.default_rng(6)
+    arch = dict(n_heads=4, n_kv_heads=2, head_dim=8, norm_eps=1e-6, rope_base=10000.0,
+                parallel=False, leaky_slope=0.0, rope_dims=None)
+    d, F = 32, 64
+    W = {"q": rng.standard_normal((d, d)), "k": rng.standard_normal((16, d)),
+         "v": rng.standard_normal((16, d)), "o": rng.standard_normal((d, d)),
+         "fc": rng.standard_normal((F, d)), "proj": rng.standard_normal((d, F))}
+    x = rng.standard_normal((1, d))
+    y = om.block_forward(x, W, arch, xsa=True)
+    a2 = om.rms_norm(x, 1e-6)
+    want = x + np.square(np.maximum(a2 @ W["fc"].T, 0.0)) @ W["proj"].T
+    np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-12)
+
+
+def test_leaky_relu_square_hand_values():
+    z = np.array([-2.0, -0.5, 0.0, 3.0])
+    np.testing.assert_array_equal(om.mlp_act(z, 0.5), [1.0, 0.0625, 0.0, 9.0])
+    np.testing.assert_array_equal(om.mlp_act(z, 0.0), [0.0, 0.0, 0.0, 9.0])
+    np.testing.assert_array_equal(om.mlp_act(z, 1.0), z * z)
+
+
+def _tiny_variant_model(**kw):
+    cfg = synth.config("11l_next", d_model=128, n_heads=2, n_kv_heads=1, vocab=128,
+                       schedule=[0, 1, 0, 1], n_skip=2, **kw)
+    model = synth.make_model(cfg["arch"], seed=7)
+    return cfg, oq.quantize_model(model)
+
+
+def test_temperature_scales_logits_and_two_logit_closed_form():
+    cfg, qm = _tiny_variant_model()
+    u = np.arange(10) % 128
+    base = dict(qm); base["arch"] = dict(qm["arch"], temperature=1.0)
+    hot = dict(qm); hot["arch"] = dict(qm["arch"], temperature=0.9)
+    np.testing.assert_allclose(om.window_logits(hot, u), om.window_logits(base, u) / 0.9, rtol=1e-15)
+    # two logits (a, b), target 0: nats = log(1 + exp((b - a)))
+    a, b = 0.3, 1.7
+    assert abs(om.log_softmax_nll(np.array([[a, b]]), np.array([0]))[0] - np.log1p(np.exp(b - a))) < 1e-15
+
+
+def test_variants_off_reduce_to_the_base_model():
+    cfg, qm = _tiny_variant_model()
+    u = (np.arange(40) * 7) % 128
+    off = dict(qm); off["arch"] = dict(qm["arch"], temperature=1.0, leaky_slope=0.0,
+                                        rope_dims=None, xsa_last_n=0)
+    plain = dict(qm); plain["arch"] = {k: v for k, v in off["arch"].items()
+                                       if k not in ("temperature", "leaky_slope", "rope_dims", "xsa_last_n")}
+    assert np.array_equal(om.window_logits(off, u), om.window_logits(plain, u))
+    full_rope = dict(qm); full_rope["arch"] = dict(off["arch"], rope_dims=qm["arch"]["head_dim"])
+    assert np.array_equal(om.window_logits(full_rope, u), om.window_logits(off, u))
+
+
+def test_xsa_last_n_picks_the_last_effective_layers():
+    # XSA on the last N layers = applying block_forward with xsa to exactly
+    # those layers by hand (4 effective layers, U-Net 2/2)
+    cfg, qm = _tiny_variant_model(xsa_last_n=1, temperature=1.0)
+    arch = qm["arch"]
+    u = (np.arange(12) * 5) % 128
+    dense = [om.dense_weights(qb) for qb in qm["qblocks"]]
+    E = qm["embed"].astype(np.float64)
+    x = E[u]
+    skip_w = qm["skip_w"].astype(np.float64)
+    stack = []
+    for e, b in enumerate(arch["schedule"]):
+        if e >= 2:
+            x = x + skip_w[e - 2] * stack.pop()
+        x = om.block_forward(x, dense[b], arch, None, xsa=(e == 3))
+        if e < 2:
+            stack.append(x)
+    want = om.rms_norm(x, arch["norm_eps"]) @ E.T
+    np.testing.assert_allclose(om.window_logits(qm, u, dense), want, rtol=1e-13, atol=1e-13)
+
+
+def test_cyclic_schedule_config():
+    a = synth.CONFIGS["11l_next"]["arch"]
+    assert a["schedule"] == [i % 4 for i in range(11)] and a["n_unique"] == 4
+    push, pop = om.skip_plan(a)
+    assert push == [True] * 5 + [False] * 6
+    assert pop == [-1] * 5 + [0, 1, 2, 3, 4, -1]
