@@ -181,6 +181,24 @@ def main():
                       if c in kernels)
         gemm_frac = (gsum_fl / gsum_ms) / PEAK_BF16_TFLOPS if gsum_ms else None
 
+    # The quantiser on its own (HBM-bound): all 66 matrices, repeated; its
+    # algorithmic bytes are 4 B read + 1 B written per weight + 2 B per row.
+    quant = None
+    if not args.no_timing:
+        n_w = sum(w.numel() for wb in w_dev for w in wb.values())
+        n_r = sum(w.shape[0] for wb in w_dev for w in wb.values())
+        reps = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            quantize_all()
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1000.0 * e0.elapsed_time(e1) / reps
+        by = 5.0 * n_w + 2.0 * n_r
+        quant = {"matrices": sum(len(wb) for wb in w_dev), "weights": n_w, "us_per_pass": us,
+                 "algorithmic_bytes": by, "gbs": by / (us * 1e3), "frac_hbm": by / (us * 1e3) / PEAK_HBM_GBS}
+
     cpu = None
     if args.cpu_windows > 0:
         cpu = cpu_baseline(model, tokens_np, L, S, args.cpu_windows)
@@ -206,6 +224,7 @@ def main():
         "gemm_mfma_frac": gemm_frac,
         "roofline": roofline,
         "kernels_warmup_step": kernels,
+        "quantize_rows": quant,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

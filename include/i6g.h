@@ -133,6 +133,21 @@ typedef struct {
  * bigram_buckets, bigram_dim, bigram_table [buckets, dim], bigram_proj
  *     [d, dim] (binary16): x0[j] += proj * table[(u[j-1]*1000003 + u[j])
  *     mod buckets] for window positions j >= 1.  0 buckets = off.
+ *
+ * Evaluation variants ([363]: EVAL_TEMPERATURE, LeakyReLU, Partial RoPE
+ * 16/64, XSA on the last layers); zero selects the base model:
+ * logit_temperature  the logits are divided by it before the log-softmax
+ *                    (0 or 1 = off; otherwise > 0).
+ * leaky_slope        MLP activation leaky_relu(z, slope)^2 (0 = ReLU^2).
+ * rope_dims          RoPE on the first rope_dims dims of each head: pairs
+ *                    (i, i + rope_dims/2), theta_i = base^(-2i/rope_dims);
+ *                    the other dims are not rotated.  0 = head_dim;
+ *                    otherwise a multiple of head_dim/4 in [head_dim/4,
+ *                    head_dim].
+ * xsa_last_n         exclusive self attention on the last xsa_last_n
+ *                    effective layers (0..n_eff): each head's attention
+ *                    output loses its component along the value vector of
+ *                    the same position (unchanged where that vector is 0).
  */
 typedef struct {
   int32_t vocab, d_model, n_heads, n_kv_heads, head_dim, d_ff;
@@ -149,6 +164,8 @@ typedef struct {
   const uint16_t *lora_aq, *lora_bq, *lora_av, *lora_bv;
   int32_t bigram_buckets, bigram_dim;
   const uint16_t *bigram_table, *bigram_proj;
+  double logit_temperature, leaky_slope;
+  int32_t rope_dims, xsa_last_n;
 } i6g_model_desc;
 
 typedef struct i6g_model i6g_model; /* opaque, owned by the library */

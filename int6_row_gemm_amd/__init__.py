@@ -56,6 +56,8 @@ class _Desc(ctypes.Structure):
         ("lora_av", ctypes.c_void_p), ("lora_bv", ctypes.c_void_p),
         ("bigram_buckets", ctypes.c_int32), ("bigram_dim", ctypes.c_int32),
         ("bigram_table", ctypes.c_void_p), ("bigram_proj", ctypes.c_void_p),
+        ("logit_temperature", ctypes.c_double), ("leaky_slope", ctypes.c_double),
+        ("rope_dims", ctypes.c_int32), ("xsa_last_n", ctypes.c_int32),
     ]
 
 
@@ -152,7 +154,8 @@ class Model:
     ``arch`` uses the keys of the synthetic configurations (vocab, d_model,
     n_heads, n_kv_heads, head_dim, d_ff, rope_base, norm_eps, schedule,
     skip_kind, n_skip, parallel, lora_rank, bigram_buckets, bigram_dim,
-    embed_dtype).  ``qblocks`` is a list of dicts name -> (codes, scales)
+    embed_dtype, and the evaluation variants temperature, leaky_slope,
+    rope_dims, xsa_last_n).  ``qblocks`` is a list of dicts name -> (codes, scales)
     for q, k, v, o, fc, proj (device or host tensors / arrays)."""
 
     def __init__(self, arch, qblocks, embed, skip_w=None, lora=None, bigram=None):
@@ -195,6 +198,10 @@ class Model:
             t1, t2 = _f16_bits(bigram["table"]), _f16_bits(bigram["proj"])
             keep += [t1, t2]
             d.bigram_table, d.bigram_proj = t1.data_ptr(), t2.data_ptr()
+        d.logit_temperature = float(arch.get("temperature", 1.0))
+        d.leaky_slope = float(arch.get("leaky_slope", 0.0))
+        d.rope_dims = int(arch.get("rope_dims") or 0)
+        d.xsa_last_n = int(arch.get("xsa_last_n", 0))
         torch.cuda.synchronize()
         h = ctypes.c_void_p(0)
         _check(lib().i6g_load_model(ctypes.byref(d), _stream(), ctypes.byref(h)))

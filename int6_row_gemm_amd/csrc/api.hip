@@ -11,6 +11,7 @@
 // GEMM that produces the layer's output.
 #include "../../include/i6g.h"
 #include "common.h"
+#include <cmath>
 
 #include <math.h>
 #include <stdarg.h>
@@ -94,6 +95,9 @@ struct i6g_model {
   std::vector<int> schedule, push_after, pop_before, pop_slot, push_slot;
   int max_depth = 0;
   int skip_kind, n_skip, parallel, lora_r, buckets, bigram_dim, embed_f32;
+  // evaluation variants
+  float inv_temp = 1.0f, leaky = 0.0f;
+  int rope_dims = 0, xsa_last_n = 0;
   int device = 0;
   // weights
   std::vector<BlockDev> blocks;
@@ -215,7 +219,7 @@ int ensure_scratch(i6g_model* m, int W, int Lp, hipStream_t s) {
   }
   if (Lp > m->rope_L) {
     HIP_TRY(m->rope.ensure((size_t)Lp * (m->hd / 2) * sizeof(float2)));
-    HIP_TRY(launch_rope_table(m->rope.as<float2>(), Lp, m->hd, m->rope_base, s));
+    HIP_TRY(launch_rope_table(m->rope.as<float2>(), Lp, m->hd, m->rope_dims, m->rope_base, s));
     m->rope_L = Lp;
   }
   return I6G_OK;
@@ -306,6 +310,15 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
   for (int e = 0; e < D.n_eff; ++e)
     if (D.schedule[e] < 0 || D.schedule[e] >= D.n_unique)
       return fail(I6G_EINVAL, "load_model: schedule[%d] = %d out of range", e, D.schedule[e]);
+  if (!(D.logit_temperature >= 0.0) || !std::isfinite(D.logit_temperature))
+    return fail(I6G_EINVAL, "load_model: logit_temperature must be finite and >= 0 (0 = off)");
+  if (!std::isfinite(D.leaky_slope)) return fail(I6G_EINVAL, "load_model: leaky_slope must be finite");
+  if (D.xsa_last_n < 0 || D.xsa_last_n > D.n_eff)
+    return fail(I6G_EINVAL, "load_model: xsa_last_n must be in 0..n_eff");
+  if (D.rope_dims < 0 || D.rope_dims > D.head_dim)
+    return fail(I6G_EINVAL, "load_model: rope_dims must be in 0..head_dim");
+  if (D.rope_dims != 0 && D.rope_dims % (D.head_dim / 4))
+    return fail(I6G_EUNSUPPORTED, "load_model: rope_dims %d is not a multiple of head_dim/4", D.rope_dims);
 
   i6g_model* m = new i6g_model();
   m->V = D.vocab; m->d = D.d_model; m->Hq = D.n_heads; m->Hkv = D.n_kv_heads; m->hd = D.head_dim;
@@ -317,6 +330,11 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
   m->parallel = D.parallel_residual != 0; m->lora_r = D.lora_rank;
   m->buckets = D.bigram_buckets; m->bigram_dim = D.bigram_dim;
   m->embed_f32 = D.embed_dtype == I6G_DTYPE_F32;
+  m->inv_temp = (D.logit_temperature == 0.0 || D.logit_temperature == 1.0)
+                    ? 1.0f : (float)(1.0 / D.logit_temperature);
+  m->leaky = (float)D.leaky_slope;
+  m->rope_dims = D.rope_dims == 0 ? D.head_dim : D.rope_dims;
+  m->xsa_last_n = D.xsa_last_n;
   (void)hipGetDevice(&m->device);
 
   int rc = build_plan(m);
@@ -494,6 +512,7 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
       g.M = M; g.N = m->nqkv; g.K = d; g.ss_in = m->ss.as<float>(); g.nt_in = nt; g.eps = eps;
       g.q = m->q.as<bf16>(); g.k = m->k.as<bf16>(); g.vt = m->vt.as<bf16>();
       g.n_heads = m->Hq; g.n_kv = m->Hkv; g.hd = m->hd; g.Lp = Lp; g.rope = m->rope.as<float2>();
+      g.rope_dims = m->rope_dims;
       if (m->lora_r > 0) {
         g.lora_u = m->lora_u.as<float>(); g.lora_r = m->lora_r;
         g.lora_bq = m->lora_bq.as<float>() + (size_t)e * d * m->lora_r;
@@ -509,6 +528,7 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
       at.q = m->q.as<bf16>(); at.k = m->k.as<bf16>(); at.vt = m->vt.as<bf16>(); at.o = m->o.as<bf16>();
       at.W = W; at.n_heads = m->Hq; at.n_kv = m->Hkv; at.hd = m->hd; at.Lp = Lp; at.scale_log2 = scale_log2;
       at.prune = pr; at.k0 = k0; at.P = P; at.L = (int32_t)L; at.S = (int32_t)S;
+      at.xsa = e >= m->n_eff - m->xsa_last_n;
       if ((rc = timed(m, I6G_K_ATTN, s, 4.0 * m->hd * m->Hq * (pr ? attn_pairs_scored : attn_pairs),
                       real_rows * (2.0 * d + 4.0 * kvd),
                       [&] { return launch_attention(at, s); })))
@@ -523,7 +543,7 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
       GemmArgs gf{};
       gf.A = m->xb.as<bf16>(); gf.B = B.fc_codes.as<int8_t>(); gf.scale = B.fc_scales.as<uint16_t>();
       gf.M = M; gf.N = F; gf.K = d; gf.ss_in = m->ss.as<float>(); gf.nt_in = nt; gf.eps = eps;
-      gf.h = m->h.as<bf16>();
+      gf.h = m->h.as<bf16>(); gf.leaky = m->leaky;
 
       GemmArgs gp{};
       gp.A = m->h.as<bf16>(); gp.B = B.proj_codes.as<int8_t>(); gp.scale = B.proj_scales.as<uint16_t>();
@@ -584,7 +604,7 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
     ha.p0 = p0;
     ha.p1 = p1;
     ha.k0 = k0; ha.K = K; ha.e0 = e0; ha.L = (int32_t)L; ha.S = (int32_t)S; ha.Lp = Lp; ha.d = d;
-    ha.vocab = m->V; ha.eps = eps; ha.flags = m->flags.as<int32_t>();
+    ha.vocab = m->V; ha.eps = eps; ha.flags = m->flags.as<int32_t>(); ha.inv_temp = m->inv_temp;
     const double Rd = (double)R;
     if ((rc = timed(m, I6G_K_HEAD, s, 2.0 * Rd * m->V * d, Rd * d * 4.0 + (double)m->V * d * 2,
                     [&] { return launch_head(ha, s); })))

@@ -311,17 +311,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD <= 64 ? 
 #undef ATT_CHUNKS
 #undef ATT_QK
 
+  // Output rows: a lane holds dims db*16 + 4*lg + i of query q; the four
+  // lane groups (lanes lr, lr^16, lr^32, lr^48) together hold the row.
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float inv = 1.0f / osum[qb][0];
     const int q = qbase + 16 * qb + lr;
     bf16* dst = a.o + ((int64_t)w * a.Lp + q) * (a.n_heads * HD) + head * HD;
+    float ov[DB][4];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[db][i] = o[qb][db][i] * inv;
+    if (a.xsa) {
+      // exclusive self attention ([363] XSA): remove the component along
+      // this position's value vector v (bf16, as the P.V product used it)
+      float vv[DB][4], dot = 0.0f, nn = 0.0f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          vv[db][i] = (float)Vg[(int64_t)(db * 16 + 4 * lg + i) * a.Lp + q];
+          dot += ov[db][i] * vv[db][i];
+          nn += vv[db][i] * vv[db][i];
+        }
+      dot += __shfl_xor(dot, 16);
+      dot += __shfl_xor(dot, 32);
+      nn += __shfl_xor(nn, 16);
+      nn += __shfl_xor(nn, 32);
+      const float coef = nn > 0.0f ? dot / nn : 0.0f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[db][i] -= coef * vv[db][i];
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       uint16_t y[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        y[i] = __builtin_bit_cast(uint16_t, (bf16)(o[qb][db][i] * inv));
+      for (int i = 0; i < 4; ++i) y[i] = __builtin_bit_cast(uint16_t, (bf16)ov[db][i]);
       *reinterpret_cast<uint2*>(dst + db * 16 + 4 * lg) =
           make_uint2((uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16));
     }

@@ -115,7 +115,9 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
       float sq = 0.f;
       for (int c = lane; c < a.d; c += 64) sq += xr[c] * xr[c];
       sq = wave_sum(sq);
-      const float rinv = 1.0f / sqrtf(sq / (float)a.d + a.eps);
+      // the evaluation temperature divides every logit, so it scales the
+      // normed row once instead
+      const float rinv = 1.0f / sqrtf(sq / (float)a.d + a.eps) * a.inv_temp;
       for (int c = lane; c < a.d; c += 64) zrow[c] = (_Float16)(xr[c] * rinv);
     } else {
       for (int c = lane; c < a.d; c += 64) zrow[c] = (_Float16)0.0f;
@@ -249,12 +251,19 @@ __global__ void reduce_final_kernel(ReduceArgs a) {
 
 // ---------------------------------------------------------------------------
 // RoPE table: (cos, sin) of p * base^(-2i/hd), evaluated in fp64.
-__global__ void rope_table_kernel(float2* tab, int Lmax, int hd, double base) {
+// (cos, sin) of rotation pair i at position p, [Lmax, hd/2]: pairs
+// i < R/2 turn by p * base^(-2i/R) (R = rotated dims per head); the other
+// pairs hold the identity (1, 0) (partial RoPE, [363] Partial RoPE 16/64).
+__global__ void rope_table_kernel(float2* tab, int Lmax, int hd, int R, double base) {
   const int half = hd / 2;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)Lmax * half) return;
   const int p = (int)(idx / half), i = (int)(idx % half);
-  const double theta = pow(base, -2.0 * (double)i / (double)hd);
+  if (i >= R / 2) {
+    tab[idx] = make_float2(1.0f, 0.0f);
+    return;
+  }
+  const double theta = pow(base, -2.0 * (double)i / (double)R);
   const double ang = (double)p * theta;
   tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
 }
@@ -321,9 +330,10 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_rope_table(float2* tab, int32_t Lmax, int32_t hd, double base, hipStream_t s) {
+hipError_t launch_rope_table(float2* tab, int32_t Lmax, int32_t hd, int32_t rope_dims, double base,
+                             hipStream_t s) {
   int64_t n = (int64_t)Lmax * (hd / 2);
-  hipLaunchKernelGGL(rope_table_kernel, dim3(nblk(n, 256)), dim3(256), 0, s, tab, Lmax, hd, base);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(nblk(n, 256)), dim3(256), 0, s, tab, Lmax, hd, rope_dims, base);
   return hipGetLastError();
 }
 

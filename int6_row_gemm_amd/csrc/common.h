@@ -49,13 +49,15 @@ struct GemmArgs {
   // EPI_QKV
   bf16* q; bf16* k; bf16* vt;
   int32_t n_heads, n_kv, hd, Lp;
-  const float2* rope;     // [Lp, hd/2] (cos, sin)
+  const float2* rope;     // [Lp, hd/2] (cos, sin) of rotation pair p
+  int32_t rope_dims;      // rotated dims per head (pairs (i, i + rope_dims/2))
   const float* lora_u;    // [M, 2r] or null
   const float* lora_bq;   // [d, r]
   const float* lora_bv;   // [Hkv*hd, r]
   int32_t lora_r;
-  // EPI_RELU2
+  // EPI_RELU2: h = leaky_relu(acc, leaky)^2 (leaky 0 = ReLU^2)
   bf16* h;                // [M, N]
+  float leaky;
   // EPI_RES
   float* x;               // [M, N] residual, updated in place
   bf16* xb;               // [M, N] bf16 copy of the new x (or null)
@@ -90,6 +92,9 @@ struct AttnArgs {
   bf16* o;         // [W*Lp, Hq*hd]
   int32_t W, n_heads, n_kv, hd, Lp;
   float scale_log2;  // log2(e) / sqrt(hd)
+  // exclusive self attention: remove from each output row its component
+  // along the same position's value vector
+  int32_t xsa;
   // final layer: only query tiles holding scored positions are computed
   int32_t prune;
   int64_t k0, P;
@@ -132,6 +137,7 @@ struct HeadArgs {
   int64_t k0, K, e0;     // first window, window count, end of window 0
   int32_t L, S, Lp, d, vocab;
   float eps;
+  float inv_temp;        // logits are multiplied by 1 / temperature
   int32_t* flags;
   int32_t compact;       // 1: row of prediction p is p - p0 (pruned last layer)
 };
@@ -146,7 +152,8 @@ struct ReduceArgs {
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 
 // Constant tables built at load time on the device.
-hipError_t launch_rope_table(float2* tab, int32_t Lmax, int32_t hd, double base, hipStream_t s);
+hipError_t launch_rope_table(float2* tab, int32_t Lmax, int32_t hd, int32_t rope_dims, double base,
+                             hipStream_t s);
 hipError_t launch_bigram_table(const uint16_t* table, const uint16_t* proj, float* out,
                                int32_t buckets, int32_t dim, int32_t d, hipStream_t s);
 hipError_t launch_f16_to_f32(const uint16_t* in, float* out, int64_t n, hipStream_t s);

@@ -53,6 +53,9 @@ __device__ inline uint32_t pack_bf16x2_from_int(int lo, int hi) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+// leaky_relu(v, slope); slope 0 gives relu (its square is ReLU^2)
+__device__ inline float lrelu(float v, float slope) { return v >= 0.0f ? v : slope * v; }
+
 __device__ inline uint16_t f2bf_bits(float f) {
   return __builtin_bit_cast(uint16_t, (bf16)f);
 }
@@ -85,17 +88,34 @@ __device__ inline int pair_phys(int u) {
   return 16 * (2 * (u >> 5) + ((u >> 2) & 1)) + 4 * ((u >> 3) & 3) + (u & 3);
 }
 
+// Rotation pairs of one q or k head with R rotated dims (partial RoPE):
+// pair p < R/2 is (p, p + R/2); the others pair up the unrotated dims as
+// (R + w, R + (hd - R)/2 + w), w = p - R/2, and turn by the identity.  For
+// R = hd these are the pairs (p, p + hd/2) of full RoPE.
+template <int HD>
+__device__ inline int pair_first(int p, int R) { return p < R / 2 ? p : R + (p - R / 2); }
+template <int HD>
+__device__ inline int pair_second(int p, int R) {
+  return p < R / 2 ? p + R / 2 : R + (HD - R) / 2 + (p - R / 2);
+}
+
 // Placement of the rows of one q or k head (HD rows) for the rotary
 // epilogue: the output rows 4g + e of fragment j (lane group g) are the
-// values t = 4j + e of that lane, and value t < HD/8 is rotation index
-// g * HD/8 + t while value t + HD/8 is its partner HD/2 further on, so a
-// lane holds whole rotation pairs.
+// values t = 4j + e of that lane, and value t < HD/8 is the first dim of
+// pair g * HD/8 + t while value t + HD/8 is its second, so a lane holds
+// whole rotation pairs, and (R a multiple of HD/4) its first and its second
+// dims are two runs of HD/8 consecutive dims.
 template <int HD>
-__device__ inline int rope_phys(int u) {
-  constexpr int HALF = HD / 2, Q8 = HD / 8;
-  const int g = (u < HALF ? u : u - HALF) / Q8;
-  const int t = (u < HALF ? 0 : Q8) + (u < HALF ? u : u - HALF) % Q8;
-  return 16 * (t >> 2) + 4 * g + (t & 3);
+__device__ inline int rope_phys(int u, int R) {
+  constexpr int Q8 = HD / 8;
+  const int h2 = R / 2, rest2 = (HD - R) / 2;
+  int p, second;
+  if (u < h2) { p = u; second = 0; }
+  else if (u < R) { p = u - h2; second = 1; }
+  else if (u < R + rest2) { p = h2 + (u - R); second = 0; }
+  else { p = h2 + (u - R - rest2); second = 1; }
+  const int t = p % Q8 + second * Q8;
+  return 16 * (t >> 2) + 4 * (p / Q8) + (t & 3);
 }
 
 template <int BM, int BN>
@@ -165,7 +185,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
     const int r = c >> 2, j2 = (c & 3) * 2;                                           \
     int pr;                                                                           \
     if constexpr (EPI == EPI_QKV) {                                                   \
-      pr = CT ? (r / WN) * WN + rope_phys<WN>(r % WN) : r;                            \
+      pr = CT ? (r / WN) * WN + rope_phys<WN>(r % WN, a.rope_dims) : r;               \
     } else {                                                                          \
       pr = (r & ~63) | pair_phys(r & 63);                                             \
     }                                                                                 \
@@ -319,8 +339,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
         for (int h = 0; h < 2; ++h) {
           const float4 s4 = reinterpret_cast<const float4*>(scale_s + cl)[h];
           const f32x4 c = acc[i][2 * p + h];
-          const float v0 = fmaxf(c[0] * s4.x * ri, 0.0f), v1 = fmaxf(c[1] * s4.y * ri, 0.0f);
-          const float v2 = fmaxf(c[2] * s4.z * ri, 0.0f), v3 = fmaxf(c[3] * s4.w * ri, 0.0f);
+          const float v0 = lrelu(c[0] * s4.x * ri, a.leaky), v1 = lrelu(c[1] * s4.y * ri, a.leaky);
+          const float v2 = lrelu(c[2] * s4.z * ri, a.leaky), v3 = lrelu(c[3] * s4.w * ri, a.leaky);
           o[2 * h] = (uint32_t)f2bf_bits(v0 * v0) | ((uint32_t)f2bf_bits(v1 * v1) << 16);
           o[2 * h + 1] = (uint32_t)f2bf_bits(v2 * v2) | ((uint32_t)f2bf_bits(v3 * v3) << 16);
         }
@@ -449,19 +469,20 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
     constexpr int HD = WN, HALF = HD / 2, Q8 = HD / 8;
     const int colbase = n0 + wn * HD;
     if constexpr (CT) {
-      // q or k head, C^T: lane holds rotation indices c1 = lg*Q8 + t and
-      // their partners c1 + HALF, t < Q8
+      // q or k head, C^T: lane holds rotation pairs c1b + t, t < Q8, whose
+      // first dims are f0 + t and second dims s0 + t
       const bool is_q = colbase < dq;
       const int head = (is_q ? colbase : colbase - dq) / HD;
       const int nh = is_q ? a.n_heads : a.n_kv;
       bf16* const base = is_q ? a.q : a.k;
       const bool lora = is_q && a.lora_u;
       const int c1b = lg * Q8;
+      const int f0 = pair_first<HD>(c1b, a.rope_dims), s0 = pair_second<HD>(c1b, a.rope_dims);
       float sc1[Q8], sc2[Q8];
 #pragma unroll
       for (int t = 0; t < Q8; ++t) {
-        sc1[t] = scale_s[wn * HD + c1b + t];
-        sc2[t] = scale_s[wn * HD + HALF + c1b + t];
+        sc1[t] = scale_s[wn * HD + f0 + t];
+        sc2[t] = scale_s[wn * HD + s0 + t];
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -481,7 +502,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
           const float* uu = a.lora_u + (int64_t)m * 2 * a.lora_r;
 #pragma unroll
           for (int t = 0; t < Q8; ++t) {
-            const int g1 = colbase + c1b + t, g2 = g1 + HALF;
+            const int g1 = colbase + f0 + t, g2 = colbase + s0 + t;
             float s1 = 0.f, s2 = 0.f;
             for (int r = 0; r < a.lora_r; ++r) {
               s1 += uu[r] * a.lora_bq[g1 * a.lora_r + r];
@@ -501,8 +522,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
           y2[t + 1] = f2bf_bits(x1[t + 1] * cs.w + x2[t + 1] * cs.z);
         }
         bf16* dst = base + (((int64_t)w * nh + head) * a.Lp + pos) * HD;
-        store_bf16_run<Q8>(dst + c1b, y1);
-        store_bf16_run<Q8>(dst + HALF + c1b, y2);
+        store_bf16_run<Q8>(dst + f0, y1);
+        store_bf16_run<Q8>(dst + s0, y2);
       }
     } else {
       // v head, C orientation, written transposed: the lane's 16 rows are

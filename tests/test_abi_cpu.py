@@ -94,6 +94,19 @@ def test_load_model_rejects_bad_descriptors():
     assert L.i6g_load_model(ctypes.byref(d), None, ctypes.byref(out)) == -6
     assert "kv heads" in L.i6g_last_error().decode()
     d.d_model, d.n_heads, d.n_kv_heads, d.head_dim = 512, 8, 4, 64
+    # evaluation variants: partial RoPE granularity, XSA depth, temperature
+    d.rope_dims = 24                     # not a multiple of head_dim / 4
+    assert L.i6g_load_model(ctypes.byref(d), None, ctypes.byref(out)) == -6
+    d.rope_dims = 80                     # more than head_dim
+    assert L.i6g_load_model(ctypes.byref(d), None, ctypes.byref(out)) == -1
+    d.rope_dims = 0
+    d.xsa_last_n = 2                     # more than n_eff = 1
+    assert L.i6g_load_model(ctypes.byref(d), None, ctypes.byref(out)) == -1
+    d.xsa_last_n = 0
+    d.logit_temperature = -0.5
+    assert L.i6g_load_model(ctypes.byref(d), None, ctypes.byref(out)) == -1
+    assert "temperature" in L.i6g_last_error().decode()
+    d.logit_temperature = 0.0
     bad = (ctypes.c_int32 * 1)(3)      # schedule names a block that does not exist
     d.schedule = ctypes.cast(bad, ctypes.c_void_p)
     assert L.i6g_load_model(ctypes.byref(d), None, ctypes.byref(out)) == -1

@@ -47,6 +47,19 @@ SMALL = [
     ("largevocab", {}, 200, 50, 700),
     ("11l", {}, 2048, 64, 100),          # stream shorter than one window
     ("11l", {"schedule": [0, 1, 2], "n_skip": 1}, 64, 16, 300),
+    # evaluation variants: all together on the cyclic 11-layer model, at
+    # stride 64 and 16, on every head size (32: tiny, 80: midcycle), one by
+    # one at head size 64, and LeakyReLU^2 on the parallel-lane model
+    ("11l_next", {}, 256, 64, 1000),
+    ("11l_next", {}, 256, 16, 400),
+    ("tiny", {"rope_dims": 8, "xsa_last_n": 2, "leaky_slope": 0.5, "temperature": 0.7}, 256, 64, 700),
+    ("midcycle", {"rope_dims": 40, "xsa_last_n": 3, "leaky_slope": 0.25, "temperature": 1.3}, 128, 128, 257),
+    ("baseline", {"temperature": 0.5}, 128, 128, 400),
+    ("baseline", {"leaky_slope": 0.5}, 128, 128, 400),
+    ("baseline", {"rope_dims": 16}, 128, 128, 400),
+    ("baseline", {"rope_dims": 48}, 128, 128, 400),
+    ("baseline", {"xsa_last_n": 9}, 128, 128, 400),
+    ("largevocab", {"leaky_slope": 0.5}, 200, 50, 700),
 ]
 
 
@@ -121,6 +134,7 @@ FULL = [
     ("baseline", [0, 37, 63]),
     ("midcycle", [0, 31]),
     ("11l", [0, 8191, 16352]),
+    ("11l_next", [0, 8191, 16352]),
     ("largevocab", [0, 40000, 65504]),
 ]
 
@@ -146,7 +160,8 @@ def test_full_size_sampled(name, sample):
 
 
 @pytest.mark.parametrize("name,L,S,N", [("11l", 256, 64, 1000), ("largevocab", 200, 50, 700),
-                                        ("midcycle", 256, 32, 600), ("tiny", 256, 64, 700)])
+                                        ("midcycle", 256, 32, 600), ("tiny", 256, 64, 700),
+                                        ("11l_next", 256, 64, 1000)])
 def test_final_layer_pruning_is_exact(name, L, S, N):
     """Computing queries, output projection and MLP of the final layer only
     for scored rows must give the same bits as computing every row."""
