@@ -1,7 +1,8 @@
 """Throughput of the int6 per-row scoring pass on one MI355X.
 
 One step = the whole hot path over the 11-layer, d=512 int6 workload:
-row-quantise all 66 block matrices (fp32 weights already in HBM), then score
+row-quantise all 66 block matrices (fp32 weights already in HBM, one
+i6g_quantize_rows_many call), then score
 the 1,048,576-token synthetic stream with sliding windows of 2048 / stride 64
 (16,353 windows, 1,048,575 scored predictions) down to bits per byte.
 Inputs are resident in HBM before the timed region starts.
@@ -93,15 +94,19 @@ def main():
     lib = g.lib()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
+    # every block matrix of the model in one i6g_quantize_rows_many call
+    # (one launch per 64 matrices)
+    jobs = (g._QuantJob * sum(len(wb) for wb in w_dev))()
+    for i, (wb, cb, sb, k) in enumerate((wb, cb, sb, k) for wb, cb, sb in zip(w_dev, codes, scales)
+                                        for k in wb):
+        w = wb[k]
+        jobs[i] = g._QuantJob(w.data_ptr(), cb[k].data_ptr(), sb[k].data_ptr(), w.shape[0], w.shape[1])
+
     def quantize_all():
-        for wb, cb, sb in zip(w_dev, codes, scales):
-            for k, w in wb.items():
-                rc = lib.i6g_quantize_rows(ctypes.c_void_p(w.data_ptr()), w.shape[0], w.shape[1],
-                                           arch["bits"], float(arch["clip_q"]),
-                                           ctypes.c_void_p(cb[k].data_ptr()),
-                                           ctypes.c_void_p(sb[k].data_ptr()), None, stream)
-                if rc != 0:
-                    raise g.I6GError(rc, lib.i6g_last_error().decode())
+        rc = lib.i6g_quantize_rows_many(ctypes.cast(jobs, ctypes.c_void_p), len(jobs), arch["bits"],
+                                        float(arch["clip_q"]), None, stream)
+        if rc != 0:
+            raise g.I6GError(rc, lib.i6g_last_error().decode())
 
     quantize_all()
     torch.cuda.synchronize()

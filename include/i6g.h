@@ -90,6 +90,27 @@ int i6g_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int bits,
                       double clip_quantile, int8_t* codes_dev, uint16_t* scales_dev,
                       int32_t* flags_dev, void* stream);
 
+/* One matrix of an i6g_quantize_rows_many call (device pointers). */
+typedef struct {
+  const float* w;     /* [rows, cols] fp32 */
+  int8_t* codes;      /* [rows, cols] int8 output */
+  uint16_t* scales;   /* [rows] binary16 output */
+  int64_t rows, cols;
+} i6g_quant_job;
+
+/*
+ * i6g_quantize_rows_many -- i6g_quantize_rows (same steps, same results) on
+ * n_jobs matrices at once, every row of up to 64 matrices a wavefront of one
+ * launch, so that a model's many small matrices fill the device (the export
+ * step of [11L] 后训练量化导出 quantises every block matrix this way).
+ * jobs is a host array of n_jobs entries; bits, clip_quantile and flags_dev
+ * apply to all of them.  Errors: I6G_EINVAL for n_jobs < 1 or a NULL jobs
+ * array, otherwise as i6g_quantize_rows for each job (checked before any
+ * work is enqueued).
+ */
+int i6g_quantize_rows_many(const i6g_quant_job* jobs, int32_t n_jobs, int bits, double clip_quantile,
+                           int32_t* flags_dev, void* stream);
+
 /* One quantised [out, in] matrix: codes (int8) and per-row binary16 scales. */
 typedef struct {
   const int8_t* codes;

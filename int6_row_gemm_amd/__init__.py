@@ -22,7 +22,7 @@ SKIP_KINDS = {"none": 0, "unet": 1, "stem_tail": 2}
 KERNEL_CLASSES = ["embed", "qkv", "attn", "oproj", "fc", "proj", "head", "reduce", "lora"]
 
 EXPORTED = [
-    "i6g_quantize_rows", "i6g_load_model", "i6g_score_tokens", "i6g_model_status",
+    "i6g_quantize_rows", "i6g_quantize_rows_many", "i6g_load_model", "i6g_score_tokens", "i6g_model_status",
     "i6g_free_model", "i6g_last_error", "i6g_plan_windows", "i6g_set_option",
     "i6g_set_timing", "i6g_get_timing",
 ]
@@ -40,6 +40,11 @@ class _Matrix(ctypes.Structure):
 
 class _Block(ctypes.Structure):
     _fields_ = [(n, _Matrix) for n in ("q", "k", "v", "o", "fc", "proj")]
+
+
+class _QuantJob(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
 
 
 class _Desc(ctypes.Structure):
@@ -74,6 +79,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
         L.i6g_quantize_rows.argtypes = [vp, i64, i64, ctypes.c_int, dbl, vp, vp, vp, vp]
+        L.i6g_quantize_rows_many.argtypes = [vp, i32, ctypes.c_int, dbl, vp, vp]
         L.i6g_load_model.argtypes = [vp, vp, ctypes.POINTER(vp)]
         L.i6g_score_tokens.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, vp]
         L.i6g_model_status.argtypes = [vp, vp]
@@ -127,6 +133,22 @@ def quantize_rows(w, bits, clip_quantile, flags=None):
     _check(lib().i6g_quantize_rows(_ptr(w), rows, cols, bits, float(clip_quantile),
                                    _ptr(codes), _ptr(scales), _ptr(flags), _stream()))
     return codes, scales
+
+
+def quantize_rows_many(jobs, bits, clip_quantile, flags=None):
+    """Row-quantise several device fp32 matrices with one launch per 64.
+    ``jobs`` is a list of (w, codes, scales) CUDA tensors (outputs written in
+    place: codes int8 [rows, cols], scales int16 [rows] of binary16 bits)."""
+    import torch
+    arr = (_QuantJob * len(jobs))()
+    for i, (w, codes, scales) in enumerate(jobs):
+        if not (w.is_cuda and w.dtype == torch.float32 and w.dim() == 2 and w.is_contiguous()):
+            raise ValueError("each w must be a contiguous 2-D float32 CUDA tensor")
+        if codes.shape != w.shape or codes.dtype != torch.int8 or scales.shape != (w.shape[0],):
+            raise ValueError("codes must be int8 like w and scales [rows]")
+        arr[i] = _QuantJob(w.data_ptr(), codes.data_ptr(), scales.data_ptr(), w.shape[0], w.shape[1])
+    _check(lib().i6g_quantize_rows_many(ctypes.cast(arr, ctypes.c_void_p), len(jobs), bits,
+                                        float(clip_quantile), _ptr(flags), _stream()))
 
 
 def _dev(x, dtype=None):

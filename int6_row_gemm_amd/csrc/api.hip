@@ -249,20 +249,35 @@ int i6g_plan_windows(int64_t n_tokens, int32_t window, int32_t stride, int64_t* 
   return I6G_OK;
 }
 
-int i6g_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int bits, double clip_quantile,
-                      int8_t* codes_dev, uint16_t* scales_dev, int32_t* flags_dev, void* stream) {
-  if (!w_dev || !codes_dev || !scales_dev) return fail(I6G_EINVAL, "quantize_rows: NULL array");
-  if (rows < 1 || cols < 1) return fail(I6G_EINVAL, "quantize_rows: rows and cols must be >= 1");
-  if (bits != 6 && bits != 8) return fail(I6G_EINVAL, "quantize_rows: bits must be 6 or 8");
+// Validation and the host-side quantile split shared by both quantiser
+// entry points: pos = q * (cols - 1) in binary64, lo = floor(pos), the
+// kernel keeps the cols - lo largest |w| and interpolates with f = pos - lo.
+static int quant_plan(const char* who, const void* w, const void* codes, const void* scales,
+                      int64_t rows, int64_t cols, int bits, double clip_quantile, int32_t* topk,
+                      float* frac) {
+  if (!w || !codes || !scales) return fail(I6G_EINVAL, "%s: NULL array", who);
+  if (rows < 1 || cols < 1) return fail(I6G_EINVAL, "%s: rows and cols must be >= 1", who);
+  if (bits != 6 && bits != 8) return fail(I6G_EINVAL, "%s: bits must be 6 or 8", who);
   if (!(clip_quantile > 0.0 && clip_quantile <= 1.0))
-    return fail(I6G_EINVAL, "quantize_rows: clip_quantile must be in (0, 1]");
-  if (cols > 65536) return fail(I6G_EUNSUPPORTED, "quantize_rows: cols > 65536");
+    return fail(I6G_EINVAL, "%s: clip_quantile must be in (0, 1]", who);
+  if (cols > 65536) return fail(I6G_EUNSUPPORTED, "%s: cols > 65536", who);
   const double pos = clip_quantile * (double)(cols - 1);
   const int64_t lo = (int64_t)floor(pos);
-  const int64_t topk = cols - lo;
-  if (topk > 8)
-    return fail(I6G_EUNSUPPORTED, "quantize_rows: quantile needs the %lld largest values (max 8)",
-                (long long)topk);
+  if (cols - lo > 8)
+    return fail(I6G_EUNSUPPORTED, "%s: quantile needs the %lld largest values (max 8)", who,
+                (long long)(cols - lo));
+  *topk = (int32_t)(cols - lo);
+  *frac = (float)(pos - (double)lo);
+  return I6G_OK;
+}
+
+int i6g_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int bits, double clip_quantile,
+                      int8_t* codes_dev, uint16_t* scales_dev, int32_t* flags_dev, void* stream) {
+  int32_t topk = 0;
+  float frac = 0.0f;
+  int rc = quant_plan("quantize_rows", w_dev, codes_dev, scales_dev, rows, cols, bits, clip_quantile,
+                      &topk, &frac);
+  if (rc) return rc;
   QuantArgs a{};
   a.w = w_dev;
   a.codes = codes_dev;
@@ -271,9 +286,38 @@ int i6g_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int bits, 
   a.rows = rows;
   a.cols = (int32_t)cols;
   a.bits = bits;
-  a.topk = (int32_t)topk;
-  a.frac = (float)(pos - (double)lo);
+  a.topk = topk;
+  a.frac = frac;
   HIP_TRY(launch_quantize(a, (hipStream_t)stream));
+  return I6G_OK;
+}
+
+int i6g_quantize_rows_many(const i6g_quant_job* jobs, int32_t n_jobs, int bits, double clip_quantile,
+                           int32_t* flags_dev, void* stream) {
+  if (!jobs || n_jobs < 1) return fail(I6G_EINVAL, "quantize_rows_many: need n_jobs >= 1 jobs");
+  std::vector<QuantJob> plan(n_jobs);
+  for (int j = 0; j < n_jobs; ++j) {
+    const i6g_quant_job& J = jobs[j];
+    char who[64];
+    snprintf(who, sizeof who, "quantize_rows_many job %d", j);
+    int rc = quant_plan(who, J.w, J.codes, J.scales, J.rows, J.cols, bits, clip_quantile, &plan[j].topk,
+                        &plan[j].frac);
+    if (rc) return rc;
+    plan[j].w = J.w; plan[j].codes = J.codes; plan[j].scales = J.scales;
+    plan[j].cols = (int32_t)J.cols;
+  }
+  for (int j0 = 0; j0 < n_jobs; j0 += kQuantJobs) {
+    QuantManyArgs a{};
+    a.n = std::min(kQuantJobs, n_jobs - j0);
+    a.bits = bits;
+    a.flags = flags_dev;
+    a.row0[0] = 0;
+    for (int j = 0; j < a.n; ++j) {
+      a.job[j] = plan[j0 + j];
+      a.row0[j + 1] = a.row0[j] + jobs[j0 + j].rows;
+    }
+    HIP_TRY(launch_quantize_many(a, (hipStream_t)stream));
+  }
   return I6G_OK;
 }
 

@@ -31,6 +31,25 @@ struct QuantArgs {
 };
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 
+// Several matrices in one launch: row r of the concatenated rows belongs to
+// the last job j with row0[j] <= r.
+constexpr int kQuantJobs = 64;
+struct QuantJob {
+  const float* w;
+  int8_t* codes;
+  uint16_t* scales;
+  int32_t cols, topk;
+  float frac;
+};
+struct QuantManyArgs {
+  int32_t n, bits;
+  int32_t* flags;
+  int64_t row0[kQuantJobs + 1];
+  QuantJob job[kQuantJobs];
+};
+static_assert(sizeof(QuantManyArgs) <= 4096, "kernel arguments are limited to 4 KB");
+hipError_t launch_quantize_many(const QuantManyArgs& a, hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // Dequant-fused GEMM: C[m, n] = sum_k A[m, k] * code[n, k], A bf16 [M, K],
 // codes int8 [N, K]; the per-row scale of B (and, for normed inputs, the

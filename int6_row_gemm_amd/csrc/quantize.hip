@@ -17,12 +17,13 @@
 namespace i6g {
 namespace {
 
-constexpr int kTop = 8;  // largest |w| kept per lane and per row
+constexpr int kTop = 8;  // most largest |w| a row's quantile may need
 
-__device__ inline void insert_top(float (&t)[kTop], float a) {
+template <int KT>
+__device__ inline void insert_top(float (&t)[KT], float a) {
   // t is sorted descending; insert a and drop the smallest.
 #pragma unroll
-  for (int i = 0; i < kTop; ++i) {
+  for (int i = 0; i < KT; ++i) {
     float hi = fmaxf(t[i], a);
     float lo = fminf(t[i], a);
     t[i] = hi;
@@ -30,27 +31,40 @@ __device__ inline void insert_top(float (&t)[kTop], float a) {
   }
 }
 
-__global__ __launch_bounds__(256) void quantize_rows_kernel(QuantArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
-  if (row >= a.rows) return;
-  const float* w = a.w + row * a.cols;
-
-  float top[kTop];
+// One row of `cols` fp32 weights -> codes and a binary16 scale, on one
+// wavefront (every lane must call it).  Each lane keeps its KT >= topk
+// largest |w|; the quantile of every row length these models use needs the
+// top two (q < 1) or one (q = 1), so KT = 2 covers them with a quarter of
+// the compare work of the general KT = 8.
+template <int KT>
+__device__ void quantize_row_k(const float* w, int cols, int topk, float frac, int bits, int8_t* codes,
+                               uint16_t* scale_out, int32_t* flags, int lane) {
+  // The row is read in chunks of kU elements per lane whose loads are all
+  // issued before any is used, so their latencies overlap.
+  constexpr int kU = 8;
+  float top[KT];
 #pragma unroll
-  for (int i = 0; i < kTop; ++i) top[i] = -1.0f;
+  for (int i = 0; i < KT; ++i) top[i] = -1.0f;
   int bad = 0;
-  for (int c = lane; c < a.cols; c += kWave) {
-    float v = w[c];
-    bad |= !isfinite(v);
-    insert_top(top, fabsf(v));
+  for (int c0 = 0; c0 < cols; c0 += kU * kWave) {
+    float v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = c0 + u * kWave + lane;
+      v[u] = c < cols ? w[c] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      bad |= !isfinite(v[u]);
+      insert_top<KT>(top, fabsf(v[u]));   // a 0 past the row end never displaces a |w|
+    }
   }
   bad = __any(bad);
   if (bad) {
-    for (int c = lane; c < a.cols; c += kWave) a.codes[row * a.cols + c] = 0;
+    for (int c = lane; c < cols; c += kWave) codes[c] = 0;
     if (lane == 0) {
-      a.scales[row] = 0x7e00;
-      if (a.flags) atomicOr(a.flags, 1);
+      *scale_out = 0x7e00;
+      if (flags) atomicOr(flags, 1);
     }
     return;
   }
@@ -58,7 +72,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantArgs a) {
   // Extract the topk largest values of the row in descending order; the
   // last two extracted are s[lo] and s[lo + 1].
   float s_lo = 0.0f, s_prev = 0.0f;
-  for (int r = 0; r < a.topk; ++r) {
+  for (int r = 0; r < topk; ++r) {
     float best = top[0];
     int who = lane;
 #pragma unroll
@@ -69,38 +83,77 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantArgs a) {
     }
     if (lane == who) {
 #pragma unroll
-      for (int i = 0; i < kTop - 1; ++i) top[i] = top[i + 1];
-      top[kTop - 1] = -1.0f;
+      for (int i = 0; i < KT - 1; ++i) top[i] = top[i + 1];
+      top[KT - 1] = -1.0f;
     }
     s_prev = s_lo;
     s_lo = best;
   }
-  const float s_hi = (a.topk >= 2) ? s_prev : s_lo;
+  const float s_hi = (topk >= 2) ? s_prev : s_lo;
 
   float diff = s_hi - s_lo;
-  float step = a.frac * diff;
+  float step = frac * diff;
   float c = s_lo + step;
   c = fmaxf(c, 1e-12f);
   const float scale = c / 127.0f;
 
-  for (int col = lane; col < a.cols; col += kWave) {
-    float v = w[col];
-    v = fminf(fmaxf(v, -c), c);
-    float r = v / scale;
-    float k = rintf(r);
-    float code;
-    if (a.bits == 8) {
-      code = fminf(fmaxf(k, -127.0f), 127.0f);
-    } else {
-      float k4 = rintf(k * 0.25f);
-      code = fminf(fmaxf(k4 * 4.0f, -128.0f), 124.0f);
+  for (int c0 = 0; c0 < cols; c0 += kU * kWave) {
+    float wv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int col = c0 + u * kWave + lane;
+      wv[u] = col < cols ? w[col] : 0.0f;
     }
-    a.codes[row * a.cols + col] = (int8_t)(int)code;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int col = c0 + u * kWave + lane;
+      float v = fminf(fmaxf(wv[u], -c), c);
+      float r = v / scale;
+      float k = rintf(r);
+      float code;
+      if (bits == 8) {
+        code = fminf(fmaxf(k, -127.0f), 127.0f);
+      } else {
+        float k4 = rintf(k * 0.25f);
+        code = fminf(fmaxf(k4 * 4.0f, -128.0f), 124.0f);
+      }
+      if (col < cols) codes[col] = (int8_t)(int)code;
+    }
   }
   if (lane == 0) {
     _Float16 h = (_Float16)scale;   // v_cvt_f16_f32: round to nearest even
-    a.scales[row] = __builtin_bit_cast(uint16_t, h);
+    *scale_out = __builtin_bit_cast(uint16_t, h);
   }
+}
+
+__device__ inline void quantize_row(const float* w, int cols, int topk, float frac, int bits,
+                                    int8_t* codes, uint16_t* scale_out, int32_t* flags, int lane) {
+  if (topk <= 2)
+    quantize_row_k<2>(w, cols, topk, frac, bits, codes, scale_out, flags, lane);
+  else
+    quantize_row_k<kTop>(w, cols, topk, frac, bits, codes, scale_out, flags, lane);
+}
+
+__global__ __launch_bounds__(256) void quantize_rows_kernel(QuantArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (row >= a.rows) return;
+  quantize_row(a.w + row * a.cols, a.cols, a.topk, a.frac, a.bits, a.codes + row * a.cols,
+               a.scales + row, a.flags, lane);
+}
+
+// Rows of several matrices in one grid; the job of a row is found by a
+// scan of the (at most 64) row offsets, which are in the kernel arguments.
+__global__ __launch_bounds__(256) void quantize_many_kernel(QuantManyArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (row >= a.row0[a.n]) return;
+  int j = 0;
+  while (j + 1 < a.n && a.row0[j + 1] <= row) ++j;
+  const QuantJob& q = a.job[j];
+  const int64_t r = row - a.row0[j];
+  quantize_row(q.w + r * q.cols, q.cols, q.topk, q.frac, a.bits, q.codes + r * q.cols, q.scales + r,
+               a.flags, lane);
 }
 
 }  // namespace
@@ -109,6 +162,13 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   const int rows_per_block = 4;
   int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
   hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_many(const QuantManyArgs& a, hipStream_t s) {
+  const int rows_per_block = 4;
+  int64_t blocks = (a.row0[a.n] + rows_per_block - 1) / rows_per_block;
+  hipLaunchKernelGGL(quantize_many_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

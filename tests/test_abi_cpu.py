@@ -119,3 +119,17 @@ def test_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(g, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         g.lib()
+
+
+def test_quantize_rows_many_validates_before_enqueueing():
+    g, L = _lib()
+    assert L.i6g_quantize_rows_many(None, 1, 6, 0.9999984, None, None) == -1
+    jobs = (g._QuantJob * 2)()
+    assert L.i6g_quantize_rows_many(ctypes.cast(jobs, ctypes.c_void_p), 0, 6, 0.9999984, None, None) == -1
+    # job 1 has NULL arrays
+    jobs[0] = g._QuantJob(0x1000, 0x2000, 0x3000, 4, 512)
+    assert L.i6g_quantize_rows_many(ctypes.cast(jobs, ctypes.c_void_p), 2, 6, 0.9999984, None, None) == -1
+    assert "job 1" in L.i6g_last_error().decode()
+    jobs[1] = g._QuantJob(0x1000, 0x2000, 0x3000, 4, 512)
+    assert L.i6g_quantize_rows_many(ctypes.cast(jobs, ctypes.c_void_p), 2, 7, 0.9999984, None, None) == -1
+    assert L.i6g_quantize_rows_many(ctypes.cast(jobs, ctypes.c_void_p), 2, 6, 0.5, None, None) == -6

@@ -73,3 +73,31 @@ def test_nonfinite_row_flagged():
     assert s[2] == 0x7E00 and np.all(codes.cpu().numpy()[2] == 0)
     rc, rs = oq.quantize_rows(w[[0, 1, 3]], 6, 1.0)
     assert np.array_equal(codes.cpu().numpy()[[0, 1, 3]], rc)
+
+
+def test_many_matrices_in_one_call_bit_exact():
+    """i6g_quantize_rows_many on more than 64 matrices (two launches) of
+    ragged shapes gives the single-matrix results and the oracle's."""
+    import torch
+    g = need_gpu()
+    rng = np.random.default_rng(11)
+    shapes = [(int(rng.integers(1, 40)), int(c)) for c in rng.choice([7, 48, 64, 100, 512, 1536, 2048], 70)]
+    ws = [torch.from_numpy((rng.standard_normal(s) * 0.02).astype(np.float32)).cuda() for s in shapes]
+    ws[5][0, 3] = float("nan")          # one non-finite row
+    for bits, q in [(6, 0.9999984), (8, 1.0)]:
+        print_case("quantize_rows_many", "bits", bits, "q", q, "jobs", len(ws))
+        jobs = [(w, torch.empty(w.shape, dtype=torch.int8, device="cuda"),
+                 torch.empty(w.shape[0], dtype=torch.int16, device="cuda")) for w in ws]
+        flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+        g.quantize_rows_many(jobs, bits, q, flags=flags)
+        torch.cuda.synchronize()
+        assert int(flags.item()) & 1
+        for w, codes, scales in jobs:
+            c1, s1 = g.quantize_rows(w, bits, q)
+            torch.cuda.synchronize()
+            assert torch.equal(codes, c1) and torch.equal(scales, s1)
+            wn = w.cpu().numpy()
+            if np.all(np.isfinite(wn)):
+                rc, rs = oq.quantize_rows(wn, bits, q)
+                np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+                np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint16), rs.view(np.uint16))
