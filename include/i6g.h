@@ -50,10 +50,10 @@ typedef enum {
 
 /* Bits of the device flag word written by kernels (see i6g_quantize_rows and
  * i6g_model_status). */
-enum { I6G_FLAG_NONFINITE = 1, I6G_FLAG_TOKEN = 2, I6G_FLAG_BYTES = 4 };
+enum { I6G_FLAG_NONFINITE = 1, I6G_FLAG_TOKEN = 2, I6G_FLAG_BYTES = 4, I6G_FLAG_CODE = 8 };
 
 enum { I6G_SKIP_NONE = 0, I6G_SKIP_UNET = 1, I6G_SKIP_STEM_TAIL = 2 };
-enum { I6G_DTYPE_F16 = 0, I6G_DTYPE_F32 = 1 };
+enum { I6G_DTYPE_F16 = 0, I6G_DTYPE_F32 = 1, I6G_DTYPE_BF16 = 2 };
 
 /*
  * i6g_quantize_rows -- per-row int8 / int6 quantisation of an fp32 matrix.
@@ -279,6 +279,74 @@ int i6g_set_timing(i6g_model* m, int enable, uint32_t class_mask);
  * and bytes of those launches. */
 int i6g_get_timing(i6g_model* m, int kernel_class, double* total_ms, int64_t* launches,
                    double* flops, double* bytes);
+
+/*
+ * Export side.  [363] timeline and run notes: the int6 codes are sized by
+ * their entropy in bits per value, compressed (bit packing among the methods
+ * tried) into an artifact of at most 16,000,000 bytes, then dequantised and
+ * evaluated again.  [11L] 后训练量化导出: codes are int8 multiples of 4 in
+ * [-128, 124] with one binary16 scale per row.
+ *
+ * Packed int6 format: code c -> u = c/4 + 32 in [0, 63]; four codes u0..u3
+ * make the 24-bit word u0 | u1 << 6 | u2 << 12 | u3 << 18, stored as 3 bytes
+ * least significant first; n codes take 3 * ceil(n / 4) bytes, a tail of
+ * fewer than four codes padded with code 0.  Code buffers and fp32/bf16
+ * outputs must be 16-byte aligned and packed buffers 4-byte aligned
+ * (I6G_EUNSUPPORTED otherwise); n = 0 enqueues nothing.
+ */
+
+/* i6g_pack_int6 -- n int6 codes (int8) -> 3 * ceil(n / 4) packed bytes.  A
+ * byte that is not a multiple of 4 is packed as if its low two bits were
+ * clear and I6G_FLAG_CODE is OR-ed into *flags_dev (may be NULL).
+ * Errors: I6G_EINVAL for n < 0 or a NULL buffer with n > 0. */
+int i6g_pack_int6(const int8_t* codes_dev, int64_t n, uint8_t* packed_dev, int32_t* flags_dev,
+                  void* stream);
+
+/* i6g_unpack_int6 -- the inverse: the first n codes held in packed_dev
+ * (3 * ceil(n / 4) bytes) -> codes_dev [n] int8.  Errors as i6g_pack_int6. */
+int i6g_unpack_int6(const uint8_t* packed_dev, int64_t n, int8_t* codes_dev, void* stream);
+
+/* i6g_dequantize_rows -- out[r, c] = code[r, c] * scale[r] for a [rows, cols]
+ * matrix of int8 codes (int6 or int8) and binary16 row scales.
+ * out_dtype I6G_DTYPE_F32: the exact product (an int8 times a binary16 has at
+ * most 19 significant bits); I6G_DTYPE_BF16: that product rounded to
+ * bfloat16, nearest with ties to even (a NaN stays a NaN).  out_dev [rows, cols].
+ * Errors: I6G_EINVAL for rows or cols < 0, an unknown dtype or a NULL
+ * buffer; I6G_EUNSUPPORTED for misaligned buffers. */
+int i6g_dequantize_rows(const int8_t* codes_dev, const uint16_t* scales_dev, int64_t rows, int64_t cols,
+                        int out_dtype, void* out_dev, void* stream);
+
+/* i6g_dequantize_int6_packed -- i6g_dequantize_rows with the codes read from
+ * their packed form (the rows * cols codes of the matrix, row-major, packed
+ * by i6g_pack_int6): the decode step of loading an artifact, without the
+ * unpacked codes ever reaching memory.  Same results and errors. */
+int i6g_dequantize_int6_packed(const uint8_t* packed_dev, const uint16_t* scales_dev, int64_t rows,
+                               int64_t cols, int out_dtype, void* out_dev, void* stream);
+
+/* i6g_code_histogram -- counts of each int8 value among n codes:
+ * hist_dev[v + 128] (int64 [256]).  accumulate = 0 overwrites the
+ * histogram; 1 adds to it, so several matrices can share one histogram.
+ * Uses 128 KiB of stream-ordered temporary device memory (hipMallocAsync /
+ * hipFreeAsync on `stream`).  Errors: I6G_EINVAL for n < 0 or NULL buffers;
+ * I6G_ENOMEM if the temporary memory cannot be had. */
+int i6g_code_histogram(const int8_t* codes_dev, int64_t n, int accumulate, int64_t* hist_dev,
+                       void* stream);
+
+/* i6g_code_entropy -- Shannon entropy in bits per value of a 256-bin
+ * histogram of non-negative counts: -sum p log2 p over the bins with a
+ * positive count, p = count / total (fp64); 0 if the total is 0.  Writes one
+ * double to bits_dev.  Errors: I6G_EINVAL for NULL buffers. */
+int i6g_code_entropy(const int64_t* hist_dev, double* bits_dev, void* stream);
+
+/* i6g_artifact_bytes -- host only: bytes of a packed artifact holding
+ * n_mats int6 matrices (shapes[2 i] rows, shapes[2 i + 1] cols) at
+ * 3 * ceil(rows * cols / 4) bytes of codes plus 2 bytes per row scale each,
+ * and passthrough_elements binary16 values (2 bytes each).  Compare the
+ * result with I6G_ARTIFACT_LIMIT.  Errors: I6G_EINVAL for a negative count
+ * or size, or NULL shapes with n_mats > 0. */
+#define I6G_ARTIFACT_LIMIT 16000000LL
+int i6g_artifact_bytes(const int64_t* shapes, int32_t n_mats, int64_t passthrough_elements,
+                       int64_t* bytes);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,12 @@ EXPORTED = [
     "i6g_quantize_rows", "i6g_quantize_rows_many", "i6g_load_model", "i6g_score_tokens", "i6g_model_status",
     "i6g_free_model", "i6g_last_error", "i6g_plan_windows", "i6g_set_option",
     "i6g_set_timing", "i6g_get_timing",
+    "i6g_pack_int6", "i6g_unpack_int6", "i6g_dequantize_rows", "i6g_dequantize_int6_packed",
+    "i6g_code_histogram", "i6g_code_entropy", "i6g_artifact_bytes",
 ]
+DTYPE_F32, DTYPE_BF16 = 1, 2
+FLAG_CODE = 8
+ARTIFACT_LIMIT = 16_000_000
 
 
 class I6GError(RuntimeError):
@@ -90,6 +95,13 @@ def lib():
         L.i6g_set_option.argtypes = [vp, ctypes.c_int, i64]
         L.i6g_set_timing.argtypes = [vp, ctypes.c_int, ctypes.c_uint32]
         L.i6g_get_timing.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp]
+        L.i6g_pack_int6.argtypes = [vp, i64, vp, vp, vp]
+        L.i6g_unpack_int6.argtypes = [vp, i64, vp, vp]
+        L.i6g_dequantize_rows.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp, vp]
+        L.i6g_dequantize_int6_packed.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp, vp]
+        L.i6g_code_histogram.argtypes = [vp, i64, ctypes.c_int, vp, vp]
+        L.i6g_code_entropy.argtypes = [vp, vp, vp]
+        L.i6g_artifact_bytes.argtypes = [vp, i32, i64, vp]
         _lib = L
     return _lib
 
@@ -300,3 +312,150 @@ def load(model, qblocks):
     """Load a synthetic model dict with the given quantised blocks."""
     return Model(model["arch"], qblocks, model["embed"], model.get("skip_w"),
                  model.get("lora"), model.get("bigram"))
+
+
+# ---------------------------------------------------------------------------
+# Export side: 6-bit packing, dequantisation and code statistics.
+
+def packed_size(n):
+    """Bytes of n packed int6 codes (3 per group of 4, the last group padded)."""
+    return 3 * ((n + 3) // 4)
+
+
+def pack_int6(codes, flags=None, out=None):
+    """Pack a device int8 tensor of int6 codes (flattened) into a uint8 tensor
+    of packed_size(numel) bytes."""
+    import torch
+    if not (codes.is_cuda and codes.dtype == torch.int8 and codes.is_contiguous()):
+        raise ValueError("codes must be a contiguous int8 CUDA tensor")
+    n = codes.numel()
+    if out is None:
+        out = torch.empty(packed_size(n), dtype=torch.uint8, device=codes.device)
+    if out.numel() < packed_size(n):
+        raise ValueError("out is too small")
+    _check(lib().i6g_pack_int6(_ptr(codes), n, _ptr(out), _ptr(flags), _stream()))
+    return out
+
+
+def unpack_int6(packed, n, out=None):
+    """The first n codes held in a packed uint8 device tensor -> int8 [n]."""
+    import torch
+    if not (packed.is_cuda and packed.dtype == torch.uint8 and packed.is_contiguous()):
+        raise ValueError("packed must be a contiguous uint8 CUDA tensor")
+    if packed.numel() < packed_size(n):
+        raise ValueError("packed holds fewer than n codes")
+    if out is None:
+        out = torch.empty(n, dtype=torch.int8, device=packed.device)
+    _check(lib().i6g_unpack_int6(_ptr(packed), n, _ptr(out), _stream()))
+    return out
+
+
+def _dq_dtype(dtype):
+    import torch
+    if dtype == torch.float32:
+        return DTYPE_F32
+    if dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise ValueError("dtype must be torch.float32 or torch.bfloat16")
+
+
+def dequantize(codes, scales, dtype=None):
+    """code * scale per row of a device int8 [rows, cols] matrix with binary16
+    row scales (int16 bit patterns or float16), as float32 or bfloat16."""
+    import torch
+    dtype = dtype or torch.float32
+    if not (codes.is_cuda and codes.dtype == torch.int8 and codes.dim() == 2 and codes.is_contiguous()):
+        raise ValueError("codes must be a contiguous 2-D int8 CUDA tensor")
+    rows, cols = codes.shape
+    if scales.numel() != rows or scales.element_size() != 2 or not scales.is_contiguous():
+        raise ValueError("scales must hold one binary16 value per row")
+    out = torch.empty((rows, cols), dtype=dtype, device=codes.device)
+    _check(lib().i6g_dequantize_rows(_ptr(codes), _ptr(scales), rows, cols, _dq_dtype(dtype), _ptr(out),
+                                     _stream()))
+    return out
+
+
+def dequantize_packed(packed, scales, rows, cols, dtype=None):
+    """dequantize() of a [rows, cols] int6 matrix given in packed form."""
+    import torch
+    dtype = dtype or torch.float32
+    if not (packed.is_cuda and packed.dtype == torch.uint8 and packed.is_contiguous()):
+        raise ValueError("packed must be a contiguous uint8 CUDA tensor")
+    if packed.numel() < packed_size(rows * cols):
+        raise ValueError("packed holds fewer than rows * cols codes")
+    if scales.numel() != rows or scales.element_size() != 2 or not scales.is_contiguous():
+        raise ValueError("scales must hold one binary16 value per row")
+    out = torch.empty((rows, cols), dtype=dtype, device=packed.device)
+    _check(lib().i6g_dequantize_int6_packed(_ptr(packed), _ptr(scales), rows, cols, _dq_dtype(dtype),
+                                            _ptr(out), _stream()))
+    return out
+
+
+def code_histogram(codes, hist=None, accumulate=False):
+    """Counts of every int8 value of a device tensor: int64 [256], index v + 128."""
+    import torch
+    if not (codes.is_cuda and codes.dtype == torch.int8 and codes.is_contiguous()):
+        raise ValueError("codes must be a contiguous int8 CUDA tensor")
+    if hist is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing histogram")
+        hist = torch.empty(256, dtype=torch.int64, device=codes.device)
+    _check(lib().i6g_code_histogram(_ptr(codes), codes.numel(), int(bool(accumulate)), _ptr(hist),
+                                    _stream()))
+    return hist
+
+
+def code_entropy(hist):
+    """Entropy in bits per value of a device int64 [256] histogram, as a
+    float64 device tensor of one element."""
+    import torch
+    if not (hist.is_cuda and hist.dtype == torch.int64 and hist.numel() == 256 and hist.is_contiguous()):
+        raise ValueError("hist must be a contiguous int64 CUDA tensor of 256 counts")
+    out = torch.empty(1, dtype=torch.float64, device=hist.device)
+    _check(lib().i6g_code_entropy(_ptr(hist), _ptr(out), _stream()))
+    return out
+
+
+def artifact_bytes(shapes, passthrough_elements=0):
+    """Bytes of a packed artifact of int6 matrices with the given (rows, cols)
+    shapes, each with binary16 row scales, plus binary16 passthrough values."""
+    arr = np.ascontiguousarray(np.asarray(shapes, dtype=np.int64).reshape(-1, 2))
+    out = ctypes.c_int64(0)
+    _check(lib().i6g_artifact_bytes(arr.ctypes.data if len(arr) else None, len(arr),
+                                    int(passthrough_elements), ctypes.byref(out)))
+    return out.value
+
+
+def export_model(qblocks, passthrough_elements=0):
+    """Pack every int6 block matrix of a quantised model and measure its codes.
+    Returns a dict with ``packed`` (list of dicts name -> (packed, scales,
+    shape)), ``hist`` (int64 [256] over all codes), ``entropy_bits`` (device
+    float64 [1]) and ``bytes`` (the artifact size)."""
+    import torch
+    packed, shapes, hist = [], [], None
+    flags = None
+    for qb in qblocks:
+        pb = {}
+        for name, (codes, scales) in qb.items():
+            if flags is None:
+                flags = torch.zeros(1, dtype=torch.int32, device=codes.device)
+            pb[name] = (pack_int6(codes, flags), scales, tuple(codes.shape))
+            hist = code_histogram(codes, hist, accumulate=hist is not None)
+            shapes.append(codes.shape)
+        packed.append(pb)
+    if flags is not None and int(flags.item()) & FLAG_CODE:
+        raise I6GError(-1, "a block matrix holds a code that is not int6")
+    return {"packed": packed, "hist": hist, "entropy_bits": code_entropy(hist),
+            "bytes": artifact_bytes(shapes, passthrough_elements)}
+
+
+def import_model(packed):
+    """Unpack the int6 codes of export_model()'s ``packed`` list; returns the
+    qblocks list (dicts name -> (codes, scales)) that load() takes."""
+    out = []
+    for pb in packed:
+        qb = {}
+        for name, (p, scales, shape) in pb.items():
+            qb[name] = (unpack_int6(p, shape[0] * shape[1]).view(shape), scales)
+        out.append(qb)
+    return out

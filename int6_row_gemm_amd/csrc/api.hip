@@ -321,6 +321,76 @@ int i6g_quantize_rows_many(const i6g_quant_job* jobs, int32_t n_jobs, int bits, 
   return I6G_OK;
 }
 
+static bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int i6g_pack_int6(const int8_t* codes_dev, int64_t n, uint8_t* packed_dev, int32_t* flags_dev, void* stream) {
+  if (n < 0 || (n > 0 && (!codes_dev || !packed_dev))) return fail(I6G_EINVAL, "pack_int6: n < 0 or NULL buffer");
+  if (n == 0) return I6G_OK;
+  if (!aligned(codes_dev, 16) || !aligned(packed_dev, 4))
+    return fail(I6G_EUNSUPPORTED, "pack_int6: codes must be 16-byte and packed 4-byte aligned");
+  HIP_TRY(launch_pack_int6(codes_dev, n, packed_dev, flags_dev, (hipStream_t)stream));
+  return I6G_OK;
+}
+
+int i6g_unpack_int6(const uint8_t* packed_dev, int64_t n, int8_t* codes_dev, void* stream) {
+  if (n < 0 || (n > 0 && (!codes_dev || !packed_dev))) return fail(I6G_EINVAL, "unpack_int6: n < 0 or NULL buffer");
+  if (n == 0) return I6G_OK;
+  if (!aligned(codes_dev, 16) || !aligned(packed_dev, 4))
+    return fail(I6G_EUNSUPPORTED, "unpack_int6: codes must be 16-byte and packed 4-byte aligned");
+  HIP_TRY(launch_unpack_int6(packed_dev, n, codes_dev, (hipStream_t)stream));
+  return I6G_OK;
+}
+
+static int dequant(const char* who, const void* src, bool packed, const uint16_t* scales_dev, int64_t rows,
+                   int64_t cols, int out_dtype, void* out_dev, void* stream) {
+  if (rows < 0 || cols < 0) return fail(I6G_EINVAL, "%s: rows and cols must be >= 0", who);
+  if (out_dtype != I6G_DTYPE_F32 && out_dtype != I6G_DTYPE_BF16)
+    return fail(I6G_EINVAL, "%s: out_dtype must be I6G_DTYPE_F32 or I6G_DTYPE_BF16", who);
+  if (rows == 0 || cols == 0) return I6G_OK;
+  if (!src || !scales_dev || !out_dev) return fail(I6G_EINVAL, "%s: NULL buffer", who);
+  if (!aligned(src, packed ? 4 : 16) || !aligned(out_dev, 16) || !aligned(scales_dev, 2))
+    return fail(I6G_EUNSUPPORTED, "%s: misaligned buffer", who);
+  HIP_TRY(launch_dequantize(src, packed, scales_dev, rows, cols, out_dtype == I6G_DTYPE_BF16, out_dev,
+                            (hipStream_t)stream));
+  return I6G_OK;
+}
+
+int i6g_dequantize_rows(const int8_t* codes_dev, const uint16_t* scales_dev, int64_t rows, int64_t cols,
+                        int out_dtype, void* out_dev, void* stream) {
+  return dequant("dequantize_rows", codes_dev, false, scales_dev, rows, cols, out_dtype, out_dev, stream);
+}
+
+int i6g_dequantize_int6_packed(const uint8_t* packed_dev, const uint16_t* scales_dev, int64_t rows,
+                               int64_t cols, int out_dtype, void* out_dev, void* stream) {
+  return dequant("dequantize_int6_packed", packed_dev, true, scales_dev, rows, cols, out_dtype, out_dev, stream);
+}
+
+int i6g_code_histogram(const int8_t* codes_dev, int64_t n, int accumulate, int64_t* hist_dev, void* stream) {
+  if (n < 0 || !hist_dev || (n > 0 && !codes_dev)) return fail(I6G_EINVAL, "code_histogram: n < 0 or NULL buffer");
+  if (n > 0 && !aligned(codes_dev, 16)) return fail(I6G_EUNSUPPORTED, "code_histogram: codes must be 16-byte aligned");
+  HIP_TRY(launch_code_histogram(codes_dev, n, accumulate != 0, hist_dev, (hipStream_t)stream));
+  return I6G_OK;
+}
+
+int i6g_code_entropy(const int64_t* hist_dev, double* bits_dev, void* stream) {
+  if (!hist_dev || !bits_dev) return fail(I6G_EINVAL, "code_entropy: NULL buffer");
+  HIP_TRY(launch_code_entropy(hist_dev, bits_dev, (hipStream_t)stream));
+  return I6G_OK;
+}
+
+int i6g_artifact_bytes(const int64_t* shapes, int32_t n_mats, int64_t passthrough_elements, int64_t* bytes) {
+  if (!bytes || n_mats < 0 || passthrough_elements < 0 || (n_mats > 0 && !shapes))
+    return fail(I6G_EINVAL, "artifact_bytes: negative count or NULL array");
+  int64_t total = 2 * passthrough_elements;
+  for (int32_t i = 0; i < n_mats; ++i) {
+    const int64_t r = shapes[2 * i], c = shapes[2 * i + 1];
+    if (r < 0 || c < 0) return fail(I6G_EINVAL, "artifact_bytes: matrix %d has a negative size", i);
+    total += 3 * ((r * c + 3) / 4) + 2 * r;
+  }
+  *bytes = total;
+  return I6G_OK;
+}
+
 int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
   if (!out) return fail(I6G_EINVAL, "load_model: out is NULL");
   *out = nullptr;

@@ -21,7 +21,7 @@ def _lib():
 def _header_functions():
     src = open(os.path.join(ROOT, "include", "i6g.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(i6g_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(i6g_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
@@ -133,3 +133,43 @@ def test_quantize_rows_many_validates_before_enqueueing():
     jobs[1] = g._QuantJob(0x1000, 0x2000, 0x3000, 4, 512)
     assert L.i6g_quantize_rows_many(ctypes.cast(jobs, ctypes.c_void_p), 2, 7, 0.9999984, None, None) == -1
     assert L.i6g_quantize_rows_many(ctypes.cast(jobs, ctypes.c_void_p), 2, 6, 0.5, None, None) == -6
+
+
+def test_export_entry_points_validate_without_gpu():
+    g, L = _lib()
+    fake = ctypes.c_void_p(0x1000)     # 4096-aligned, never dereferenced
+    odd = ctypes.c_void_p(0x1001)
+    null = ctypes.c_void_p(0)
+    assert L.i6g_pack_int6(fake, -1, fake, null, null) == -1
+    assert L.i6g_pack_int6(null, 4, fake, null, null) == -1
+    assert L.i6g_pack_int6(null, 0, null, null, null) == 0          # nothing to do
+    assert L.i6g_pack_int6(odd, 16, fake, null, null) == -6
+    assert L.i6g_unpack_int6(fake, 16, odd, null) == -6
+    assert L.i6g_unpack_int6(fake, -3, fake, null) == -1
+    assert L.i6g_dequantize_rows(fake, fake, 4, 4, 0, fake, null) == -1   # fp16 output: not offered
+    assert L.i6g_dequantize_rows(fake, fake, -1, 4, 1, fake, null) == -1
+    assert L.i6g_dequantize_rows(null, fake, 4, 4, 1, fake, null) == -1
+    assert L.i6g_dequantize_rows(fake, fake, 0, 4, 2, null, null) == 0
+    assert L.i6g_dequantize_int6_packed(fake, fake, 4, 4, 2, odd, null) == -6
+    assert L.i6g_code_histogram(fake, 16, 0, null, null) == -1
+    assert L.i6g_code_histogram(odd, 16, 0, fake, null) == -6
+    assert L.i6g_code_entropy(null, fake, null) == -1
+    out = ctypes.c_int64(0)
+    assert L.i6g_artifact_bytes(None, -1, 0, ctypes.byref(out)) == -1
+    assert L.i6g_artifact_bytes(None, 0, -5, ctypes.byref(out)) == -1
+    bad = (ctypes.c_int64 * 2)(3, -1)
+    assert L.i6g_artifact_bytes(bad, 1, 0, ctypes.byref(out)) == -1
+
+
+def test_artifact_bytes_matches_oracle():
+    g, _ = _lib()
+    from oracle import export as ox
+    import synth
+    for shapes, pt in [([(3, 5)], 7), ([(1, 4), (2, 2), (7, 1)], 0), ([], 11), ([(0, 5), (5, 0)], 1)]:
+        assert g.artifact_bytes(shapes, pt) == ox.artifact_bytes(shapes, pt)
+    for name in ("11l", "11l_next", "midcycle", "tiny"):
+        arch = synth.config(name)["arch"]
+        d, kv, F = arch["d_model"], arch["n_kv_heads"] * arch["head_dim"], arch["d_ff"]
+        shapes = [(d, d), (kv, d), (kv, d), (d, d), (F, d), (d, F)] * len(set(arch["schedule"]))
+        pt = arch["vocab"] * d
+        assert g.artifact_bytes(shapes, pt) == ox.artifact_bytes(shapes, pt)
