@@ -47,6 +47,10 @@ _BASE = dict(
     embed_dtype="fp16",
     bits=6,
     clip_q=0.9999984,
+    # mixed precision: bits of the attention (q, k, v, o) and MLP (fc, proj)
+    # matrices when they differ from ``bits`` (None = ``bits``)
+    bits_attn=None,
+    bits_mlp=None,
     # evaluation variants (off by default): logits divided by the
     # temperature, MLP activation leaky_relu(x, slope)^2, RoPE on the first
     # rope_dims dims of each head (None = all), exclusive self attention on
@@ -100,6 +104,20 @@ CONFIGS = {
         arch=_arch(vocab=1024, d_model=512, n_heads=8, n_kv_heads=4, mlp_mult=3,
                    schedule=[i % 4 for i in range(11)], skip_kind=SKIP_UNET, n_skip=5,
                    temperature=0.90, leaky_slope=0.5, rope_dims=16, xsa_last_n=4),
+        n_tokens=1_048_576, zipf=1.1, bytes_max=8, window=2048, stride=64,
+    ),
+    # the flat 11-layer model exported with every block matrix at int5
+    # (MLP_INT5 and ATTN_INT5 in the PR #363 write-up's run commands)
+    "11l_int5": dict(
+        arch=_arch(vocab=1024, d_model=512, n_heads=8, n_kv_heads=4, mlp_mult=3,
+                   schedule=list(range(11)), skip_kind=SKIP_UNET, n_skip=5, bits=5),
+        n_tokens=1_048_576, zipf=1.1, bytes_max=8, window=2048, stride=64,
+    ),
+    # 10 layers with int5 MLP matrices and int6 attention matrices (the
+    # mixed int5 / int6 "10L Int5-MLP" entry of the records table)
+    "10l_int5mlp": dict(
+        arch=_arch(vocab=1024, d_model=512, n_heads=8, n_kv_heads=4, mlp_mult=3,
+                   schedule=list(range(10)), skip_kind=SKIP_UNET, n_skip=5, bits=6, bits_mlp=5),
         n_tokens=1_048_576, zipf=1.1, bytes_max=8, window=2048, stride=64,
     ),
     "largevocab": dict(

@@ -70,13 +70,15 @@ def replay_row(w, bits, q):
     f = r32(Fr(pos) - lo)
     c = r32(srt[lo] + r32(f * r32(srt[hi] - srt[lo])))
     c = max(c, r32(Fr(1e-12)))
-    scale = r32(c / 127)
+    scale = r32(c / (15 if bits == 5 else 127))
     codes = []
     for v in ws:
         v = min(max(v, -c), c)
         k = _rne_int(r32(v / scale))
         if bits == 8:
             code = min(max(k, -127), 127)
+        elif bits == 5:
+            code = min(max(k, -16), 15)
         else:
             code = min(max(_rne_int(Fr(k, 4)) * 4, -128), 124)
         codes.append(code)
@@ -91,7 +93,8 @@ def _check_rows(w, bits, q):
         assert Fr(float(s16[i])) == ref_s, f"row {i} scale"
 
 
-@pytest.mark.parametrize("bits,q", [(8, 1.0), (8, 0.9999984), (6, 0.9999984), (6, 1.0), (6, 0.9)])
+@pytest.mark.parametrize("bits,q", [(8, 1.0), (8, 0.9999984), (6, 0.9999984), (6, 1.0), (6, 0.9),
+                                    (5, 0.9999984), (5, 1.0), (5, 0.9)])
 def test_exact_replay_random(bits, q):
     rng = np.random.default_rng(7)
     for cols in (1, 2, 3, 17, 64, 130):
@@ -100,7 +103,7 @@ def test_exact_replay_random(bits, q):
         _check_rows(w, bits, q)
 
 
-@pytest.mark.parametrize("bits,q", [(8, 1.0), (6, 0.9999984), (6, 0.5)])
+@pytest.mark.parametrize("bits,q", [(8, 1.0), (6, 0.9999984), (6, 0.5), (5, 0.9999984), (5, 1.0)])
 def test_exact_replay_adversarial(bits, q):
     rng = np.random.default_rng(11)
     w = synth.adversarial_rows(rng, 48)
@@ -226,3 +229,49 @@ def test_config_matrix_counts():
     arch = synth.CONFIGS["11l"]["arch"]
     rows, weights = synth.gemm_rows(arch)
     assert (rows, weights) == (39_424, 25_952_256)
+
+
+# ---------------------------------------------------------------- int5
+def test_int5_hand_row():
+    # c = 0.9375 (q = 1), scale = c / 15 = 0.0625 exactly; ratios w / scale
+    # 15, -8, 0.5 (tie -> 0), 1.5 (tie -> 2), -2.5 (tie -> -2), 3.2, -15, 7.5 (tie -> 8)
+    w = np.array([[0.9375, -0.5, 0.03125, 0.09375, -0.15625, 0.2, -0.9375, 0.46875]], np.float32)
+    codes, s16 = quant.quantize_rows(w, 5, 1.0)
+    assert codes[0].tolist() == [15, -8, 0, 2, -2, 3, -15, 8]
+    assert float(s16[0]) == 0.0625
+
+
+def test_int5_code_set_and_step():
+    rng = np.random.default_rng(5)
+    w = rng.normal(0, 0.02, size=(8, 4096)).astype(np.float32)
+    codes, s16 = quant.quantize_rows(w, 5, 1.0)
+    # inside the clip |w / scale| <= 15: at most 31 levels; Gaussian rows
+    # of 4096 reach every level of the bulk on both signs
+    assert codes.min() >= -15 and codes.max() <= 15
+    for row in codes:
+        assert set(range(-10, 11)) <= set(row.tolist())
+    # the step is amax / 15 (the largest |w| of each row maps to +-15)
+    amax = np.abs(w).max(axis=1)
+    assert np.allclose(s16.astype(np.float64), amax / 15.0, rtol=2 ** -11)
+    assert np.all(np.abs(codes[np.arange(8), np.abs(w).argmax(axis=1)]) == 15)
+
+
+def test_rms_error_ratio_int5_vs_int8():
+    # uniform rounding error: RMS = step / sqrt(12); the steps are amax/15
+    # and amax/127, so the ratio is 127 / 15 for rows whose values fill the range
+    rng = np.random.default_rng(9)
+    w = rng.uniform(-1, 1, size=(64, 2048)).astype(np.float32)
+    e5 = quant.dequantize(*quant.quantize_rows(w, 5, 1.0)) - w
+    e8 = quant.dequantize(*quant.quantize_rows(w, 8, 1.0)) - w
+    ratio = math.sqrt(np.mean(e5 ** 2) / np.mean(e8 ** 2))
+    assert abs(ratio - 127 / 15) < 0.25
+
+
+def test_mixed_bits_per_matrix():
+    arch = dict(bits=6, bits_mlp=5)
+    assert [quant.matrix_bits(arch, n) for n in ("q", "k", "v", "o", "fc", "proj")] == [6, 6, 6, 6, 5, 5]
+    arch = dict(bits=6, bits_attn=5, bits_mlp=5)
+    assert {quant.matrix_bits(arch, n) for n in ("q", "k", "v", "o", "fc", "proj")} == {5}
+    assert quant.matrix_bits(dict(bits=8), "fc") == 8
+    with pytest.raises(ValueError):
+        quant.quantize_rows(np.ones((1, 4), np.float32), 4, 1.0)
