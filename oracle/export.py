@@ -1,5 +1,5 @@
-"""Export side of the int6 format: bit packing, code statistics, artifact
-size, dequantisation.  Test infrastructure: only tests/,
+"""Export side of the int6 / int5 formats: bit packing, code statistics,
+artifact size, dequantisation.  Test infrastructure: only tests/,
 __graft_entry__.smoke() and bench.py's CPU baseline use this package.
 
 Sources (page, section):
@@ -17,9 +17,9 @@ Readings (listed in the design doc): an int6 code c (a multiple of 4 in
 the 24-bit word u0 | u1 << 6 | u2 << 12 | u3 << 18 stored as 3 bytes, least
 significant first; a tail of fewer than four codes is padded with code 0;
 entropy is the Shannon entropy of the code histogram in bits per value;
-the artifact's byte count is the packed codes plus 2 bytes per row scale
-plus every passthrough tensor at 2 bytes per element (no general-purpose
-compressor).
+the artifact's byte count is the packed codes (int8 matrices at one byte
+per code) plus 2 bytes per row scale plus every passthrough tensor at 2
+bytes per element (no general-purpose compressor).
 """
 from __future__ import annotations
 
@@ -58,6 +58,56 @@ def unpack_int6(packed: np.ndarray, n: int) -> np.ndarray:
     return ((u[:n] - 32) * 4).astype(np.int8)
 
 
+def is_int5_code(c: np.ndarray) -> np.ndarray:
+    """True where c is in [-16, 15]."""
+    c = np.asarray(c, dtype=np.int64)
+    return (c >= -16) & (c <= 15)
+
+
+def pack_int5(codes: np.ndarray) -> np.ndarray:
+    """int5 codes (int8, flattened) -> uint8 bytes, 5 per 8 codes."""
+    c = np.asarray(codes, dtype=np.int64).ravel()
+    if not np.all(is_int5_code(c)):
+        raise ValueError("not an int5 code")
+    pad = (-len(c)) % 8
+    u = np.concatenate([c + 16, np.full(pad, 16, dtype=np.int64)]).reshape(-1, 8)
+    word = np.zeros(len(u), dtype=np.int64)
+    for i in range(8):
+        word |= u[:, i] << (5 * i)
+    out = np.stack([(word >> (8 * k)) & 0xFF for k in range(5)], axis=1).astype(np.uint8)
+    return out.ravel()
+
+
+def unpack_int5(packed: np.ndarray, n: int) -> np.ndarray:
+    """The first n int5 codes (int8) held in packed bytes."""
+    b = np.asarray(packed, dtype=np.int64).reshape(-1, 5)
+    word = np.zeros(len(b), dtype=np.int64)
+    for k in range(5):
+        word |= b[:, k] << (8 * k)
+    u = np.stack([(word >> (5 * i)) & 31 for i in range(8)], axis=1).ravel()
+    return (u[:n] - 16).astype(np.int8)
+
+
+def packed_bytes(n: int, bits: int) -> int:
+    """Bytes of n packed codes: 3 per 4 int6 codes, 5 per 8 int5 codes, 1 per
+    int8 code (unpacked), each rounded up to whole words."""
+    if bits == 6:
+        return 3 * ((n + 3) // 4)
+    if bits == 5:
+        return 5 * ((n + 7) // 8)
+    if bits == 8:
+        return n
+    raise ValueError("bits must be 5, 6 or 8")
+
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    return {6: pack_int6, 5: pack_int5}[bits](codes)
+
+
+def unpack_codes(packed: np.ndarray, n: int, bits: int) -> np.ndarray:
+    return {6: unpack_int6, 5: unpack_int5}[bits](packed, n)
+
+
 def code_histogram(codes: np.ndarray) -> np.ndarray:
     """Counts of every int8 value, index v + 128 (int64 [256])."""
     c = np.asarray(codes, dtype=np.int64).ravel()
@@ -72,13 +122,14 @@ def entropy_bits(hist: np.ndarray) -> float:
     return float(-(p * np.log2(p)).sum())
 
 
-def artifact_bytes(matrices, passthrough_elements: int) -> int:
-    """Bytes of the packed artifact: for each (rows, cols) int6 matrix,
-    3 bytes per 4 codes (rounded up per matrix) + 2 bytes per row scale;
-    plus 2 bytes per passthrough (fp16) element."""
+def artifact_bytes(matrices, passthrough_elements: int, bits=None) -> int:
+    """Bytes of the packed artifact: for each (rows, cols) matrix its packed
+    codes (bits[i], default 6; rounded up per matrix) + 2 bytes per row
+    scale; plus 2 bytes per passthrough (fp16) element."""
     total = 0
-    for rows, cols in matrices:
-        total += 3 * ((rows * cols + 3) // 4) + 2 * rows
+    for i, (rows, cols) in enumerate(matrices):
+        b = 6 if bits is None else bits[i]
+        total += packed_bytes(rows * cols, b) + 2 * rows
     return total + 2 * passthrough_elements
 
 

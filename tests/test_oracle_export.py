@@ -105,3 +105,45 @@ def test_dequantize_matches_quantiser_reconstruction():
     inside = np.abs(w) <= 122 * sc
     assert inside.mean() > 0.9
     assert np.all(err[inside] <= 2.57 * np.broadcast_to(sc, w.shape)[inside])
+
+
+INT5 = np.arange(-16, 16, dtype=np.int8)
+
+
+def test_int5_hand_packed_bytes():
+    # codes -16, 15, 0, 1, -1, 2, -2, 3 -> u = 0, 31, 16, 17, 15, 18, 14, 19
+    u = [0, 31, 16, 17, 15, 18, 14, 19]
+    word = sum(v << (5 * i) for i, v in enumerate(u))
+    got = ox.pack_int5(np.array([-16, 15, 0, 1, -1, 2, -2, 3], dtype=np.int8))
+    assert list(got) == [(word >> (8 * k)) & 255 for k in range(5)]
+    # one code pads with seven zeros (u = 16): -16 -> u = 0
+    word = sum(16 << (5 * i) for i in range(1, 8))
+    assert list(ox.pack_int5(np.array([-16], dtype=np.int8))) == [(word >> (8 * k)) & 255 for k in range(5)]
+
+
+def test_int5_roundtrip_and_sizes():
+    rng = np.random.default_rng(2)
+    for n in (1, 7, 8, 9, 31, 32, 33, 1000, 1003):
+        c = rng.choice(INT5, n)
+        p = ox.pack_int5(c)
+        assert len(p) == ox.packed_bytes(n, 5) == 5 * ((n + 7) // 8)
+        np.testing.assert_array_equal(ox.unpack_int5(p, n), c)
+    for pos in range(8):
+        c = np.zeros((32, 8), dtype=np.int8)
+        c[:, pos] = np.roll(INT5, 5 * pos)
+        np.testing.assert_array_equal(ox.unpack_codes(ox.pack_codes(c, 5), 256, 5).reshape(32, 8), c)
+    with pytest.raises(ValueError):
+        ox.pack_int5(np.array([16], dtype=np.int8))
+    with pytest.raises(ValueError):
+        ox.pack_int5(np.array([-17], dtype=np.int8))
+
+
+def test_artifact_bytes_mixed_widths():
+    # int5 [3, 5]: 15 codes -> 2 words of 5 bytes; int8 [2, 3]: 6 bytes
+    assert ox.artifact_bytes([(3, 5), (2, 3), (1, 4)], 1, bits=[5, 8, 6]) == (10 + 6) + (6 + 4) + (3 + 2) + 2
+    # the all-int5 11-layer model: 5/8 byte per code
+    arch = synth.config("11l_int5")["arch"]
+    shapes = list(synth.matrix_shapes(arch).values()) * 11
+    n = sum(r * c for r, c in shapes)
+    rows = sum(r for r, _ in shapes)
+    assert ox.artifact_bytes(shapes, 0, bits=[5] * len(shapes)) == 5 * n // 8 + 2 * rows
