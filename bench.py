@@ -94,19 +94,22 @@ def main():
     lib = g.lib()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
-    # every block matrix of the model in one i6g_quantize_rows_many call
-    # (one launch per 64 matrices)
-    jobs = (g._QuantJob * sum(len(wb) for wb in w_dev))()
-    for i, (wb, cb, sb, k) in enumerate((wb, cb, sb, k) for wb, cb, sb in zip(w_dev, codes, scales)
-                                        for k in wb):
-        w = wb[k]
-        jobs[i] = g._QuantJob(w.data_ptr(), cb[k].data_ptr(), sb[k].data_ptr(), w.shape[0], w.shape[1])
+    # every block matrix of the model in one i6g_quantize_rows_many call per
+    # bit width (one launch per 64 matrices)
+    by_bits = {}
+    for wb, cb, sb in zip(w_dev, codes, scales):
+        for k in wb:
+            w = wb[k]
+            by_bits.setdefault(g.matrix_bits(arch, k), []).append(
+                g._QuantJob(w.data_ptr(), cb[k].data_ptr(), sb[k].data_ptr(), w.shape[0], w.shape[1]))
+    job_arrays = {b: (g._QuantJob * len(js))(*js) for b, js in by_bits.items()}
 
     def quantize_all():
-        rc = lib.i6g_quantize_rows_many(ctypes.cast(jobs, ctypes.c_void_p), len(jobs), arch["bits"],
-                                        float(arch["clip_q"]), None, stream)
-        if rc != 0:
-            raise g.I6GError(rc, lib.i6g_last_error().decode())
+        for b, jobs in job_arrays.items():
+            rc = lib.i6g_quantize_rows_many(ctypes.cast(jobs, ctypes.c_void_p), len(jobs), b,
+                                            float(arch["clip_q"]), None, stream)
+            if rc != 0:
+                raise g.I6GError(rc, lib.i6g_last_error().decode())
 
     quantize_all()
     torch.cuda.synchronize()
@@ -226,50 +229,59 @@ def main():
         quant["us_per_pass"] = us
 
     # The export side on the model's codes, each a kernel over the block
-    # matrices laid end to end: 6-bit packing (1 B read + 0.75 B written per
-    # code), decoding the packed matrices to bfloat16 (0.75 B + 2 B per code
-    # + 2 B per row; two launches, one per row length) and the code
-    # histogram (1 B per code).
+    # matrices of one bit width laid end to end: packing (1 B read + b/8 B
+    # written per code), decoding the packed matrices to bfloat16 (b/8 B +
+    # 2 B per code + 2 B per row; one launch per row length) and the code
+    # histogram over every matrix (1 B per code).
     export = None
     if not args.no_timing:
         flat = torch.cat([cb[k].reshape(-1) for cb in codes for k in cb])
-        by_cols = {}
-        for cb, sb in zip(codes, scales):
-            for k in cb:
-                by_cols.setdefault(cb[k].shape[1], []).append((cb[k], sb[k]))
-        stacks = [(torch.cat([c for c, _ in v]), torch.cat([s for _, s in v])) for v in by_cols.values()]
-        stacks = [(g.pack_int6(c.reshape(-1)), s, c.shape[0], c.shape[1]) for c, s in stacks]
-        packed = g.pack_int6(flat)
         hist = torch.empty(256, dtype=torch.int64, device="cuda")
-        outs = [torch.empty((r, c), dtype=torch.bfloat16, device="cuda") for _, _, r, c in stacks]
-        n_c, n_r = flat.numel(), sum(r for _, _, r, _ in stacks)
+        export = {"codes": flat.numel()}
+        parts = {}
+        keep = []
+        for b in sorted({g.matrix_bits(arch, k) for k in codes[0]}):
+            if b == 8:
+                continue
+            mats = [(cb[k], sb[k]) for cb, sb in zip(codes, scales) for k in cb if g.matrix_bits(arch, k) == b]
+            fb = torch.cat([c.reshape(-1) for c, _ in mats])
+            by_cols = {}
+            for c, s_ in mats:
+                by_cols.setdefault(c.shape[1], []).append((c, s_))
+            stacks = [(torch.cat([c for c, _ in v]), torch.cat([s_ for _, s_ in v])) for v in by_cols.values()]
+            stacks = [(g.pack_codes(c.reshape(-1), b), s_, c.shape[0], c.shape[1]) for c, s_ in stacks]
+            pk = g.pack_codes(fb, b)
+            outs = [torch.empty((r, c), dtype=torch.bfloat16, device="cuda") for _, _, r, c in stacks]
+            keep += [fb, pk, stacks, outs]
+            n_c, n_r = fb.numel(), sum(r for _, _, r, _ in stacks)
 
-        def dq():
-            for (p, s_, r, c), o in zip(stacks, outs):
-                rc = lib.i6g_dequantize_int6_packed(ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(s_.data_ptr()),
-                                                    r, c, g.DTYPE_BF16, ctypes.c_void_p(o.data_ptr()), stream)
-                if rc:
-                    raise g.I6GError(rc, lib.i6g_last_error().decode())
+            def dq(stacks=stacks, outs=outs, b=b):
+                for (p, s_, r, c), o in zip(stacks, outs):
+                    rc = lib.i6g_dequantize_packed(ctypes.c_void_p(p.data_ptr()), b, ctypes.c_void_p(s_.data_ptr()),
+                                                   r, c, g.DTYPE_BF16, ctypes.c_void_p(o.data_ptr()), stream)
+                    if rc:
+                        raise g.I6GError(rc, lib.i6g_last_error().decode())
 
-        parts = {
-            "pack_int6": (lambda: g.pack_int6(flat, out=packed), 1.75 * n_c),
-            "dequantize_int6_packed_bf16": (dq, 2.75 * n_c + 2.0 * n_r),
-            "code_histogram": (lambda: g.code_histogram(flat, hist), 1.0 * n_c),
-        }
-        export = {"codes": n_c}
+            parts[f"pack_int{b}"] = (lambda fb=fb, pk=pk, b=b: g.pack_codes(fb, b, out=pk), (1 + b / 8) * n_c)
+            parts[f"dequantize_packed_int{b}_bf16"] = (dq, (b / 8 + 2) * n_c + 2.0 * n_r)
+        parts["code_histogram"] = (lambda: g.code_histogram(flat, hist), 1.0 * flat.numel())
         for name, (fn, by) in parts.items():
             export[name] = hbm_entry(*timed(fn), by)
-        export["artifact_bytes"] = g.artifact_bytes([c.shape for cb in codes for c in cb.values()],
-                                                    model["embed"].size + (model["skip_w"].size
-                                                                           if model["skip_w"] is not None else 0))
+        names = [k for k in codes[0]]
+        export["artifact_bytes"] = g.artifact_bytes(
+            [cb[k].shape for cb in codes for k in names],
+            model["embed"].size + (model["skip_w"].size if model["skip_w"] is not None else 0),
+            [g.matrix_bits(arch, k) for _ in codes for k in names])
         export["entropy_bits"] = g.code_entropy(g.code_histogram(flat, hist)).item()
-        del flat, stacks, packed, outs
+        del flat, keep
     del flush
 
     cpu = None
     if args.cpu_windows > 0:
         cpu = cpu_baseline(model, tokens_np, L, S, args.cpu_windows)
 
+    widths = sorted({g.matrix_bits(arch, k) for k in ("q", "fc")})
+    bits_label = "/".join(f"int{b}" for b in widths)
     out = {
         "metric": "scored tokens/sec, 11L-512d int6 sliding-window bpb eval",
         "value": value,
@@ -284,7 +296,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded Zipf tokens, uniform byte counts, N(0,0.02) weights)",
         "config": {"workload": f"{args.config}: {arch['n_eff']} layers d={arch['d_model']} "
-                               f"int{arch['bits']} sliding window {L} stride {S} over {N} tokens",
+                               f"{bits_label} sliding window {L} stride {S} over {N} tokens",
                    "tokens": N, "scored": P, "window": L, "stride": S, "seed": args.seed,
                    "parallelism": "single GPU"},
         "bpb": float(tot[3]),

@@ -56,33 +56,38 @@ enum { I6G_SKIP_NONE = 0, I6G_SKIP_UNET = 1, I6G_SKIP_STEM_TAIL = 2 };
 enum { I6G_DTYPE_F16 = 0, I6G_DTYPE_F32 = 1, I6G_DTYPE_BF16 = 2 };
 
 /*
- * i6g_quantize_rows -- per-row int8 / int6 quantisation of an fp32 matrix.
+ * i6g_quantize_rows -- per-row int8 / int6 / int5 quantisation of an fp32
+ * matrix.
  *
  * [11L] 训练时的模拟量化 and 后训练量化导出: one scale per row, scale =
  * c / 127 where c is the row's clipped absolute maximum; codes are
  * round(w / scale) and, in int6 mode, round(code / 4) * 4 clamped to
  * [-128, 124] (64 levels in an int8 container); the stored scale is binary16.
- * [363] Noisy-QAT block: c is floored at 1e-12.
+ * [363] Noisy-QAT block: c is floored at 1e-12.  [363] run commands
+ * (MLP_INT5, ATTN_INT5) and closing notes (int5 step amax / 15): in int5
+ * mode scale = c / 15 and codes are round(w / scale) clamped to [-16, 15].
  *
  * Exact steps (all binary32, each operation rounded separately):
  *   c      = s[lo] + f * (s[hi] - s[lo]), s = |w| sorted ascending,
  *            pos = clip_quantile * (cols - 1) (binary64), lo = floor(pos),
  *            hi = min(lo + 1, cols - 1), f = (float)(pos - lo);
- *   c      = max(c, 1e-12f);   scale = c / 127.0f (correctly rounded);
+ *   c      = max(c, 1e-12f);   scale = c / L (correctly rounded), L = 127.0f
+ *            for bits 8 and 6, 15.0f for bits 5;
  *   r      = clamp(w, -c, c) / scale;   k = rint(r) (half to even);
  *   bits 8: code = clamp(k, -127, 127)
  *   bits 6: code = clamp(rint(k / 4) * 4, -128, 124)
+ *   bits 5: code = clamp(k, -16, 15)
  *   scale_f16 = binary16 round-to-nearest-even of scale (subnormals kept).
  *
  * w_dev          [rows, cols] fp32, device.
- * bits           6 or 8.
+ * bits           5, 6 or 8.
  * clip_quantile  in (0, 1]; 1.0 = plain absolute maximum.
  * codes_dev      [rows, cols] int8 output, device (caller-owned).
  * scales_dev     [rows] binary16 bit patterns output, device (caller-owned).
  * flags_dev      optional device int32; I6G_FLAG_NONFINITE is OR-ed in when
  *                a row holds NaN/Inf (that row's codes are then 0 and its
  *                scale is the binary16 NaN 0x7e00).  May be NULL.
- * Errors: I6G_EINVAL for rows/cols < 1, bits not in {6, 8}, quantile out of
+ * Errors: I6G_EINVAL for rows/cols < 1, bits not in {5, 6, 8}, quantile out of
  * (0, 1] or a NULL array; I6G_EUNSUPPORTED if cols - floor(pos) > 8 (the
  * kernel keeps the 8 largest |w| of a row) or cols > 65536.
  */
@@ -281,33 +286,38 @@ int i6g_get_timing(i6g_model* m, int kernel_class, double* total_ms, int64_t* la
                    double* flops, double* bytes);
 
 /*
- * Export side.  [363] timeline and run notes: the int6 codes are sized by
- * their entropy in bits per value, compressed (bit packing among the methods
+ * Export side.  [363] timeline and run notes: the codes are sized by their
+ * entropy in bits per value, compressed (bit packing among the methods
  * tried) into an artifact of at most 16,000,000 bytes, then dequantised and
- * evaluated again.  [11L] 后训练量化导出: codes are int8 multiples of 4 in
+ * evaluated again; its run commands export int5 matrices (MLP_INT5,
+ * ATTN_INT5).  [11L] 后训练量化导出: int6 codes are int8 multiples of 4 in
  * [-128, 124] with one binary16 scale per row.
  *
- * Packed int6 format: code c -> u = c/4 + 32 in [0, 63]; four codes u0..u3
- * make the 24-bit word u0 | u1 << 6 | u2 << 12 | u3 << 18, stored as 3 bytes
- * least significant first; n codes take 3 * ceil(n / 4) bytes, a tail of
- * fewer than four codes padded with code 0.  Code buffers and fp32/bf16
- * outputs must be 16-byte aligned and packed buffers 4-byte aligned
- * (I6G_EUNSUPPORTED otherwise); n = 0 enqueues nothing.
+ * Packed formats (bits), least significant bit first:
+ *   6: code c -> u = c/4 + 32 in [0, 63]; four codes u0..u3 make the 24-bit
+ *      word u0 | u1 << 6 | u2 << 12 | u3 << 18, stored as 3 bytes;
+ *      n codes take 3 * ceil(n / 4) bytes;
+ *   5: code c -> u = c + 16 in [0, 31]; eight codes make the 40-bit word
+ *      sum u_i << 5i, stored as 5 bytes; n codes take 5 * ceil(n / 8) bytes;
+ * a tail shorter than a word is padded with code 0.  Code buffers and
+ * fp32/bf16 outputs must be 16-byte aligned and packed buffers 4-byte
+ * aligned (I6G_EUNSUPPORTED otherwise); n = 0 enqueues nothing.
  */
 
-/* i6g_pack_int6 -- n int6 codes (int8) -> 3 * ceil(n / 4) packed bytes.  A
- * byte that is not a multiple of 4 is packed as if its low two bits were
- * clear and I6G_FLAG_CODE is OR-ed into *flags_dev (may be NULL).
- * Errors: I6G_EINVAL for n < 0 or a NULL buffer with n > 0. */
-int i6g_pack_int6(const int8_t* codes_dev, int64_t n, uint8_t* packed_dev, int32_t* flags_dev,
-                  void* stream);
+/* i6g_pack_codes -- n codes (int8) -> their packed bytes (bits 5 or 6).  A
+ * byte that is not a code of the format (int6: not a multiple of 4; int5:
+ * outside [-16, 15]) is packed from its low bits and I6G_FLAG_CODE is OR-ed
+ * into *flags_dev (may be NULL).  Errors: I6G_EINVAL for bits not in {5, 6},
+ * n < 0 or a NULL buffer with n > 0. */
+int i6g_pack_codes(const int8_t* codes_dev, int64_t n, int bits, uint8_t* packed_dev, int32_t* flags_dev,
+                   void* stream);
 
-/* i6g_unpack_int6 -- the inverse: the first n codes held in packed_dev
- * (3 * ceil(n / 4) bytes) -> codes_dev [n] int8.  Errors as i6g_pack_int6. */
-int i6g_unpack_int6(const uint8_t* packed_dev, int64_t n, int8_t* codes_dev, void* stream);
+/* i6g_unpack_codes -- the inverse: the first n codes held in packed_dev ->
+ * codes_dev [n] int8.  Errors as i6g_pack_codes. */
+int i6g_unpack_codes(const uint8_t* packed_dev, int64_t n, int bits, int8_t* codes_dev, void* stream);
 
 /* i6g_dequantize_rows -- out[r, c] = code[r, c] * scale[r] for a [rows, cols]
- * matrix of int8 codes (int6 or int8) and binary16 row scales.
+ * matrix of int8 codes (int8, int6 or int5) and binary16 row scales.
  * out_dtype I6G_DTYPE_F32: the exact product (an int8 times a binary16 has at
  * most 19 significant bits); I6G_DTYPE_BF16: that product rounded to
  * bfloat16, nearest with ties to even (a NaN stays a NaN).  out_dev [rows, cols].
@@ -316,12 +326,13 @@ int i6g_unpack_int6(const uint8_t* packed_dev, int64_t n, int8_t* codes_dev, voi
 int i6g_dequantize_rows(const int8_t* codes_dev, const uint16_t* scales_dev, int64_t rows, int64_t cols,
                         int out_dtype, void* out_dev, void* stream);
 
-/* i6g_dequantize_int6_packed -- i6g_dequantize_rows with the codes read from
- * their packed form (the rows * cols codes of the matrix, row-major, packed
- * by i6g_pack_int6): the decode step of loading an artifact, without the
- * unpacked codes ever reaching memory.  Same results and errors. */
-int i6g_dequantize_int6_packed(const uint8_t* packed_dev, const uint16_t* scales_dev, int64_t rows,
-                               int64_t cols, int out_dtype, void* out_dev, void* stream);
+/* i6g_dequantize_packed -- i6g_dequantize_rows with the codes read from their
+ * packed form (bits 5 or 6: the rows * cols codes of the matrix, row-major,
+ * packed by i6g_pack_codes): the decode step of loading an artifact, without
+ * the unpacked codes ever reaching memory.  Same results; errors as
+ * i6g_dequantize_rows, and I6G_EINVAL for bits not in {5, 6}. */
+int i6g_dequantize_packed(const uint8_t* packed_dev, int bits, const uint16_t* scales_dev, int64_t rows,
+                          int64_t cols, int out_dtype, void* out_dev, void* stream);
 
 /* i6g_code_histogram -- counts of each int8 value among n codes:
  * hist_dev[v + 128] (int64 [256]).  accumulate = 0 overwrites the
@@ -339,14 +350,15 @@ int i6g_code_histogram(const int8_t* codes_dev, int64_t n, int accumulate, int64
 int i6g_code_entropy(const int64_t* hist_dev, double* bits_dev, void* stream);
 
 /* i6g_artifact_bytes -- host only: bytes of a packed artifact holding
- * n_mats int6 matrices (shapes[2 i] rows, shapes[2 i + 1] cols) at
- * 3 * ceil(rows * cols / 4) bytes of codes plus 2 bytes per row scale each,
- * and passthrough_elements binary16 values (2 bytes each).  Compare the
- * result with I6G_ARTIFACT_LIMIT.  Errors: I6G_EINVAL for a negative count
- * or size, or NULL shapes with n_mats > 0. */
+ * n_mats matrices (shapes[2 i] rows, shapes[2 i + 1] cols, bits[i] in
+ * {5, 6, 8}; bits may be NULL for all-int6): each its packed codes (int8 at
+ * one byte per code) plus 2 bytes per row scale, and passthrough_elements
+ * binary16 values (2 bytes each).  Compare the result with
+ * I6G_ARTIFACT_LIMIT.  Errors: I6G_EINVAL for a negative count or size, a
+ * bit width outside {5, 6, 8}, or NULL shapes with n_mats > 0. */
 #define I6G_ARTIFACT_LIMIT 16000000LL
-int i6g_artifact_bytes(const int64_t* shapes, int32_t n_mats, int64_t passthrough_elements,
-                       int64_t* bytes);
+int i6g_artifact_bytes(const int64_t* shapes, const int32_t* bits, int32_t n_mats,
+                       int64_t passthrough_elements, int64_t* bytes);
 
 #ifdef __cplusplus
 }

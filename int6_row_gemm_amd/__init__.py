@@ -25,7 +25,7 @@ EXPORTED = [
     "i6g_quantize_rows", "i6g_quantize_rows_many", "i6g_load_model", "i6g_score_tokens", "i6g_model_status",
     "i6g_free_model", "i6g_last_error", "i6g_plan_windows", "i6g_set_option",
     "i6g_set_timing", "i6g_get_timing",
-    "i6g_pack_int6", "i6g_unpack_int6", "i6g_dequantize_rows", "i6g_dequantize_int6_packed",
+    "i6g_pack_codes", "i6g_unpack_codes", "i6g_dequantize_rows", "i6g_dequantize_packed",
     "i6g_code_histogram", "i6g_code_entropy", "i6g_artifact_bytes",
 ]
 DTYPE_F32, DTYPE_BF16 = 1, 2
@@ -95,13 +95,13 @@ def lib():
         L.i6g_set_option.argtypes = [vp, ctypes.c_int, i64]
         L.i6g_set_timing.argtypes = [vp, ctypes.c_int, ctypes.c_uint32]
         L.i6g_get_timing.argtypes = [vp, ctypes.c_int, vp, vp, vp, vp]
-        L.i6g_pack_int6.argtypes = [vp, i64, vp, vp, vp]
-        L.i6g_unpack_int6.argtypes = [vp, i64, vp, vp]
+        L.i6g_pack_codes.argtypes = [vp, i64, ctypes.c_int, vp, vp, vp]
+        L.i6g_unpack_codes.argtypes = [vp, i64, ctypes.c_int, vp, vp]
         L.i6g_dequantize_rows.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp, vp]
-        L.i6g_dequantize_int6_packed.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp, vp]
+        L.i6g_dequantize_packed.argtypes = [vp, ctypes.c_int, vp, i64, i64, ctypes.c_int, vp, vp]
         L.i6g_code_histogram.argtypes = [vp, i64, ctypes.c_int, vp, vp]
         L.i6g_code_entropy.argtypes = [vp, vp, vp]
-        L.i6g_artifact_bytes.argtypes = [vp, i32, i64, vp]
+        L.i6g_artifact_bytes.argtypes = [vp, vp, i32, i64, vp]
         _lib = L
     return _lib
 
@@ -293,6 +293,13 @@ class Model:
         return ms.value, n.value, fl.value, by.value
 
 
+def matrix_bits(arch, name):
+    """Bits of one block matrix: ``bits_attn`` for q, k, v, o and ``bits_mlp``
+    for fc, proj when the arch gives them (mixed int5 / int6), else ``bits``."""
+    key = "bits_attn" if name in ("q", "k", "v", "o") else "bits_mlp"
+    return int(arch.get(key) or arch["bits"])
+
+
 def quantize_model(model, flags=None):
     """Quantise every block matrix of a synthetic model on the GPU; returns
     a list of dicts name -> (codes, scales) of device tensors."""
@@ -303,7 +310,7 @@ def quantize_model(model, flags=None):
         qb = {}
         for name, w in blk.items():
             wt = _dev(w, torch.float32)
-            qb[name] = quantize_rows(wt, arch["bits"], arch["clip_q"], flags)
+            qb[name] = quantize_rows(wt, matrix_bits(arch, name), arch["clip_q"], flags)
         out.append(qb)
     return out
 
@@ -315,38 +322,44 @@ def load(model, qblocks):
 
 
 # ---------------------------------------------------------------------------
-# Export side: 6-bit packing, dequantisation and code statistics.
+# Export side: bit packing, dequantisation and code statistics.
 
-def packed_size(n):
-    """Bytes of n packed int6 codes (3 per group of 4, the last group padded)."""
-    return 3 * ((n + 3) // 4)
+def packed_size(n, bits=6):
+    """Bytes of n packed codes: 3 per 4 int6 codes, 5 per 8 int5 codes (the
+    last word padded)."""
+    if bits == 6:
+        return 3 * ((n + 3) // 4)
+    if bits == 5:
+        return 5 * ((n + 7) // 8)
+    raise ValueError("bits must be 5 or 6")
 
 
-def pack_int6(codes, flags=None, out=None):
-    """Pack a device int8 tensor of int6 codes (flattened) into a uint8 tensor
-    of packed_size(numel) bytes."""
+def pack_codes(codes, bits=6, flags=None, out=None):
+    """Pack a device int8 tensor of int6 or int5 codes (flattened) into a
+    uint8 tensor of packed_size(numel, bits) bytes."""
     import torch
     if not (codes.is_cuda and codes.dtype == torch.int8 and codes.is_contiguous()):
         raise ValueError("codes must be a contiguous int8 CUDA tensor")
     n = codes.numel()
+    size = packed_size(n, bits)
     if out is None:
-        out = torch.empty(packed_size(n), dtype=torch.uint8, device=codes.device)
-    if out.numel() < packed_size(n):
+        out = torch.empty(size, dtype=torch.uint8, device=codes.device)
+    if out.numel() < size:
         raise ValueError("out is too small")
-    _check(lib().i6g_pack_int6(_ptr(codes), n, _ptr(out), _ptr(flags), _stream()))
+    _check(lib().i6g_pack_codes(_ptr(codes), n, bits, _ptr(out), _ptr(flags), _stream()))
     return out
 
 
-def unpack_int6(packed, n, out=None):
+def unpack_codes(packed, n, bits=6, out=None):
     """The first n codes held in a packed uint8 device tensor -> int8 [n]."""
     import torch
     if not (packed.is_cuda and packed.dtype == torch.uint8 and packed.is_contiguous()):
         raise ValueError("packed must be a contiguous uint8 CUDA tensor")
-    if packed.numel() < packed_size(n):
+    if packed.numel() < packed_size(n, bits):
         raise ValueError("packed holds fewer than n codes")
     if out is None:
         out = torch.empty(n, dtype=torch.int8, device=packed.device)
-    _check(lib().i6g_unpack_int6(_ptr(packed), n, _ptr(out), _stream()))
+    _check(lib().i6g_unpack_codes(_ptr(packed), n, bits, _ptr(out), _stream()))
     return out
 
 
@@ -375,19 +388,19 @@ def dequantize(codes, scales, dtype=None):
     return out
 
 
-def dequantize_packed(packed, scales, rows, cols, dtype=None):
-    """dequantize() of a [rows, cols] int6 matrix given in packed form."""
+def dequantize_packed(packed, scales, rows, cols, dtype=None, bits=6):
+    """dequantize() of a [rows, cols] int6 or int5 matrix given in packed form."""
     import torch
     dtype = dtype or torch.float32
     if not (packed.is_cuda and packed.dtype == torch.uint8 and packed.is_contiguous()):
         raise ValueError("packed must be a contiguous uint8 CUDA tensor")
-    if packed.numel() < packed_size(rows * cols):
+    if packed.numel() < packed_size(rows * cols, bits):
         raise ValueError("packed holds fewer than rows * cols codes")
     if scales.numel() != rows or scales.element_size() != 2 or not scales.is_contiguous():
         raise ValueError("scales must hold one binary16 value per row")
     out = torch.empty((rows, cols), dtype=dtype, device=packed.device)
-    _check(lib().i6g_dequantize_int6_packed(_ptr(packed), _ptr(scales), rows, cols, _dq_dtype(dtype),
-                                            _ptr(out), _stream()))
+    _check(lib().i6g_dequantize_packed(_ptr(packed), bits, _ptr(scales), rows, cols, _dq_dtype(dtype),
+                                       _ptr(out), _stream()))
     return out
 
 
@@ -416,46 +429,59 @@ def code_entropy(hist):
     return out
 
 
-def artifact_bytes(shapes, passthrough_elements=0):
-    """Bytes of a packed artifact of int6 matrices with the given (rows, cols)
-    shapes, each with binary16 row scales, plus binary16 passthrough values."""
+def artifact_bytes(shapes, passthrough_elements=0, bits=None):
+    """Bytes of a packed artifact of matrices with the given (rows, cols)
+    shapes and bit widths (default int6), each with binary16 row scales,
+    plus binary16 passthrough values."""
     arr = np.ascontiguousarray(np.asarray(shapes, dtype=np.int64).reshape(-1, 2))
+    b = None if bits is None else np.ascontiguousarray(np.asarray(bits, dtype=np.int32))
+    if b is not None and len(b) != len(arr):
+        raise ValueError("one bit width per matrix")
     out = ctypes.c_int64(0)
-    _check(lib().i6g_artifact_bytes(arr.ctypes.data if len(arr) else None, len(arr),
+    _check(lib().i6g_artifact_bytes(arr.ctypes.data if len(arr) else None,
+                                    b.ctypes.data if b is not None and len(b) else None, len(arr),
                                     int(passthrough_elements), ctypes.byref(out)))
     return out.value
 
 
-def export_model(qblocks, passthrough_elements=0):
-    """Pack every int6 block matrix of a quantised model and measure its codes.
-    Returns a dict with ``packed`` (list of dicts name -> (packed, scales,
-    shape)), ``hist`` (int64 [256] over all codes), ``entropy_bits`` (device
-    float64 [1]) and ``bytes`` (the artifact size)."""
+def export_model(qblocks, arch, passthrough_elements=0):
+    """Pack every block matrix of a quantised model at its bit width
+    (matrix_bits) and measure its codes.  Returns a dict with ``packed``
+    (list of dicts name -> (packed, scales, shape, bits)), ``hist`` (int64
+    [256] over all codes), ``entropy_bits`` (device float64 [1]) and
+    ``bytes`` (the artifact size)."""
     import torch
-    packed, shapes, hist = [], [], None
-    flags = None
+    packed, shapes, widths, hist, flags = [], [], [], None, None
     for qb in qblocks:
         pb = {}
         for name, (codes, scales) in qb.items():
+            b = matrix_bits(arch, name)
             if flags is None:
                 flags = torch.zeros(1, dtype=torch.int32, device=codes.device)
-            pb[name] = (pack_int6(codes, flags), scales, tuple(codes.shape))
+            if b == 8:
+                pb[name] = (codes.reshape(-1).view(torch.uint8).clone(), scales, tuple(codes.shape), b)
+            else:
+                pb[name] = (pack_codes(codes, b, flags), scales, tuple(codes.shape), b)
             hist = code_histogram(codes, hist, accumulate=hist is not None)
             shapes.append(codes.shape)
+            widths.append(b)
         packed.append(pb)
     if flags is not None and int(flags.item()) & FLAG_CODE:
-        raise I6GError(-1, "a block matrix holds a code that is not int6")
+        raise I6GError(-1, "a block matrix holds a code outside its format")
     return {"packed": packed, "hist": hist, "entropy_bits": code_entropy(hist),
-            "bytes": artifact_bytes(shapes, passthrough_elements)}
+            "bytes": artifact_bytes(shapes, passthrough_elements, widths)}
 
 
 def import_model(packed):
-    """Unpack the int6 codes of export_model()'s ``packed`` list; returns the
+    """Unpack the codes of export_model()'s ``packed`` list; returns the
     qblocks list (dicts name -> (codes, scales)) that load() takes."""
+    import torch
     out = []
     for pb in packed:
         qb = {}
-        for name, (p, scales, shape) in pb.items():
-            qb[name] = (unpack_int6(p, shape[0] * shape[1]).view(shape), scales)
+        for name, (p, scales, shape, b) in pb.items():
+            n = shape[0] * shape[1]
+            codes = p.view(torch.int8).clone() if b == 8 else unpack_codes(p, n, b)
+            qb[name] = (codes.view(shape), scales)
         out.append(qb)
     return out

@@ -257,7 +257,7 @@ static int quant_plan(const char* who, const void* w, const void* codes, const v
                       float* frac) {
   if (!w || !codes || !scales) return fail(I6G_EINVAL, "%s: NULL array", who);
   if (rows < 1 || cols < 1) return fail(I6G_EINVAL, "%s: rows and cols must be >= 1", who);
-  if (bits != 6 && bits != 8) return fail(I6G_EINVAL, "%s: bits must be 6 or 8", who);
+  if (bits != 5 && bits != 6 && bits != 8) return fail(I6G_EINVAL, "%s: bits must be 5, 6 or 8", who);
   if (!(clip_quantile > 0.0 && clip_quantile <= 1.0))
     return fail(I6G_EINVAL, "%s: clip_quantile must be in (0, 1]", who);
   if (cols > 65536) return fail(I6G_EUNSUPPORTED, "%s: cols > 65536", who);
@@ -323,46 +323,54 @@ int i6g_quantize_rows_many(const i6g_quant_job* jobs, int32_t n_jobs, int bits, 
 
 static bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-int i6g_pack_int6(const int8_t* codes_dev, int64_t n, uint8_t* packed_dev, int32_t* flags_dev, void* stream) {
-  if (n < 0 || (n > 0 && (!codes_dev || !packed_dev))) return fail(I6G_EINVAL, "pack_int6: n < 0 or NULL buffer");
+static int64_t packed_bytes(int64_t n, int bits) {
+  return bits == 6 ? 3 * ((n + 3) / 4) : bits == 5 ? 5 * ((n + 7) / 8) : n;
+}
+
+int i6g_pack_codes(const int8_t* codes_dev, int64_t n, int bits, uint8_t* packed_dev, int32_t* flags_dev,
+                   void* stream) {
+  if (bits != 5 && bits != 6) return fail(I6G_EINVAL, "pack_codes: bits must be 5 or 6");
+  if (n < 0 || (n > 0 && (!codes_dev || !packed_dev))) return fail(I6G_EINVAL, "pack_codes: n < 0 or NULL buffer");
   if (n == 0) return I6G_OK;
   if (!aligned(codes_dev, 16) || !aligned(packed_dev, 4))
-    return fail(I6G_EUNSUPPORTED, "pack_int6: codes must be 16-byte and packed 4-byte aligned");
-  HIP_TRY(launch_pack_int6(codes_dev, n, packed_dev, flags_dev, (hipStream_t)stream));
+    return fail(I6G_EUNSUPPORTED, "pack_codes: codes must be 16-byte and packed 4-byte aligned");
+  HIP_TRY(launch_pack_codes(codes_dev, n, bits, packed_dev, flags_dev, (hipStream_t)stream));
   return I6G_OK;
 }
 
-int i6g_unpack_int6(const uint8_t* packed_dev, int64_t n, int8_t* codes_dev, void* stream) {
-  if (n < 0 || (n > 0 && (!codes_dev || !packed_dev))) return fail(I6G_EINVAL, "unpack_int6: n < 0 or NULL buffer");
+int i6g_unpack_codes(const uint8_t* packed_dev, int64_t n, int bits, int8_t* codes_dev, void* stream) {
+  if (bits != 5 && bits != 6) return fail(I6G_EINVAL, "unpack_codes: bits must be 5 or 6");
+  if (n < 0 || (n > 0 && (!codes_dev || !packed_dev))) return fail(I6G_EINVAL, "unpack_codes: n < 0 or NULL buffer");
   if (n == 0) return I6G_OK;
   if (!aligned(codes_dev, 16) || !aligned(packed_dev, 4))
-    return fail(I6G_EUNSUPPORTED, "unpack_int6: codes must be 16-byte and packed 4-byte aligned");
-  HIP_TRY(launch_unpack_int6(packed_dev, n, codes_dev, (hipStream_t)stream));
+    return fail(I6G_EUNSUPPORTED, "unpack_codes: codes must be 16-byte and packed 4-byte aligned");
+  HIP_TRY(launch_unpack_codes(packed_dev, n, bits, codes_dev, (hipStream_t)stream));
   return I6G_OK;
 }
 
-static int dequant(const char* who, const void* src, bool packed, const uint16_t* scales_dev, int64_t rows,
+static int dequant(const char* who, const void* src, int bits, const uint16_t* scales_dev, int64_t rows,
                    int64_t cols, int out_dtype, void* out_dev, void* stream) {
   if (rows < 0 || cols < 0) return fail(I6G_EINVAL, "%s: rows and cols must be >= 0", who);
   if (out_dtype != I6G_DTYPE_F32 && out_dtype != I6G_DTYPE_BF16)
     return fail(I6G_EINVAL, "%s: out_dtype must be I6G_DTYPE_F32 or I6G_DTYPE_BF16", who);
   if (rows == 0 || cols == 0) return I6G_OK;
   if (!src || !scales_dev || !out_dev) return fail(I6G_EINVAL, "%s: NULL buffer", who);
-  if (!aligned(src, packed ? 4 : 16) || !aligned(out_dev, 16) || !aligned(scales_dev, 2))
+  if (!aligned(src, bits == 8 ? 16 : 4) || !aligned(out_dev, 16) || !aligned(scales_dev, 2))
     return fail(I6G_EUNSUPPORTED, "%s: misaligned buffer", who);
-  HIP_TRY(launch_dequantize(src, packed, scales_dev, rows, cols, out_dtype == I6G_DTYPE_BF16, out_dev,
+  HIP_TRY(launch_dequantize(src, bits, scales_dev, rows, cols, out_dtype == I6G_DTYPE_BF16, out_dev,
                             (hipStream_t)stream));
   return I6G_OK;
 }
 
 int i6g_dequantize_rows(const int8_t* codes_dev, const uint16_t* scales_dev, int64_t rows, int64_t cols,
                         int out_dtype, void* out_dev, void* stream) {
-  return dequant("dequantize_rows", codes_dev, false, scales_dev, rows, cols, out_dtype, out_dev, stream);
+  return dequant("dequantize_rows", codes_dev, 8, scales_dev, rows, cols, out_dtype, out_dev, stream);
 }
 
-int i6g_dequantize_int6_packed(const uint8_t* packed_dev, const uint16_t* scales_dev, int64_t rows,
-                               int64_t cols, int out_dtype, void* out_dev, void* stream) {
-  return dequant("dequantize_int6_packed", packed_dev, true, scales_dev, rows, cols, out_dtype, out_dev, stream);
+int i6g_dequantize_packed(const uint8_t* packed_dev, int bits, const uint16_t* scales_dev, int64_t rows,
+                          int64_t cols, int out_dtype, void* out_dev, void* stream) {
+  if (bits != 5 && bits != 6) return fail(I6G_EINVAL, "dequantize_packed: bits must be 5 or 6");
+  return dequant("dequantize_packed", packed_dev, bits, scales_dev, rows, cols, out_dtype, out_dev, stream);
 }
 
 int i6g_code_histogram(const int8_t* codes_dev, int64_t n, int accumulate, int64_t* hist_dev, void* stream) {
@@ -378,14 +386,17 @@ int i6g_code_entropy(const int64_t* hist_dev, double* bits_dev, void* stream) {
   return I6G_OK;
 }
 
-int i6g_artifact_bytes(const int64_t* shapes, int32_t n_mats, int64_t passthrough_elements, int64_t* bytes) {
+int i6g_artifact_bytes(const int64_t* shapes, const int32_t* bits, int32_t n_mats, int64_t passthrough_elements,
+                       int64_t* bytes) {
   if (!bytes || n_mats < 0 || passthrough_elements < 0 || (n_mats > 0 && !shapes))
     return fail(I6G_EINVAL, "artifact_bytes: negative count or NULL array");
   int64_t total = 2 * passthrough_elements;
   for (int32_t i = 0; i < n_mats; ++i) {
     const int64_t r = shapes[2 * i], c = shapes[2 * i + 1];
+    const int b = bits ? bits[i] : 6;
     if (r < 0 || c < 0) return fail(I6G_EINVAL, "artifact_bytes: matrix %d has a negative size", i);
-    total += 3 * ((r * c + 3) / 4) + 2 * r;
+    if (b != 5 && b != 6 && b != 8) return fail(I6G_EINVAL, "artifact_bytes: matrix %d: bits must be 5, 6 or 8", i);
+    total += packed_bytes(r * c, b) + 2 * r;
   }
   *bytes = total;
   return I6G_OK;

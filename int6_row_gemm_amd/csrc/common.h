@@ -16,8 +16,8 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
-// Device flag bit set by the packer for a byte that is not an int6 code
-// (a multiple of 4); equals I6G_FLAG_CODE of the C ABI.
+// Device flag bit set by the packer for a byte that is not a code of the
+// format being packed; equals I6G_FLAG_CODE of the C ABI.
 constexpr int32_t kFlagCode = 8;
 
 // ---------------------------------------------------------------------------
@@ -183,13 +183,15 @@ hipError_t launch_f16_to_f32(const uint16_t* in, float* out, int64_t n, hipStrea
 hipError_t launch_f32_to_f16(const float* in, _Float16* out, int64_t n, hipStream_t s);
 
 // ---------------------------------------------------------------------------
-// Export side: 6-bit packing of int6 codes (3 bytes per 4 codes), its
-// inverse, dequantisation (from codes or packed bytes) to fp32 or bfloat16,
-// and the code histogram / entropy.  Code and output pointers must be 16-byte
-// aligned, packed pointers 4-byte aligned (checked by the callers).
-hipError_t launch_pack_int6(const int8_t* codes, int64_t n, uint8_t* packed, int32_t* flags, hipStream_t s);
-hipError_t launch_unpack_int6(const uint8_t* packed, int64_t n, int8_t* codes, hipStream_t s);
-hipError_t launch_dequantize(const void* src, bool packed, const uint16_t* scales, int64_t rows, int64_t cols,
+// Export side: bit packing of int6 codes (3 bytes per 4) and int5 codes (5
+// bytes per 8), its inverse, dequantisation (from int8 codes, bits = 8, or
+// packed codes) to fp32 or bfloat16, and the code histogram / entropy.  Code
+// and output pointers must be 16-byte aligned, packed pointers 4-byte
+// aligned (checked by the callers).
+hipError_t launch_pack_codes(const int8_t* codes, int64_t n, int bits, uint8_t* packed, int32_t* flags,
+                             hipStream_t s);
+hipError_t launch_unpack_codes(const uint8_t* packed, int64_t n, int bits, int8_t* codes, hipStream_t s);
+hipError_t launch_dequantize(const void* src, int bits, const uint16_t* scales, int64_t rows, int64_t cols,
                              bool bf16_out, void* out, hipStream_t s);
 hipError_t launch_code_histogram(const int8_t* codes, int64_t n, bool accumulate, int64_t* hist, hipStream_t s);
 hipError_t launch_code_entropy(const int64_t* hist, double* out, hipStream_t s);

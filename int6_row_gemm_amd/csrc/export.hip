@@ -1,23 +1,28 @@
-// Export side of the int6 format: 6-bit packing, unpacking, dequantisation
-// and code statistics.
+// Export side of the int6 / int5 formats: bit packing, unpacking,
+// dequantisation and code statistics.
 //
 // kwkr.cn write-up of parameter-golf PR #363, timeline and run notes: the
-// int6 codes are measured by their entropy (bits per value) and compressed
-// (bit packing among the methods tried) into an artifact of at most
-// 16,000,000 bytes, which is dequantised and evaluated again.  pwwt.cn
-// "parameter-golf 16MB 极限压缩实战 …", 后训练量化导出: codes are int8
-// multiples of 4 in [-128, 124] with one binary16 scale per row.
+// codes are measured by their entropy (bits per value) and compressed (bit
+// packing among the methods tried) into an artifact of at most 16,000,000
+// bytes, which is dequantised and evaluated again; its run commands export
+// int5 matrices (MLP_INT5, ATTN_INT5).  pwwt.cn "parameter-golf 16MB 极限压缩
+// 实战 …", 后训练量化导出: int6 codes are int8 multiples of 4 in
+// [-128, 124] with one binary16 scale per row.
 //
-// Packed format: code c -> u = c/4 + 32 in [0, 63]; four codes u0..u3 make
-// the 24-bit word u0 | u1 << 6 | u2 << 12 | u3 << 18, stored as 3 bytes,
-// least significant first; a tail of fewer than four codes is padded with
-// code 0.
+// Packed formats, least significant bit first:
+//   int6: code c -> u = c/4 + 32 (6 bits); 4 codes -> 3 bytes;
+//   int5: code c -> u = c + 16 (5 bits);   8 codes -> 5 bytes;
+// a tail shorter than a word is padded with code 0.
 //
-// All kernels are bound by HBM traffic.  A thread moves 16 codes (one 16-byte
-// load or store of codes, 12 bytes of packed data) per group and each thread
-// issues its kU groups' loads before using any, so that enough bytes are in
-// flight to cover HBM latency.  The last, partial group of a buffer is done
-// by the thread whose group index is the group count.
+// All kernels are bound by HBM traffic.  A thread moves one group of codes
+// per step (16 int6 codes = one 16-byte load and 12 packed bytes; 32 int5
+// codes = two 16-byte loads and 20 packed bytes; 16 int8 codes for the
+// dequantisation of unpacked codes) and issues its kU groups' loads before
+// using any, so that enough bytes are in flight to cover HBM latency (the
+// registers are zeroed first: without that the compiler waits for each
+// group's load before issuing the next).  The
+// last, partial group of a buffer is done one word at a time by the thread
+// whose group index is the group count.
 #include "common.h"
 
 namespace i6g {
@@ -28,18 +33,105 @@ constexpr int kThreads = 256;   // threads per workgroup
 constexpr int64_t kGroupsPerBlock = (int64_t)kU * kThreads;
 constexpr int kHistParts = 64;  // partial histograms (see hist_kernel)
 
-// Four codes, one per byte of x, -> their 24-bit packed word.  For a code
-// c = 4t (t in [-32, 31]) bits 2..7 of the byte are t in 6-bit two's
+// Group and word geometry of each code format (8: unpacked int8 codes).
+template <int BITS> struct Fmt;
+template <> struct Fmt<6> { static constexpr int G = 16, PB = 12, WC = 4, WB = 3; };
+template <> struct Fmt<5> { static constexpr int G = 32, PB = 20, WC = 8, WB = 5; };
+template <> struct Fmt<8> { static constexpr int G = 16, PB = 16, WC = 1, WB = 1; };
+
+// --- int6: four codes, one per byte of x, <-> a 24-bit packed word.  For a
+// code c = 4t (t in [-32, 31]) bits 2..7 of the byte are t in 6-bit two's
 // complement, and t + 32 mod 64 flips its top bit.
-__device__ inline uint32_t pack4(uint32_t x) {
+__device__ inline uint32_t pack6x4(uint32_t x) {
   const uint32_t y = ((x >> 2) & 0x3F3F3F3Fu) ^ 0x20202020u;
   return (y & 0x3Fu) | ((y >> 2) & 0xFC0u) | ((y >> 4) & 0x3F000u) | ((y >> 6) & 0xFC0000u);
 }
-
-// The inverse: a 24-bit packed word -> four codes, one per byte.
-__device__ inline uint32_t unpack4(uint32_t w) {
+__device__ inline uint32_t unpack6x4(uint32_t w) {
   const uint32_t y = (w & 0x3Fu) | ((w << 2) & 0x3F00u) | ((w << 4) & 0x3F0000u) | ((w << 6) & 0x3F000000u);
   return (y ^ 0x20202020u) << 2;
+}
+// a byte is an int6 code iff its low two bits are clear
+__device__ inline bool bad6(uint32_t x) { return (x & 0x03030303u) != 0; }
+
+// --- int5: four codes <-> a 20-bit word.  The low 5 bits of a code in
+// [-16, 15] are its 5-bit two's complement; + 16 mod 32 flips bit 4.
+__device__ inline uint32_t pack5x4(uint32_t x) {
+  const uint32_t y = (x ^ 0x10101010u) & 0x1F1F1F1Fu;
+  return (y & 0x1Fu) | ((y >> 3) & 0x3E0u) | ((y >> 6) & 0x7C00u) | ((y >> 9) & 0xF8000u);
+}
+__device__ inline uint32_t unpack5x4(uint32_t w) {
+  const uint32_t y = (w & 0x1Fu) | ((w << 3) & 0x1F00u) | ((w << 6) & 0x1F0000u) | ((w << 9) & 0x1F000000u);
+  const uint32_t v = y ^ 0x10101010u;       // 5-bit two's complement per byte
+  return v | ((v & 0x10101010u) * 14u);     // sign-extend: bit 4 -> bits 5..7
+}
+// a byte is an int5 code iff its bits 4..7 are equal
+__device__ inline bool bad5(uint32_t x) { return ((x ^ (x << 1)) & 0xE0E0E0E0u) != 0; }
+
+// A group's codes (G/4 words of 4 codes) -> its packed words (PB/4).
+__device__ inline void pack_group(const uint32_t (&c)[4], uint32_t (&p)[3]) {
+  const uint32_t w0 = pack6x4(c[0]), w1 = pack6x4(c[1]), w2 = pack6x4(c[2]), w3 = pack6x4(c[3]);
+  p[0] = w0 | (w1 << 24);
+  p[1] = (w1 >> 8) | (w2 << 16);
+  p[2] = (w2 >> 16) | (w3 << 8);
+}
+__device__ inline void unpack_group(const uint32_t (&p)[3], uint32_t (&c)[4]) {
+  c[0] = unpack6x4(p[0] & 0xFFFFFFu);
+  c[1] = unpack6x4((p[0] >> 24) | ((p[1] & 0xFFFFu) << 8));
+  c[2] = unpack6x4((p[1] >> 16) | ((p[2] & 0xFFu) << 16));
+  c[3] = unpack6x4(p[2] >> 8);
+}
+__device__ inline uint64_t pack5x8(uint32_t lo, uint32_t hi) {
+  return (uint64_t)pack5x4(lo) | ((uint64_t)pack5x4(hi) << 20);
+}
+__device__ inline void pack_group(const uint32_t (&c)[8], uint32_t (&p)[5]) {
+  const uint64_t q0 = pack5x8(c[0], c[1]), q1 = pack5x8(c[2], c[3]);
+  const uint64_t q2 = pack5x8(c[4], c[5]), q3 = pack5x8(c[6], c[7]);
+  p[0] = (uint32_t)q0;
+  p[1] = (uint32_t)(q0 >> 32) | (uint32_t)(q1 << 8);
+  p[2] = (uint32_t)(q1 >> 24) | (uint32_t)(q2 << 16);
+  p[3] = (uint32_t)(q2 >> 16) | (uint32_t)(q3 << 24);
+  p[4] = (uint32_t)(q3 >> 8);
+}
+__device__ inline void unpack_group(const uint32_t (&p)[5], uint32_t (&c)[8]) {
+  const uint64_t q[4] = {
+      (uint64_t)p[0] | ((uint64_t)(p[1] & 0xFFu) << 32),
+      (uint64_t)(p[1] >> 8) | ((uint64_t)(p[2] & 0xFFFFu) << 24),
+      (uint64_t)(p[2] >> 16) | ((uint64_t)(p[3] & 0xFFFFFFu) << 16),
+      (uint64_t)(p[3] >> 24) | ((uint64_t)p[4] << 8)};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[2 * j] = unpack5x4((uint32_t)q[j] & 0xFFFFFu);
+    c[2 * j + 1] = unpack5x4((uint32_t)(q[j] >> 20) & 0xFFFFFu);
+  }
+}
+
+// One word (WC codes in the low bytes of a uint64, WB packed bytes) of the
+// tail, for formats 6 and 5.
+template <int BITS> __device__ inline uint64_t pack_word(uint64_t codes);
+template <> __device__ inline uint64_t pack_word<6>(uint64_t c) { return pack6x4((uint32_t)c); }
+template <> __device__ inline uint64_t pack_word<5>(uint64_t c) { return pack5x8((uint32_t)c, (uint32_t)(c >> 32)); }
+template <int BITS> __device__ inline uint64_t unpack_word(uint64_t w);
+template <> __device__ inline uint64_t unpack_word<6>(uint64_t w) { return unpack6x4((uint32_t)w); }
+template <> __device__ inline uint64_t unpack_word<5>(uint64_t w) {
+  return (uint64_t)unpack5x4((uint32_t)w & 0xFFFFFu) | ((uint64_t)unpack5x4((uint32_t)(w >> 20) & 0xFFFFFu) << 32);
+}
+template <int BITS> __device__ inline bool bad_word(uint32_t x);
+template <> __device__ inline bool bad_word<6>(uint32_t x) { return bad6(x); }
+template <> __device__ inline bool bad_word<5>(uint32_t x) { return bad5(x); }
+
+// Tail word j: codes idx0 .. idx0 + WC - 1 (those below n), zero padded.
+template <int BITS>
+__device__ inline uint64_t gather_codes(const int8_t* codes, int64_t idx0, int64_t n) {
+  uint64_t x = 0;
+  for (int b = 0; b < Fmt<BITS>::WC; ++b)
+    if (idx0 + b < n) x |= (uint64_t)(uint8_t)codes[idx0 + b] << (8 * b);
+  return x;
+}
+template <int BITS>
+__device__ inline uint64_t gather_packed(const uint8_t* p) {
+  uint64_t w = 0;
+  for (int b = 0; b < Fmt<BITS>::WB; ++b) w |= (uint64_t)p[b] << (8 * b);
+  return w;
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -54,125 +146,135 @@ __device__ inline uint32_t bf16x2_rne(float a, float b) {
 
 __device__ inline float f16_bits_to_float(uint16_t s) { return (float)__builtin_bit_cast(_Float16, s); }
 
-// Codes of a partial last group (idx0 .. n-1, fewer than 16), padded with 0.
-__device__ inline uint32_t tail_word(const int8_t* codes, int64_t idx0, int64_t n, int& bad) {
-  uint32_t x = 0;
-  for (int b = 0; b < 4; ++b) {
-    if (idx0 + b < n) {
-      const uint32_t byte = (uint8_t)codes[idx0 + b];
-      bad |= (byte & 3u) != 0;
-      x |= byte << (8 * b);
+// Loads of group g: NW 32-bit words at byte offset NW * 4 * g (16-byte loads
+// where NW is a multiple of 4).
+template <int NW>
+__device__ inline void load_words(const void* base, int64_t g, uint32_t (&d)[NW]) {
+  const uint32_t* p = reinterpret_cast<const uint32_t*>(base) + NW * g;
+  if (NW % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+      d[4 * i] = v.x; d[4 * i + 1] = v.y; d[4 * i + 2] = v.z; d[4 * i + 3] = v.w;
     }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) d[i] = p[i];
   }
-  return x;
+}
+template <int NW>
+__device__ inline void store_words(void* base, int64_t g, const uint32_t (&d)[NW]) {
+  uint32_t* p = reinterpret_cast<uint32_t*>(base) + NW * g;
+  if (NW % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i)
+      reinterpret_cast<uint4*>(p)[i] = make_uint4(d[4 * i], d[4 * i + 1], d[4 * i + 2], d[4 * i + 3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) p[i] = d[i];
+  }
 }
 
-__device__ inline uint32_t load_packed_word(const uint8_t* p) {
-  return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16);
-}
-
+template <int BITS>
 __global__ __launch_bounds__(kThreads) void pack_kernel(const int8_t* codes, int64_t n, uint8_t* packed,
                                                         int32_t* flags) {
-  const int64_t n16 = n >> 4;
+  using F = Fmt<BITS>;
+  const int64_t ng = n / F::G;
   const int64_t gb = blockIdx.x * kGroupsPerBlock + threadIdx.x;
-  int bad = 0;
-  uint4 x[kU];
+  bool bad = false;
+  uint32_t c[kU][F::G / 4];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const int64_t g = gb + u * kThreads;
-    x[u] = g < n16 ? reinterpret_cast<const uint4*>(codes)[g] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < F::G / 4; ++i) c[u][i] = 0;
+    if (g < ng) load_words<F::G / 4>(codes, g, c[u]);
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const int64_t g = gb + u * kThreads;
-    if (g < n16) {
-      bad |= ((x[u].x | x[u].y | x[u].z | x[u].w) & 0x03030303u) != 0;
-      const uint32_t w0 = pack4(x[u].x), w1 = pack4(x[u].y), w2 = pack4(x[u].z), w3 = pack4(x[u].w);
-      uint32_t* o = reinterpret_cast<uint32_t*>(packed + 12 * g);
-      o[0] = w0 | (w1 << 24);
-      o[1] = (w1 >> 8) | (w2 << 16);
-      o[2] = (w2 >> 16) | (w3 << 8);
-    } else if (g == n16 && (n & 15)) {
-      for (int64_t j = 0; 16 * n16 + 4 * j < n; ++j) {
-        const uint32_t w = pack4(tail_word(codes, 16 * n16 + 4 * j, n, bad));
-        uint8_t* o = packed + 12 * n16 + 3 * j;
-        o[0] = w & 0xFF;
-        o[1] = (w >> 8) & 0xFF;
-        o[2] = w >> 16;
+    if (g < ng) {
+      uint32_t p[F::PB / 4];
+#pragma unroll
+      for (int i = 0; i < F::G / 4; ++i) bad |= bad_word<BITS>(c[u][i]);
+      pack_group(c[u], p);
+      store_words<F::PB / 4>(packed, g, p);
+    } else if (g == ng && n % F::G) {
+      for (int64_t j = 0; F::G * ng + F::WC * j < n; ++j) {
+        const int64_t idx0 = F::G * ng + F::WC * j;
+        const uint64_t x = gather_codes<BITS>(codes, idx0, n);
+        bad |= bad_word<BITS>((uint32_t)x) || bad_word<BITS>((uint32_t)(x >> 32));
+        const uint64_t w = pack_word<BITS>(x);
+        uint8_t* o = packed + F::PB * ng + F::WB * j;
+        for (int b = 0; b < F::WB; ++b) o[b] = (uint8_t)(w >> (8 * b));
       }
     }
   }
   if (bad && flags) atomicOr(flags, kFlagCode);
 }
 
+template <int BITS>
 __global__ __launch_bounds__(kThreads) void unpack_kernel(const uint8_t* packed, int64_t n, int8_t* codes) {
-  const int64_t n16 = n >> 4;
+  using F = Fmt<BITS>;
+  const int64_t ng = n / F::G;
   const int64_t gb = blockIdx.x * kGroupsPerBlock + threadIdx.x;
-  uint32_t d[kU][3];
+  uint32_t p[kU][F::PB / 4];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const int64_t g = gb + u * kThreads;
-    d[u][0] = d[u][1] = d[u][2] = 0;
-    if (g < n16) {
-      const uint32_t* p = reinterpret_cast<const uint32_t*>(packed + 12 * g);
-      d[u][0] = p[0]; d[u][1] = p[1]; d[u][2] = p[2];
-    }
+#pragma unroll
+    for (int i = 0; i < F::PB / 4; ++i) p[u][i] = 0;
+    if (g < ng) load_words<F::PB / 4>(packed, g, p[u]);
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const int64_t g = gb + u * kThreads;
-    if (g < n16) {
-      uint4 x;
-      x.x = unpack4(d[u][0] & 0xFFFFFFu);
-      x.y = unpack4((d[u][0] >> 24) | ((d[u][1] & 0xFFFFu) << 8));
-      x.z = unpack4((d[u][1] >> 16) | ((d[u][2] & 0xFFu) << 16));
-      x.w = unpack4(d[u][2] >> 8);
-      reinterpret_cast<uint4*>(codes)[g] = x;
-    } else if (g == n16 && (n & 15)) {
-      for (int64_t j = 0; 16 * n16 + 4 * j < n; ++j) {
-        const uint32_t x = unpack4(load_packed_word(packed + 12 * n16 + 3 * j));
-        for (int b = 0; b < 4; ++b) {
-          const int64_t idx = 16 * n16 + 4 * j + b;
-          if (idx < n) codes[idx] = (int8_t)((x >> (8 * b)) & 0xFF);
+    if (g < ng) {
+      uint32_t c[F::G / 4];
+      unpack_group(p[u], c);
+      store_words<F::G / 4>(codes, g, c);
+    } else if (g == ng && n % F::G) {
+      for (int64_t j = 0; F::G * ng + F::WC * j < n; ++j) {
+        const uint64_t x = unpack_word<BITS>(gather_packed<BITS>(packed + F::PB * ng + F::WB * j));
+        for (int b = 0; b < F::WC; ++b) {
+          const int64_t idx = F::G * ng + F::WC * j + b;
+          if (idx < n) codes[idx] = (int8_t)(x >> (8 * b));
         }
       }
     }
   }
 }
 
-// out[i] = code[i] * scale[i / cols] for the 16 codes of group g (four per
-// word of x), written as fp32 or bfloat16.  ROW16: cols is a multiple of 16,
+// out[i] = code[i] * scale[i / cols] for the G codes of group g (four per
+// word of c), written as fp32 or bfloat16.  ROWG: cols is a multiple of G,
 // so the whole group lies in one row, and rows * cols < 2^32.
-template <bool BF16, bool ROW16>
-__device__ inline void dequant_group(const uint32_t (&x)[4], int64_t g, int64_t cols, const uint16_t* scales,
+template <int G, bool BF16, bool ROWG>
+__device__ inline void dequant_group(const uint32_t (&c)[G / 4], int64_t g, int64_t cols, const uint16_t* scales,
                                      void* out) {
-  float v[16];
-  if (ROW16) {
-    // every index fits 32 bits (checked on the host), and 32-bit division
-    // is a few instructions where 64-bit division is a long sequence
-    const float s = f16_bits_to_float(scales[(uint32_t)(16 * g) / (uint32_t)cols]);
+  float v[G];
+  if (ROWG) {
+    // 32-bit division: a few instructions where 64-bit division is a long sequence
+    const float s = f16_bits_to_float(scales[(uint32_t)(G * g) / (uint32_t)cols]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = (float)(int8_t)((x[i >> 2] >> (8 * (i & 3))) & 0xFF) * s;
+    for (int i = 0; i < G; ++i) v[i] = (float)(int8_t)((c[i >> 2] >> (8 * (i & 3))) & 0xFF) * s;
   } else {
-    int64_t r = (16 * g) / cols, c = 16 * g - r * cols;
+    int64_t r = (G * g) / cols, col = G * g - r * cols;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      while (c >= cols) { c -= cols; ++r; }
-      v[i] = (float)(int8_t)((x[i >> 2] >> (8 * (i & 3))) & 0xFF) * f16_bits_to_float(scales[r]);
-      ++c;
+    for (int i = 0; i < G; ++i) {
+      while (col >= cols) { col -= cols; ++r; }
+      v[i] = (float)(int8_t)((c[i >> 2] >> (8 * (i & 3))) & 0xFF) * f16_bits_to_float(scales[r]);
+      ++col;
     }
   }
   if (BF16) {
-    uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + 16 * g);
-    uint32_t p[8];
+    uint32_t p[G / 2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = bf16x2_rne(v[2 * i], v[2 * i + 1]);
-    o[0] = make_uint4(p[0], p[1], p[2], p[3]);
-    o[1] = make_uint4(p[4], p[5], p[6], p[7]);
+    for (int i = 0; i < G / 2; ++i) p[i] = bf16x2_rne(v[2 * i], v[2 * i + 1]);
+    store_words<G / 2>(out, g, p);
   } else {
-    float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + 16 * g);
+    float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + G * g);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    for (int i = 0; i < G / 4; ++i) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
   }
 }
 
@@ -183,52 +285,43 @@ __device__ inline void dequant_one(int8_t code, int64_t idx, int64_t cols, const
   else static_cast<float*>(out)[idx] = v;
 }
 
-// PACKED: src holds the packed bytes, else int8 codes.
-template <bool PACKED, bool BF16, bool ROW16>
+// BITS 6 / 5: src holds packed codes; BITS 8: int8 codes.
+template <int BITS, bool BF16, bool ROWG>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const void* src, const uint16_t* scales, int64_t n,
                                                            int64_t cols, void* out) {
-  const int64_t n16 = n >> 4;
+  using F = Fmt<BITS>;
+  const int64_t ng = n / F::G;
   const int64_t gb = blockIdx.x * kGroupsPerBlock + threadIdx.x;
-  uint32_t x[kU][4];
+  uint32_t p[kU][F::PB / 4];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const int64_t g = gb + u * kThreads;
-    x[u][0] = x[u][1] = x[u][2] = x[u][3] = 0;
-    if (g < n16) {
-      if (PACKED) {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(src) + 12 * g);
-        x[u][0] = p[0]; x[u][1] = p[1]; x[u][2] = p[2];
-      } else {
-        const uint4 c = reinterpret_cast<const uint4*>(src)[g];
-        x[u][0] = c.x; x[u][1] = c.y; x[u][2] = c.z; x[u][3] = c.w;
-      }
-    }
+#pragma unroll
+    for (int i = 0; i < F::PB / 4; ++i) p[u][i] = 0;
+    if (g < ng) load_words<F::PB / 4>(src, g, p[u]);
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const int64_t g = gb + u * kThreads;
-    if (g < n16) {
-      if (PACKED) {
-        const uint32_t d0 = x[u][0], d1 = x[u][1], d2 = x[u][2];
-        x[u][0] = unpack4(d0 & 0xFFFFFFu);
-        x[u][1] = unpack4((d0 >> 24) | ((d1 & 0xFFFFu) << 8));
-        x[u][2] = unpack4((d1 >> 16) | ((d2 & 0xFFu) << 16));
-        x[u][3] = unpack4(d2 >> 8);
+    if (g < ng) {
+      if constexpr (BITS == 8) {
+        dequant_group<F::G, BF16, ROWG>(p[u], g, cols, scales, out);
+      } else {
+        uint32_t c[F::G / 4];
+        unpack_group(p[u], c);
+        dequant_group<F::G, BF16, ROWG>(c, g, cols, scales, out);
       }
-      dequant_group<BF16, ROW16>(x[u], g, cols, scales, out);
-    } else if (g == n16 && (n & 15)) {
-      for (int64_t j = 0; 16 * n16 + 4 * j < n; ++j) {
-        uint32_t w;
-        if (PACKED) {
-          w = unpack4(load_packed_word(static_cast<const uint8_t*>(src) + 12 * n16 + 3 * j));
+    } else if (g == ng && n % F::G) {
+      for (int64_t idx0 = F::G * ng; idx0 < n; idx0 += F::WC) {
+        uint64_t x;
+        if constexpr (BITS == 8) {
+          x = (uint64_t)(uint8_t) static_cast<const int8_t*>(src)[idx0];
         } else {
-          int unused = 0;
-          w = tail_word(static_cast<const int8_t*>(src), 16 * n16 + 4 * j, n, unused);
+          const int64_t j = (idx0 - F::G * ng) / F::WC;
+          x = unpack_word<BITS>(gather_packed<BITS>(static_cast<const uint8_t*>(src) + F::PB * ng + F::WB * j));
         }
-        for (int b = 0; b < 4; ++b) {
-          const int64_t idx = 16 * n16 + 4 * j + b;
-          if (idx < n) dequant_one<BF16>((int8_t)((w >> (8 * b)) & 0xFF), idx, cols, scales, out);
-        }
+        for (int b = 0; b < F::WC; ++b)
+          if (idx0 + b < n) dequant_one<BF16>((int8_t)(x >> (8 * b)), idx0 + b, cols, scales, out);
       }
     }
   }
@@ -323,33 +416,44 @@ __global__ __launch_bounds__(256) void entropy_kernel(const int64_t* hist, doubl
   if (t == 0) *out = red[0];
 }
 
-inline unsigned grid_for(int64_t n) {
-  const int64_t groups = (n >> 4) + ((n & 15) != 0);
+// Workgroups covering the groups of G codes of n (a last partial group
+// included).
+inline unsigned grid_for(int64_t n, int G) {
+  const int64_t groups = n / G + (n % G != 0);
   return (unsigned)((groups + kGroupsPerBlock - 1) / kGroupsPerBlock);
 }
 
 }  // namespace
 
-hipError_t launch_pack_int6(const int8_t* codes, int64_t n, uint8_t* packed, int32_t* flags, hipStream_t s) {
-  hipLaunchKernelGGL(pack_kernel, dim3(grid_for(n)), dim3(kThreads), 0, s, codes, n, packed, flags);
+hipError_t launch_pack_codes(const int8_t* codes, int64_t n, int bits, uint8_t* packed, int32_t* flags,
+                             hipStream_t s) {
+  if (bits == 6)
+    hipLaunchKernelGGL(pack_kernel<6>, dim3(grid_for(n, 16)), dim3(kThreads), 0, s, codes, n, packed, flags);
+  else
+    hipLaunchKernelGGL(pack_kernel<5>, dim3(grid_for(n, 32)), dim3(kThreads), 0, s, codes, n, packed, flags);
   return hipGetLastError();
 }
 
-hipError_t launch_unpack_int6(const uint8_t* packed, int64_t n, int8_t* codes, hipStream_t s) {
-  hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(n)), dim3(kThreads), 0, s, packed, n, codes);
+hipError_t launch_unpack_codes(const uint8_t* packed, int64_t n, int bits, int8_t* codes, hipStream_t s) {
+  if (bits == 6)
+    hipLaunchKernelGGL(unpack_kernel<6>, dim3(grid_for(n, 16)), dim3(kThreads), 0, s, packed, n, codes);
+  else
+    hipLaunchKernelGGL(unpack_kernel<5>, dim3(grid_for(n, 32)), dim3(kThreads), 0, s, packed, n, codes);
   return hipGetLastError();
 }
 
-hipError_t launch_dequantize(const void* src, bool packed, const uint16_t* scales, int64_t rows, int64_t cols,
+hipError_t launch_dequantize(const void* src, int bits, const uint16_t* scales, int64_t rows, int64_t cols,
                              bool bf16_out, void* out, hipStream_t s) {
   const int64_t n = rows * cols;
-  const bool row16 = cols % 16 == 0 && n < (int64_t(1) << 32);
-#define I6G_DQ(P, B, R)                                                                               \
-  if (packed == P && bf16_out == B && row16 == R)                                                     \
-    hipLaunchKernelGGL((dequant_kernel<P, B, R>), dim3(grid_for(n)), dim3(kThreads), 0, s, src, scales, \
-                       n, cols, out);
-  I6G_DQ(true, true, true) I6G_DQ(true, true, false) I6G_DQ(true, false, true) I6G_DQ(true, false, false)
-  I6G_DQ(false, true, true) I6G_DQ(false, true, false) I6G_DQ(false, false, true) I6G_DQ(false, false, false)
+  const int G = bits == 5 ? 32 : 16;
+  const bool rowg = cols % G == 0 && n < (int64_t(1) << 32);
+  const unsigned grid = grid_for(n, G);
+#define I6G_DQ(B, O, R)                                                                                  \
+  if (bits == B && bf16_out == O && rowg == R)                                                           \
+    hipLaunchKernelGGL((dequant_kernel<B, O, R>), dim3(grid), dim3(kThreads), 0, s, src, scales, n, cols, out);
+  I6G_DQ(8, true, true) I6G_DQ(8, true, false) I6G_DQ(8, false, true) I6G_DQ(8, false, false)
+  I6G_DQ(6, true, true) I6G_DQ(6, true, false) I6G_DQ(6, false, true) I6G_DQ(6, false, false)
+  I6G_DQ(5, true, true) I6G_DQ(5, true, false) I6G_DQ(5, false, true) I6G_DQ(5, false, false)
 #undef I6G_DQ
   return hipGetLastError();
 }
@@ -361,7 +465,7 @@ hipError_t launch_code_histogram(const int8_t* codes, int64_t n, bool accumulate
   hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&parts), sizeof(unsigned long long) * 256 * kHistParts, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(zero_parts_kernel, dim3(kHistParts), dim3(256), 0, s, parts);
-  if (n > 0) hipLaunchKernelGGL(hist_kernel, dim3(grid_for(n)), dim3(kThreads), 0, s, codes, n, parts);
+  if (n > 0) hipLaunchKernelGGL(hist_kernel, dim3(grid_for(n, 16)), dim3(kThreads), 0, s, codes, n, parts);
   hipLaunchKernelGGL(hist_finish_kernel, dim3(1), dim3(256), 0, s, parts, (int)accumulate,
                      reinterpret_cast<long long*>(hist));
   e = hipGetLastError();

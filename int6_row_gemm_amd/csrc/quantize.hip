@@ -1,11 +1,13 @@
-// Per-row int8 / int6 quantiser: one wavefront per row.
+// Per-row int8 / int6 / int5 quantiser: one wavefront per row.
 //
 // pwwt.cn "parameter-golf 16MB 极限压缩实战 …", sections 训练时的模拟量化 and
 // 后训练量化导出: scale = clipped |w| maximum / 127 per row, stored binary16;
 // codes round(w/scale), in int6 mode round(code/4)*4 clamped to [-128, 124].
 // The clip value is the linear-interpolation quantile of |w| over the row
 // (at q = 0.99999 84 only the top two order statistics matter for rows up to
-// 625,000 long); kwkr.cn PR #363 Noisy-QAT block: floor 1e-12.
+// 625,000 long); kwkr.cn PR #363 Noisy-QAT block: floor 1e-12.  int5 (the
+// same write-up's MLP_INT5 / ATTN_INT5 export, step amax / 15): scale = c/15,
+// codes round(w/scale) clamped to [-16, 15].
 //
 // Every fp32 operation is rounded on its own: contraction into FMA is off in
 // this file and division is IEEE correctly rounded (the HIP default), so the
@@ -95,7 +97,7 @@ __device__ void quantize_row_k(const float* w, int cols, int topk, float frac, i
   float step = frac * diff;
   float c = s_lo + step;
   c = fmaxf(c, 1e-12f);
-  const float scale = c / 127.0f;
+  const float scale = c / (bits == 5 ? 15.0f : 127.0f);
 
   for (int c0 = 0; c0 < cols; c0 += kU * kWave) {
     float wv[kU];
@@ -113,6 +115,8 @@ __device__ void quantize_row_k(const float* w, int cols, int topk, float frac, i
       float code;
       if (bits == 8) {
         code = fminf(fmaxf(k, -127.0f), 127.0f);
+      } else if (bits == 5) {
+        code = fminf(fmaxf(k, -16.0f), 15.0f);
       } else {
         float k4 = rintf(k * 0.25f);
         code = fminf(fmaxf(k4 * 4.0f, -128.0f), 124.0f);

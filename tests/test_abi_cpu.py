@@ -140,36 +140,47 @@ def test_export_entry_points_validate_without_gpu():
     fake = ctypes.c_void_p(0x1000)     # 4096-aligned, never dereferenced
     odd = ctypes.c_void_p(0x1001)
     null = ctypes.c_void_p(0)
-    assert L.i6g_pack_int6(fake, -1, fake, null, null) == -1
-    assert L.i6g_pack_int6(null, 4, fake, null, null) == -1
-    assert L.i6g_pack_int6(null, 0, null, null, null) == 0          # nothing to do
-    assert L.i6g_pack_int6(odd, 16, fake, null, null) == -6
-    assert L.i6g_unpack_int6(fake, 16, odd, null) == -6
-    assert L.i6g_unpack_int6(fake, -3, fake, null) == -1
+    for bits in (5, 6):
+        assert L.i6g_pack_codes(fake, -1, bits, fake, null, null) == -1
+        assert L.i6g_pack_codes(null, 4, bits, fake, null, null) == -1
+        assert L.i6g_pack_codes(null, 0, bits, null, null, null) == 0          # nothing to do
+        assert L.i6g_pack_codes(odd, 16, bits, fake, null, null) == -6
+        assert L.i6g_unpack_codes(fake, 16, bits, odd, null) == -6
+        assert L.i6g_unpack_codes(fake, -3, bits, fake, null) == -1
+        assert L.i6g_dequantize_packed(fake, bits, fake, 4, 4, 2, odd, null) == -6
+    for bits in (4, 7, 8):
+        assert L.i6g_pack_codes(fake, 16, bits, fake, null, null) == -1
+        assert L.i6g_unpack_codes(fake, 16, bits, fake, null) == -1
+        assert L.i6g_dequantize_packed(fake, bits, fake, 4, 4, 2, fake, null) == -1
     assert L.i6g_dequantize_rows(fake, fake, 4, 4, 0, fake, null) == -1   # fp16 output: not offered
     assert L.i6g_dequantize_rows(fake, fake, -1, 4, 1, fake, null) == -1
     assert L.i6g_dequantize_rows(null, fake, 4, 4, 1, fake, null) == -1
     assert L.i6g_dequantize_rows(fake, fake, 0, 4, 2, null, null) == 0
-    assert L.i6g_dequantize_int6_packed(fake, fake, 4, 4, 2, odd, null) == -6
     assert L.i6g_code_histogram(fake, 16, 0, null, null) == -1
     assert L.i6g_code_histogram(odd, 16, 0, fake, null) == -6
     assert L.i6g_code_entropy(null, fake, null) == -1
     out = ctypes.c_int64(0)
-    assert L.i6g_artifact_bytes(None, -1, 0, ctypes.byref(out)) == -1
-    assert L.i6g_artifact_bytes(None, 0, -5, ctypes.byref(out)) == -1
+    assert L.i6g_artifact_bytes(None, None, -1, 0, ctypes.byref(out)) == -1
+    assert L.i6g_artifact_bytes(None, None, 0, -5, ctypes.byref(out)) == -1
     bad = (ctypes.c_int64 * 2)(3, -1)
-    assert L.i6g_artifact_bytes(bad, 1, 0, ctypes.byref(out)) == -1
+    assert L.i6g_artifact_bytes(bad, None, 1, 0, ctypes.byref(out)) == -1
+    ok = (ctypes.c_int64 * 2)(3, 5)
+    assert L.i6g_artifact_bytes(ok, (ctypes.c_int32 * 1)(7), 1, 0, ctypes.byref(out)) == -1
 
 
 def test_artifact_bytes_matches_oracle():
     g, _ = _lib()
     from oracle import export as ox
+    from oracle import quant as oq
     import synth
     for shapes, pt in [([(3, 5)], 7), ([(1, 4), (2, 2), (7, 1)], 0), ([], 11), ([(0, 5), (5, 0)], 1)]:
         assert g.artifact_bytes(shapes, pt) == ox.artifact_bytes(shapes, pt)
-    for name in ("11l", "11l_next", "midcycle", "tiny"):
+        for b in (5, 8):
+            assert g.artifact_bytes(shapes, pt, [b] * len(shapes)) == ox.artifact_bytes(shapes, pt, [b] * len(shapes))
+    for name in ("11l", "11l_next", "midcycle", "tiny", "11l_int5", "10l_int5mlp"):
         arch = synth.config(name)["arch"]
-        d, kv, F = arch["d_model"], arch["n_kv_heads"] * arch["head_dim"], arch["d_ff"]
-        shapes = [(d, d), (kv, d), (kv, d), (d, d), (F, d), (d, F)] * len(set(arch["schedule"]))
-        pt = arch["vocab"] * d
-        assert g.artifact_bytes(shapes, pt) == ox.artifact_bytes(shapes, pt)
+        ms = synth.matrix_shapes(arch)
+        shapes = list(ms.values()) * len(set(arch["schedule"]))
+        bits = [oq.matrix_bits(arch, k) for k in ms] * len(set(arch["schedule"]))
+        pt = arch["vocab"] * arch["d_model"]
+        assert g.artifact_bytes(shapes, pt, bits) == ox.artifact_bytes(shapes, pt, bits)

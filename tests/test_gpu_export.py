@@ -1,6 +1,7 @@
-"""Parity of the export side (6-bit packing, dequantisation, code histogram
-and entropy, artifact size) between the HIP kernels and the oracle: packed
-bytes, codes, histograms and dequantised values bit-exact, entropy to 1e-12."""
+"""Parity of the export side (int6 / int5 bit packing, dequantisation, code
+histogram and entropy, artifact size) between the HIP kernels and the
+oracle: packed bytes, codes, histograms and dequantised values bit-exact,
+entropy to 1e-12."""
 import numpy as np
 import pytest
 
@@ -10,6 +11,8 @@ from gpu_common import make_case, need_gpu, oracle_quantized
 pytestmark = pytest.mark.gpu
 
 LEVELS = np.arange(-128, 125, 4, dtype=np.int8)
+INT5 = np.arange(-16, 16, dtype=np.int8)
+CODESET = {6: LEVELS, 5: INT5}
 # binary16 scales: ordinary, smallest subnormal, largest subnormal, largest
 # finite, zero, -1, +Inf, NaN
 EDGE_SCALES = np.array([0x2E66, 0x0001, 0x03FF, 0x7BFF, 0x0000, 0xBC00, 0x7C00, 0x7E00], dtype=np.uint16)
@@ -37,51 +40,57 @@ def _f32_bits_equal(got, ref):
     assert np.array_equal(got[~nan].view(np.int32), ref[~nan].view(np.int32))
 
 
-@pytest.mark.parametrize("n", [1, 3, 4, 5, 15, 16, 17, 31, 33, 1000, 16 * 1024 + 7, 16 * 1024 * 4 + 12,
-                               3_000_017])
-def test_pack_unpack_bit_exact(n):
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 7, 8, 9, 15, 16, 17, 31, 32, 33, 1000, 16 * 1024 + 7,
+                               16 * 1024 * 4 + 12, 3_000_017])
+@pytest.mark.parametrize("bits", [6, 5])
+def test_pack_unpack_bit_exact(n, bits):
     g = need_gpu()
     import torch
-    print(f"pack/unpack n={n}", flush=True)
-    codes = np.random.default_rng(n).choice(LEVELS, n)
+    print(f"pack/unpack int{bits} n={n}", flush=True)
+    codes = np.random.default_rng(n).choice(CODESET[bits], n)
     flags = torch.zeros(1, dtype=torch.int32, device="cuda")
-    packed = g.pack_int6(_dev(codes), flags)
-    ref = ox.pack_int6(codes)
+    packed = g.pack_codes(_dev(codes), bits, flags)
+    ref = ox.pack_codes(codes, bits)
     assert np.array_equal(packed.cpu().numpy(), ref)
     assert int(flags.item()) == 0
-    back = g.unpack_int6(_dev(ref), n)
+    back = g.unpack_codes(_dev(ref), n, bits)
     assert np.array_equal(back.cpu().numpy(), codes)
 
 
-def test_pack_every_level_in_every_slot_and_empty():
+@pytest.mark.parametrize("bits", [6, 5])
+def test_pack_every_level_in_every_slot_and_empty(bits):
     g = need_gpu()
     import torch
-    codes = np.zeros((64, 4), dtype=np.int8)
-    for pos in range(4):
-        codes[:, pos] = np.roll(LEVELS, 17 * pos)
-    packed = g.pack_int6(_dev(codes.ravel()))
-    assert np.array_equal(packed.cpu().numpy(), ox.pack_int6(codes))
+    lv = CODESET[bits]
+    wc = 4 if bits == 6 else 8
+    codes = np.zeros((len(lv), wc), dtype=np.int8)
+    for pos in range(wc):
+        codes[:, pos] = np.roll(lv, 17 * pos)
+    packed = g.pack_codes(_dev(codes.ravel()), bits)
+    assert np.array_equal(packed.cpu().numpy(), ox.pack_codes(codes, bits))
     empty = torch.empty(0, dtype=torch.int8, device="cuda")
-    assert g.pack_int6(empty).numel() == 0
-    assert g.unpack_int6(torch.empty(0, dtype=torch.uint8, device="cuda"), 0).numel() == 0
+    assert g.pack_codes(empty, bits).numel() == 0
+    assert g.unpack_codes(torch.empty(0, dtype=torch.uint8, device="cuda"), 0, bits).numel() == 0
 
 
 @pytest.mark.parametrize("bad_at", [0, 5, 16 * 300 + 3, 16 * 1024 + 2])
-def test_pack_flags_non_int6_codes(bad_at):
+@pytest.mark.parametrize("bits,bad,fixed", [(6, 6, 4), (5, 16, -16), (5, -17, 15), (5, 100, 4)])
+def test_pack_flags_codes_outside_the_format(bad_at, bits, bad, fixed):
     g = need_gpu()
     import torch
     n = 16 * 1024 + 5
-    codes = np.random.default_rng(bad_at).choice(LEVELS, n)
-    codes[bad_at] = 6            # not a multiple of 4
+    codes = np.random.default_rng(bad_at).choice(CODESET[bits], n)
+    codes[bad_at] = bad
     flags = torch.zeros(1, dtype=torch.int32, device="cuda")
-    packed = g.pack_int6(_dev(codes), flags)
+    packed = g.pack_codes(_dev(codes), bits, flags)
     assert int(flags.item()) & g.FLAG_CODE
     with pytest.raises(ValueError):
-        ox.pack_int6(codes)
-    # the other codes are packed as usual: compare with the code cleared of its low bits
-    fixed = codes.copy()
-    fixed[bad_at] = 4
-    assert np.array_equal(packed.cpu().numpy(), ox.pack_int6(fixed))
+        ox.pack_codes(codes, bits)
+    # the other codes are packed as usual; the bad byte is packed from its
+    # low bits (int6: bits 2..7; int5: bits 0..4), i.e. as the code `fixed`
+    ok = codes.copy()
+    ok[bad_at] = fixed
+    assert np.array_equal(packed.cpu().numpy(), ox.pack_codes(ok, bits))
 
 
 def _scales(rows, seed):
@@ -91,15 +100,15 @@ def _scales(rows, seed):
     return s
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 5), (8, 16), (37, 45), (64, 512), (9, 1536), (1536, 512),
-                                       (5, 4099)])
-@pytest.mark.parametrize("bits", [6, 8])
+@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 5), (8, 16), (4, 32), (37, 45), (64, 512), (9, 1536),
+                                       (1536, 512), (5, 4099)])
+@pytest.mark.parametrize("bits", [6, 5, 8])
 def test_dequantize_bit_exact(rows, cols, bits):
     g = need_gpu()
     import torch
     print(f"dequantize {rows}x{cols} bits={bits}", flush=True)
     rng = np.random.default_rng(rows * 7919 + cols)
-    codes = (rng.choice(LEVELS, (rows, cols)) if bits == 6
+    codes = (rng.choice(CODESET[bits], (rows, cols)) if bits in CODESET
              else rng.integers(-127, 128, (rows, cols)).astype(np.int8))
     s16 = _scales(rows, cols)
     ref32 = ox.dequantize_f32(codes, s16.view(np.float16))
@@ -107,11 +116,11 @@ def test_dequantize_bit_exact(rows, cols, bits):
     c_d, s_d = _dev(codes), _dev(s16.view(np.int16))
     _f32_bits_equal(g.dequantize(c_d, s_d, torch.float32).cpu().numpy(), ref32)
     _bf16_bits_equal(g.dequantize(c_d, s_d, torch.bfloat16).view(torch.int16).cpu().numpy(), ref16)
-    if bits == 6:
-        p = _dev(ox.pack_int6(codes))
-        _f32_bits_equal(g.dequantize_packed(p, s_d, rows, cols, torch.float32).cpu().numpy(), ref32)
-        _bf16_bits_equal(g.dequantize_packed(p, s_d, rows, cols, torch.bfloat16).view(torch.int16).cpu().numpy(),
-                         ref16)
+    if bits in CODESET:
+        p = _dev(ox.pack_codes(codes, bits))
+        _f32_bits_equal(g.dequantize_packed(p, s_d, rows, cols, torch.float32, bits).cpu().numpy(), ref32)
+        _bf16_bits_equal(g.dequantize_packed(p, s_d, rows, cols, torch.bfloat16, bits).view(torch.int16)
+                         .cpu().numpy(), ref16)
 
 
 @pytest.mark.parametrize("n", [1, 15, 16, 17, 4097, 1_000_003])
@@ -142,34 +151,39 @@ def test_entropy_closed_forms():
     assert g.code_entropy(one).item() == 0.0
 
 
-def test_model_export_roundtrip_full_size():
-    """The 11-layer model at its real shapes: pack every block matrix, check
-    bytes, histogram, entropy and artifact size against the oracle, decode
-    the packed matrices to bfloat16 bit-exactly, and score with the unpacked
-    codes: identical nats to the codes that were packed."""
+@pytest.mark.parametrize("name", ["11l", "10l_int5mlp"])
+def test_model_export_roundtrip_full_size(name):
+    """A full-size model (all int6; int5 MLP with int6 attention): pack every
+    block matrix at its width, check bytes, histogram, entropy and artifact
+    size against the oracle, decode the packed matrices to bfloat16
+    bit-exactly, and score with the unpacked codes: identical nats to the
+    codes that were packed."""
     g = need_gpu()
     import torch
     import synth
-    cfg, model = make_case("11l")
+    from oracle import quant as oq
+    cfg, model = make_case(name)
+    arch = cfg["arch"]
     ref_q = oracle_quantized(model)
     qb = g.quantize_model(model)
     pt = model["embed"].size + (model["skip_w"].size if model["skip_w"] is not None else 0)
-    print("export 11l", flush=True)
-    ex = g.export_model(qb, pt)
-    shapes, all_codes = [], []
+    print(f"export {name}", flush=True)
+    ex = g.export_model(qb, arch, pt)
+    shapes, widths, all_codes = [], [], []
     for pb, rb in zip(ex["packed"], ref_q["qblocks"]):
-        for name, (packed, scales, shape) in pb.items():
-            codes, s16 = rb[name]
-            assert np.array_equal(packed.cpu().numpy(), ox.pack_int6(codes)), name
-            got = g.dequantize_packed(packed, scales, shape[0], shape[1], torch.bfloat16)
+        for mname, (packed, scales, shape, bits) in pb.items():
+            codes, s16 = rb[mname]
+            assert bits == oq.matrix_bits(arch, mname)
+            assert np.array_equal(packed.cpu().numpy(), ox.pack_codes(codes, bits)), mname
+            got = g.dequantize_packed(packed, scales, shape[0], shape[1], torch.bfloat16, bits)
             _bf16_bits_equal(got.view(torch.int16).cpu().numpy(), ox.dequantize_bf16(codes, s16))
             shapes.append(shape)
+            widths.append(bits)
             all_codes.append(codes.ravel())
     hist = ox.code_histogram(np.concatenate(all_codes))
     assert np.array_equal(ex["hist"].cpu().numpy(), hist)
     assert abs(ex["entropy_bits"].item() - ox.entropy_bits(hist)) <= 1e-12
-    assert ex["bytes"] == ox.artifact_bytes(shapes, pt)
-    print(f"11l artifact {ex['bytes']} bytes, code entropy {ex['entropy_bits'].item():.4f} bits", flush=True)
+    assert ex["bytes"] == ox.artifact_bytes(shapes, pt, widths)
 
     back = g.import_model(ex["packed"])
     tokens, nbytes = synth.make_stream(cfg, seed=7, n_tokens=2 * 2048 + 1)

@@ -28,7 +28,7 @@ def _assert_same(g, w, bits, q, label):
     assert sb.size == 0, f"{label}: {len(sb)} scale mismatches, first {sb[:3].tolist()}"
 
 
-@pytest.mark.parametrize("name", ["tiny", "baseline", "11l", "midcycle", "largevocab"])
+@pytest.mark.parametrize("name", ["tiny", "baseline", "11l", "midcycle", "largevocab", "11l_int5", "10l_int5mlp"])
 def test_config_matrices_bit_exact(name):
     g = need_gpu()
     cfg = synth.config(name)
@@ -38,11 +38,12 @@ def test_config_matrices_bit_exact(name):
         if b > 1 and name != "tiny" and b % 3:
             continue                     # every third block beyond the first two
         for mname, w in blk.items():
-            _assert_same(g, w, a["bits"], a["clip_q"], f"{name}/block{b}/{mname}")
+            _assert_same(g, w, oq.matrix_bits(a, mname), a["clip_q"], f"{name}/block{b}/{mname}")
 
 
 @pytest.mark.parametrize("cols", [48, 512, 1536, 2048])
-@pytest.mark.parametrize("bits,q", [(6, 0.9999984), (8, 0.9999984), (6, 1.0), (8, 1.0), (6, 0.999)])
+@pytest.mark.parametrize("bits,q", [(6, 0.9999984), (8, 0.9999984), (6, 1.0), (8, 1.0), (6, 0.999),
+                                    (5, 0.9999984), (5, 1.0)])
 def test_adversarial_rows_bit_exact(cols, bits, q):
     g = need_gpu()
     if cols - int(np.floor(q * (cols - 1))) > 8:
@@ -84,7 +85,7 @@ def test_many_matrices_in_one_call_bit_exact():
     shapes = [(int(rng.integers(1, 40)), int(c)) for c in rng.choice([7, 48, 64, 100, 512, 1536, 2048], 70)]
     ws = [torch.from_numpy((rng.standard_normal(s) * 0.02).astype(np.float32)).cuda() for s in shapes]
     ws[5][0, 3] = float("nan")          # one non-finite row
-    for bits, q in [(6, 0.9999984), (8, 1.0)]:
+    for bits, q in [(6, 0.9999984), (8, 1.0), (5, 0.9999984)]:
         print_case("quantize_rows_many", "bits", bits, "q", q, "jobs", len(ws))
         jobs = [(w, torch.empty(w.shape, dtype=torch.int8, device="cuda"),
                  torch.empty(w.shape[0], dtype=torch.int16, device="cuda")) for w in ws]

@@ -60,6 +60,9 @@ SMALL = [
     ("baseline", {"rope_dims": 48}, 128, 128, 400),
     ("baseline", {"xsa_last_n": 9}, 128, 128, 400),
     ("largevocab", {"leaky_slope": 0.5}, 200, 50, 700),
+    # int5 export: every matrix, and int5 MLP with int6 attention
+    ("11l_int5", {}, 256, 64, 1000),
+    ("10l_int5mlp", {}, 256, 64, 1000),
 ]
 
 
@@ -135,6 +138,8 @@ FULL = [
     ("midcycle", [0, 31]),
     ("11l", [0, 8191, 16352]),
     ("11l_next", [0, 8191, 16352]),
+    ("11l_int5", [0, 16352]),
+    ("10l_int5mlp", [8191]),
     ("largevocab", [0, 40000, 65504]),
 ]
 
