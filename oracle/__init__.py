@@ -1,4 +1,5 @@
-"""CPU oracle for the int6/int8 per-row scoring pass.
+"""CPU oracle for the int6 / int5 / int8 per-row scoring pass, its export side
+and the forward-only quantisation-aware weights.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or call anything here.  The HIP
@@ -21,10 +22,13 @@ Modules:
   ``quant``   -- row quantiser, step by step in IEEE binary32 (bit-exact gate).
   ``model``   -- the transformer forward in float64 with dequantised weights.
   ``windows`` -- the sliding-window plan and bits-per-byte.
+  ``export``  -- int6 / int5 bit packing, code histogram and entropy,
+                 artifact bytes, dequantisation to fp32 / bf16.
+  ``qat``     -- STE fake quantisation, Noisy-QAT noise, Philox4x32-10.
 
 Every function here is pinned by CPU tests in ``tests/test_oracle_*.py``
 against closed forms, brute force, invariants and the pages' printed numbers.
 """
-from . import quant, model, windows  # noqa: F401
+from . import quant, model, windows, export, qat  # noqa: F401
 from .quant import quantize_rows, quantize_model  # noqa: F401
 from .windows import plan_windows, score, bpb  # noqa: F401
