@@ -274,6 +274,33 @@ def main():
             [g.matrix_bits(arch, k) for _ in codes for k in names])
         export["entropy_bits"] = g.code_entropy(g.code_histogram(flat, hist)).item()
         del flat, keep
+    # Forward-only QAT weights on the model's 512-column matrices stacked
+    # (q, k, v, o and fc of every block): fake quantisation and Noisy-QAT
+    # noise, each 4 B read + 2 B written (bfloat16) per weight (the row is
+    # read twice by the kernel, the second time mostly from cache).
+    qat = None
+    if not args.no_timing:
+        w512 = torch.cat([w for wb in w_dev for w in wb.values() if w.shape[1] == arch["d_model"]])
+        o16 = torch.empty(w512.shape, dtype=torch.bfloat16, device="cuda")
+        n_w512 = w512.numel()
+
+        def fq():
+            rc = lib.i6g_fake_quantize_rows(ctypes.c_void_p(w512.data_ptr()), w512.shape[0], w512.shape[1],
+                                            g.matrix_bits(arch, "fc"), 1.0, g.DTYPE_BF16,
+                                            ctypes.c_void_p(o16.data_ptr()), None, stream)
+            if rc:
+                raise g.I6GError(rc, lib.i6g_last_error().decode())
+
+        def nz():
+            rc = lib.i6g_noisy_weights(ctypes.c_void_p(w512.data_ptr()), w512.shape[0], w512.shape[1], 127.0,
+                                       1234, g.DTYPE_BF16, ctypes.c_void_p(o16.data_ptr()), None, stream)
+            if rc:
+                raise g.I6GError(rc, lib.i6g_last_error().decode())
+
+        qat = {"weights": n_w512, "shape": list(w512.shape),
+               "fake_quantize_bf16": hbm_entry(*timed(fq), 6.0 * n_w512),
+               "noisy_weights_bf16": hbm_entry(*timed(nz), 6.0 * n_w512)}
+        del w512, o16
     del flush
 
     cpu = None
@@ -305,6 +332,7 @@ def main():
         "kernels_warmup_step": kernels,
         "quantize_rows": quant,
         "export": export,
+        "qat": qat,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

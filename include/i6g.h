@@ -116,6 +116,39 @@ typedef struct {
 int i6g_quantize_rows_many(const i6g_quant_job* jobs, int32_t n_jobs, int bits, double clip_quantile,
                            int32_t* flags_dev, void* stream);
 
+/*
+ * Forward-only quantisation-aware weights (the training forward's view of a
+ * weight matrix; no backward pass is involved).
+ *
+ * i6g_fake_quantize_rows -- [11L] 训练时的模拟量化: the straight-through
+ * estimator's forward value w + (w_q - w) = w_q, with w_q = code * scale
+ * from the steps of i6g_quantize_rows (same bits and clip_quantile; 1.0 is
+ * the plain absolute maximum of the training-time simulation) but the fp32
+ * scale, not its binary16 rounding: out = code * scale in fp32 (one
+ * rounding), or that value rounded to bfloat16 (nearest even).  A row with
+ * NaN/Inf gives NaN outputs and sets I6G_FLAG_NONFINITE in *flags_dev (may
+ * be NULL).  out_dev [rows, cols] fp32 or bf16.  Errors as
+ * i6g_quantize_rows, and I6G_EINVAL for an unknown out_dtype.
+ */
+int i6g_fake_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int bits, double clip_quantile,
+                           int out_dtype, void* out_dev, int32_t* flags_dev, void* stream);
+
+/*
+ * i6g_noisy_weights -- [363] Noisy QAT: out = w + (U - 0.5) * step per row,
+ * step = max(amax, 1e-12) / levels (127 in the write-up's code block; 15 to
+ * match an int5 export), each fp32 operation rounded once.  U is uniform on
+ * [0, 1): U = (x >> 8) * 2^-24 with x word (i % 4) of Philox4x32-10 (Salmon,
+ * Moraes, Dror, Shaw, SC 2011) at key (seed low 32 bits, seed high 32 bits)
+ * and counter (i / 4 low 32 bits, i / 4 high 32 bits, 0, 0), i = r * cols + c.
+ * Output fp32, or bfloat16 (nearest even).  A row with NaN/Inf gives NaN
+ * outputs and sets I6G_FLAG_NONFINITE.  w_dev and out_dev must be 16-byte
+ * aligned.  Errors: I6G_EINVAL for rows/cols < 1, levels not positive and
+ * finite, an unknown out_dtype or a NULL array; I6G_EUNSUPPORTED for
+ * misaligned buffers.
+ */
+int i6g_noisy_weights(const float* w_dev, int64_t rows, int64_t cols, double levels, uint64_t seed,
+                      int out_dtype, void* out_dev, int32_t* flags_dev, void* stream);
+
 /* One quantised [out, in] matrix: codes (int8) and per-row binary16 scales. */
 typedef struct {
   const int8_t* codes;

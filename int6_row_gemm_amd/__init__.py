@@ -27,6 +27,7 @@ EXPORTED = [
     "i6g_set_timing", "i6g_get_timing",
     "i6g_pack_codes", "i6g_unpack_codes", "i6g_dequantize_rows", "i6g_dequantize_packed",
     "i6g_code_histogram", "i6g_code_entropy", "i6g_artifact_bytes",
+    "i6g_fake_quantize_rows", "i6g_noisy_weights",
 ]
 DTYPE_F32, DTYPE_BF16 = 1, 2
 FLAG_CODE = 8
@@ -102,6 +103,8 @@ def lib():
         L.i6g_code_histogram.argtypes = [vp, i64, ctypes.c_int, vp, vp]
         L.i6g_code_entropy.argtypes = [vp, vp, vp]
         L.i6g_artifact_bytes.argtypes = [vp, vp, i32, i64, vp]
+        L.i6g_fake_quantize_rows.argtypes = [vp, i64, i64, ctypes.c_int, dbl, ctypes.c_int, vp, vp, vp]
+        L.i6g_noisy_weights.argtypes = [vp, i64, i64, dbl, ctypes.c_uint64, ctypes.c_int, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -484,4 +487,35 @@ def import_model(packed):
             codes = p.view(torch.int8).clone() if b == 8 else unpack_codes(p, n, b)
             qb[name] = (codes.view(shape), scales)
         out.append(qb)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Forward-only quantisation-aware weights.
+
+def fake_quantize_rows(w, bits, clip_quantile=1.0, dtype=None, flags=None):
+    """The straight-through forward value code * fp32 scale of each row of a
+    device fp32 matrix, as float32 or bfloat16."""
+    import torch
+    dtype = dtype or torch.float32
+    if not (w.is_cuda and w.dtype == torch.float32 and w.dim() == 2):
+        raise ValueError("w must be a 2-D float32 CUDA tensor")
+    w = w.contiguous()
+    out = torch.empty(w.shape, dtype=dtype, device=w.device)
+    _check(lib().i6g_fake_quantize_rows(_ptr(w), w.shape[0], w.shape[1], bits, float(clip_quantile),
+                                        _dq_dtype(dtype), _ptr(out), _ptr(flags), _stream()))
+    return out
+
+
+def noisy_weights(w, levels, seed, dtype=None, flags=None):
+    """w + (U - 0.5) * amax / levels per row of a device fp32 matrix (U from
+    Philox4x32-10 keyed by ``seed``), as float32 or bfloat16."""
+    import torch
+    dtype = dtype or torch.float32
+    if not (w.is_cuda and w.dtype == torch.float32 and w.dim() == 2):
+        raise ValueError("w must be a 2-D float32 CUDA tensor")
+    w = w.contiguous()
+    out = torch.empty(w.shape, dtype=dtype, device=w.device)
+    _check(lib().i6g_noisy_weights(_ptr(w), w.shape[0], w.shape[1], float(levels), int(seed) & (2 ** 64 - 1),
+                                   _dq_dtype(dtype), _ptr(out), _ptr(flags), _stream()))
     return out

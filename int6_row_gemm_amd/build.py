@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libi6g.so")
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "attention.hip", "aux.hip", "export.hip"]
+SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "attention.hip", "aux.hip", "export.hip", "qat.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

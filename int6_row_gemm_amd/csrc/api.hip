@@ -323,6 +323,53 @@ int i6g_quantize_rows_many(const i6g_quant_job* jobs, int32_t n_jobs, int bits, 
 
 static bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+int i6g_fake_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int bits, double clip_quantile,
+                           int out_dtype, void* out_dev, int32_t* flags_dev, void* stream) {
+  int32_t topk = 0;
+  float frac = 0.0f;
+  int rc = quant_plan("fake_quantize_rows", w_dev, out_dev, out_dev, rows, cols, bits, clip_quantile, &topk,
+                      &frac);
+  if (rc) return rc;
+  if (out_dtype != I6G_DTYPE_F32 && out_dtype != I6G_DTYPE_BF16)
+    return fail(I6G_EINVAL, "fake_quantize_rows: out_dtype must be I6G_DTYPE_F32 or I6G_DTYPE_BF16");
+  QuantArgs a{};
+  a.w = w_dev;
+  a.flags = flags_dev;
+  a.rows = rows;
+  a.cols = (int32_t)cols;
+  a.bits = bits;
+  a.topk = topk;
+  a.frac = frac;
+  a.fq = out_dev;
+  a.fq_bf16 = out_dtype == I6G_DTYPE_BF16;
+  HIP_TRY(launch_fake_quantize(a, (hipStream_t)stream));
+  return I6G_OK;
+}
+
+int i6g_noisy_weights(const float* w_dev, int64_t rows, int64_t cols, double levels, uint64_t seed, int out_dtype,
+                      void* out_dev, int32_t* flags_dev, void* stream) {
+  if (!w_dev || !out_dev) return fail(I6G_EINVAL, "noisy_weights: NULL array");
+  if (rows < 1 || cols < 1 || cols > INT32_MAX) return fail(I6G_EINVAL, "noisy_weights: need rows, cols >= 1");
+  if (!(levels > 0.0) || !std::isfinite(levels) || !std::isfinite((float)levels))
+    return fail(I6G_EINVAL, "noisy_weights: levels must be positive and finite");
+  if (out_dtype != I6G_DTYPE_F32 && out_dtype != I6G_DTYPE_BF16)
+    return fail(I6G_EINVAL, "noisy_weights: out_dtype must be I6G_DTYPE_F32 or I6G_DTYPE_BF16");
+  if (!aligned(w_dev, 16) || !aligned(out_dev, 16))
+    return fail(I6G_EUNSUPPORTED, "noisy_weights: w and out must be 16-byte aligned");
+  NoisyArgs a{};
+  a.w = w_dev;
+  a.out = out_dev;
+  a.flags = flags_dev;
+  a.rows = rows;
+  a.cols = (int32_t)cols;
+  a.out_bf16 = out_dtype == I6G_DTYPE_BF16;
+  a.levels = (float)levels;
+  a.key0 = (uint32_t)seed;
+  a.key1 = (uint32_t)(seed >> 32);
+  HIP_TRY(launch_noisy_weights(a, (hipStream_t)stream));
+  return I6G_OK;
+}
+
 static int64_t packed_bytes(int64_t n, int bits) {
   return bits == 6 ? 3 * ((n + 3) / 4) : bits == 5 ? 5 * ((n + 7) / 8) : n;
 }

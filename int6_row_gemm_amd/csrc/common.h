@@ -32,8 +32,26 @@ struct QuantArgs {
   int32_t bits;
   int32_t topk;   // number of largest |w| kept per row (cols - lo)
   float frac;     // fp32 interpolation weight f
+  void* fq;       // fake quantisation: [rows, cols] output, fp32 or bf16
+  int32_t fq_bf16;
 };
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+// code * fp32 scale per element (fake quantisation) into a.fq
+hipError_t launch_fake_quantize(const QuantArgs& a, hipStream_t s);
+
+// Noisy-QAT weights: out = w + (U - 0.5) * max(amax, 1e-12) / levels per
+// row, U from Philox4x32-10 (key = seed, counter = element index / 4).
+struct NoisyArgs {
+  const float* w;
+  void* out;
+  int32_t* flags;
+  int64_t rows;
+  int32_t cols;
+  int32_t out_bf16;
+  float levels;
+  uint32_t key0, key1;
+};
+hipError_t launch_noisy_weights(const NoisyArgs& a, hipStream_t s);
 
 // Several matrices in one launch: row r of the concatenated rows belongs to
 // the last job j with row0[j] <= r.

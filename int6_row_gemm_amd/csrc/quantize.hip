@@ -38,9 +38,11 @@ __device__ inline void insert_top(float (&t)[KT], float a) {
 // largest |w|; the quantile of every row length these models use needs the
 // top two (q < 1) or one (q = 1), so KT = 2 covers them with a quarter of
 // the compare work of the general KT = 8.
-template <int KT>
+// FQ: instead of codes and the binary16 scale, write the fake-quantised
+// row code * scale (fp32 scale, one rounding) to fq as fp32 or bfloat16.
+template <int KT, bool FQ>
 __device__ void quantize_row_k(const float* w, int cols, int topk, float frac, int bits, int8_t* codes,
-                               uint16_t* scale_out, int32_t* flags, int lane) {
+                               uint16_t* scale_out, int32_t* flags, int lane, void* fq, int fq_bf16) {
   // The row is read in chunks of kU elements per lane whose loads are all
   // issued before any is used, so their latencies overlap.
   constexpr int kU = 8;
@@ -63,9 +65,16 @@ __device__ void quantize_row_k(const float* w, int cols, int topk, float frac, i
   }
   bad = __any(bad);
   if (bad) {
-    for (int c = lane; c < cols; c += kWave) codes[c] = 0;
+    for (int c = lane; c < cols; c += kWave) {
+      if (FQ) {
+        if (fq_bf16) static_cast<uint16_t*>(fq)[c] = 0x7FC0;
+        else static_cast<float*>(fq)[c] = __builtin_nanf("");
+      } else {
+        codes[c] = 0;
+      }
+    }
     if (lane == 0) {
-      *scale_out = 0x7e00;
+      if (!FQ) *scale_out = 0x7e00;
       if (flags) atomicOr(flags, 1);
     }
     return;
@@ -121,10 +130,20 @@ __device__ void quantize_row_k(const float* w, int cols, int topk, float frac, i
         float k4 = rintf(k * 0.25f);
         code = fminf(fmaxf(k4 * 4.0f, -128.0f), 124.0f);
       }
-      if (col < cols) codes[col] = (int8_t)(int)code;
+      if (col < cols) {
+        if (FQ) {
+          // the code as an integer: a zero code gives +0, as the
+          // straight-through sum w + (w_q - w) does
+          const float q = (float)(int)code * scale;
+          if (fq_bf16) static_cast<__bf16*>(fq)[col] = (__bf16)q;   // v_cvt_pk_bf16_f32: nearest even
+          else static_cast<float*>(fq)[col] = q;
+        } else {
+          codes[col] = (int8_t)(int)code;
+        }
+      }
     }
   }
-  if (lane == 0) {
+  if (!FQ && lane == 0) {
     _Float16 h = (_Float16)scale;   // v_cvt_f16_f32: round to nearest even
     *scale_out = __builtin_bit_cast(uint16_t, h);
   }
@@ -133,9 +152,9 @@ __device__ void quantize_row_k(const float* w, int cols, int topk, float frac, i
 __device__ inline void quantize_row(const float* w, int cols, int topk, float frac, int bits,
                                     int8_t* codes, uint16_t* scale_out, int32_t* flags, int lane) {
   if (topk <= 2)
-    quantize_row_k<2>(w, cols, topk, frac, bits, codes, scale_out, flags, lane);
+    quantize_row_k<2, false>(w, cols, topk, frac, bits, codes, scale_out, flags, lane, nullptr, 0);
   else
-    quantize_row_k<kTop>(w, cols, topk, frac, bits, codes, scale_out, flags, lane);
+    quantize_row_k<kTop, false>(w, cols, topk, frac, bits, codes, scale_out, flags, lane, nullptr, 0);
 }
 
 __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantArgs a) {
@@ -144,6 +163,21 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantArgs a) {
   if (row >= a.rows) return;
   quantize_row(a.w + row * a.cols, a.cols, a.topk, a.frac, a.bits, a.codes + row * a.cols,
                a.scales + row, a.flags, lane);
+}
+
+// The straight-through forward value of each row (fake quantisation).
+__global__ __launch_bounds__(256) void fake_quant_kernel(QuantArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (row >= a.rows) return;
+  void* out = a.fq_bf16 ? (void*)(static_cast<uint16_t*>(a.fq) + row * a.cols)
+                        : (void*)(static_cast<float*>(a.fq) + row * a.cols);
+  if (a.topk <= 2)
+    quantize_row_k<2, true>(a.w + row * a.cols, a.cols, a.topk, a.frac, a.bits, nullptr, nullptr, a.flags, lane,
+                            out, a.fq_bf16);
+  else
+    quantize_row_k<kTop, true>(a.w + row * a.cols, a.cols, a.topk, a.frac, a.bits, nullptr, nullptr, a.flags,
+                               lane, out, a.fq_bf16);
 }
 
 // Rows of several matrices in one grid; the job of a row is found by a
@@ -166,6 +200,13 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   const int rows_per_block = 4;
   int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
   hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fake_quantize(const QuantArgs& a, hipStream_t s) {
+  const int rows_per_block = 4;
+  int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+  hipLaunchKernelGGL(fake_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ Readings (listed in DESIGN.md):
     the fp32 scale, not its binary16 rounding (the training forward never
     rounds the scale); w_q = code * scale in fp32;
   * the STE sum w + (w_q - w) equals w_q exactly (pinned by a test), so the
-    forward value is w_q;
+    forward value is w_q; a zero code gives +0 (the sum x + (-x) is +0);
   * the uniform numbers come from Philox4x32-10 (Salmon, Moraes, Dror, Shaw,
     "Parallel random numbers: as easy as 1, 2, 3", SC 2011), key = the 64-bit
     seed, counter = (i // 4 as 64 bits, 0, 0) for element i of the row-major

@@ -184,3 +184,21 @@ def test_artifact_bytes_matches_oracle():
         bits = [oq.matrix_bits(arch, k) for k in ms] * len(set(arch["schedule"]))
         pt = arch["vocab"] * arch["d_model"]
         assert g.artifact_bytes(shapes, pt, bits) == ox.artifact_bytes(shapes, pt, bits)
+
+
+def test_qat_entry_points_validate_without_gpu():
+    g, L = _lib()
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1004)
+    null = ctypes.c_void_p(0)
+    assert L.i6g_fake_quantize_rows(fake, 4, 4, 7, 1.0, 1, fake, null, null) == -1     # bits
+    assert L.i6g_fake_quantize_rows(fake, 4, 4, 6, 1.5, 1, fake, null, null) == -1     # quantile
+    assert L.i6g_fake_quantize_rows(fake, 4, 4, 6, 1.0, 0, fake, null, null) == -1     # fp16 output
+    assert L.i6g_fake_quantize_rows(null, 4, 4, 6, 1.0, 1, fake, null, null) == -1
+    assert L.i6g_fake_quantize_rows(fake, 4, 100, 5, 0.5, 1, fake, null, null) == -6   # > 8 largest
+    for levels in (0.0, -1.0, float("inf"), float("nan"), 1e300):
+        assert L.i6g_noisy_weights(fake, 4, 4, levels, 1, 1, fake, null, null) == -1
+    assert L.i6g_noisy_weights(fake, 0, 4, 127.0, 1, 1, fake, null, null) == -1
+    assert L.i6g_noisy_weights(fake, 4, 4, 127.0, 1, 3, fake, null, null) == -1
+    assert L.i6g_noisy_weights(odd, 4, 4, 127.0, 1, 1, fake, null, null) == -6
+    assert L.i6g_noisy_weights(fake, 4, 4, 127.0, 1, 1, odd, null, null) == -6
