@@ -95,7 +95,7 @@ def main():
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     # every block matrix of the model in one i6g_quantize_rows_many call per
-    # bit width (one launch per 64 matrices)
+    # bit width (one launch per 80 matrices)
     by_bits = {}
     for wb, cb, sb in zip(w_dev, codes, scales):
         for k in wb:

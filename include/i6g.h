@@ -105,7 +105,7 @@ typedef struct {
 
 /*
  * i6g_quantize_rows_many -- i6g_quantize_rows (same steps, same results) on
- * n_jobs matrices at once, every row of up to 64 matrices a wavefront of one
+ * n_jobs matrices at once, every row of up to 80 matrices a wavefront of one
  * launch, so that a model's many small matrices fill the device (the export
  * step of [11L] 后训练量化导出 quantises every block matrix this way).
  * jobs is a host array of n_jobs entries; bits, clip_quantile and flags_dev

@@ -151,7 +151,7 @@ def quantize_rows(w, bits, clip_quantile, flags=None):
 
 
 def quantize_rows_many(jobs, bits, clip_quantile, flags=None):
-    """Row-quantise several device fp32 matrices with one launch per 64.
+    """Row-quantise several device fp32 matrices with one launch per 80.
     ``jobs`` is a list of (w, codes, scales) CUDA tensors (outputs written in
     place: codes int8 [rows, cols], scales int16 [rows] of binary16 bits)."""
     import torch

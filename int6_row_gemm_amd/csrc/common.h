@@ -54,8 +54,9 @@ struct NoisyArgs {
 hipError_t launch_noisy_weights(const NoisyArgs& a, hipStream_t s);
 
 // Several matrices in one launch: row r of the concatenated rows belongs to
-// the last job j with row0[j] <= r.
-constexpr int kQuantJobs = 64;
+// the last job j with row0[j] <= r.  The table travels in the kernel
+// arguments (at most 4 KiB), so no device buffer is needed.
+constexpr int kQuantJobs = 80;   // the 66 matrices of an 11-layer model fit one launch
 struct QuantJob {
   const float* w;
   int8_t* codes;
