@@ -37,6 +37,7 @@ def parse():
     ap.add_argument("--config", default="11l")
     ap.add_argument("--seed", type=int, default=1337)
     ap.add_argument("--batch-windows", type=int, default=0)
+    ap.add_argument("--streams", type=int, default=0, help="1 or 2 streams for the batches (0 = default)")
     ap.add_argument("--cpu-windows", type=int, default=6,
                     help="full windows the CPU oracle scores for its baseline (0 = skip)")
     ap.add_argument("--no-timing", action="store_true", help="no per-launch events")
@@ -117,6 +118,8 @@ def main():
     gm = g.load(model, qblocks)
     if args.batch_windows:
         gm.set_batch_windows(args.batch_windows)
+    if args.streams:
+        gm.set_streams(args.streams)
 
     def step():
         quantize_all()

@@ -297,8 +297,16 @@ int i6g_plan_windows(int64_t n_tokens, int32_t window, int32_t stride, int64_t* 
  *   I6G_OPT_PRUNE_LAST     1 (default): the final layer computes queries,
  *                          the output projection and the MLP only for the
  *                          scored rows; 0: for every row.
+ *   I6G_OPT_STREAMS        1 (default): every batch on the caller's
+ *                          stream.  2: consecutive batches alternate between
+ *                          the caller's stream and a second stream the
+ *                          model owns (default priority), each with its own
+ *                          scratch, so their kernels can overlap; the
+ *                          second stream waits for the caller's earlier work
+ *                          and the caller's stream waits for it before the
+ *                          totals are reduced.  Results are identical.
  * Errors: I6G_EINVAL for an unknown option or a value out of range. */
-enum { I6G_OPT_BATCH_WINDOWS = 0, I6G_OPT_PRUNE_LAST = 1 };
+enum { I6G_OPT_BATCH_WINDOWS = 0, I6G_OPT_PRUNE_LAST = 1, I6G_OPT_STREAMS = 2 };
 int i6g_set_option(i6g_model* m, int option, int64_t value);
 
 /* Per-launch kernel timing with HIP events, for measurement.  Kernel

@@ -258,6 +258,11 @@ class Model:
     def set_prune_last(self, on):
         _check(lib().i6g_set_option(self._h, 1, int(bool(on))))
 
+    def set_streams(self, n):
+        """1 (default): every batch on the caller's stream; 2: batches
+        alternate with a second stream owned by the model."""
+        _check(lib().i6g_set_option(self._h, 2, int(n)))
+
     def score(self, tokens, nbytes, window, stride, nats=None, totals=None, check=True):
         """Score a device token stream; returns (nats [N-1] fp32, totals [4] fp64)
         with totals = (sum nats, sum bytes, scored predictions, bits per byte)."""

@@ -105,8 +105,16 @@ struct i6g_model {
   // tables and scratch
   DevBuf rope;
   int rope_L = 0;
-  DevBuf x, xb, ss, q, k, vt, o, h, slots, lora_u, flags, part_n, part_b;
+  // per-batch scratch: two sets, so that consecutive batches of windows can
+  // run on two streams at once (batches are independent)
+  struct Scratch {
+    DevBuf x, xb, ss, q, k, vt, o, h, slots, lora_u;
+  } sc[2];
+  DevBuf flags, part_n, part_b;
   int64_t scratch_rows = 0;
+  int streams = 1;                 // 1: every batch on the caller's stream
+  hipStream_t aux = nullptr;       // the second stream (default priority)
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   int batch_windows = 0;
   int prune_last = 1;
   // timing
@@ -131,6 +139,12 @@ struct i6g_model {
   ~i6g_model() {
     for (auto& r : recs) { pool.push_back(r.a); pool.push_back(r.b); }
     for (auto e : pool) (void)hipEventDestroy(e);
+    if (aux) {
+      (void)hipStreamSynchronize(aux);
+      (void)hipStreamDestroy(aux);
+    }
+    if (ev_fork) (void)hipEventDestroy(ev_fork);
+    if (ev_join) (void)hipEventDestroy(ev_join);
   }
 };
 
@@ -205,17 +219,24 @@ int ensure_scratch(i6g_model* m, int W, int Lp, hipStream_t s) {
   const int64_t M = (int64_t)W * Lp;
   if (M > m->scratch_rows) {
     const int nt = m->d / 128;
-    HIP_TRY(m->x.ensure(M * m->d * 4));
-    HIP_TRY(m->xb.ensure(M * m->d * 2));
-    HIP_TRY(m->ss.ensure(M * nt * 4));
-    HIP_TRY(m->q.ensure(M * m->d * 2));
-    HIP_TRY(m->k.ensure(M * m->kvd * 2));
-    HIP_TRY(m->vt.ensure(M * m->kvd * 2));
-    HIP_TRY(m->o.ensure(M * m->d * 2));
-    HIP_TRY(m->h.ensure(M * m->F * 2));
-    if (m->max_depth > 0) HIP_TRY(m->slots.ensure((size_t)m->max_depth * M * m->d * 4));
-    if (m->lora_r > 0) HIP_TRY(m->lora_u.ensure(M * 2 * m->lora_r * 4));
+    for (auto& c : m->sc) {
+      HIP_TRY(c.x.ensure(M * m->d * 4));
+      HIP_TRY(c.xb.ensure(M * m->d * 2));
+      HIP_TRY(c.ss.ensure(M * nt * 4));
+      HIP_TRY(c.q.ensure(M * m->d * 2));
+      HIP_TRY(c.k.ensure(M * m->kvd * 2));
+      HIP_TRY(c.vt.ensure(M * m->kvd * 2));
+      HIP_TRY(c.o.ensure(M * m->d * 2));
+      HIP_TRY(c.h.ensure(M * m->F * 2));
+      if (m->max_depth > 0) HIP_TRY(c.slots.ensure((size_t)m->max_depth * M * m->d * 4));
+      if (m->lora_r > 0) HIP_TRY(c.lora_u.ensure(M * 2 * m->lora_r * 4));
+    }
     m->scratch_rows = M;
+  }
+  if (!m->aux) {
+    HIP_TRY(hipStreamCreateWithFlags(&m->aux, hipStreamNonBlocking));
+    HIP_TRY(hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming));
   }
   if (Lp > m->rope_L) {
     HIP_TRY(m->rope.ensure((size_t)Lp * (m->hd / 2) * sizeof(float2)));
@@ -597,6 +618,10 @@ int i6g_set_option(i6g_model* m, int option, int64_t value) {
     case I6G_OPT_PRUNE_LAST:
       m->prune_last = value != 0;
       return I6G_OK;
+    case I6G_OPT_STREAMS:
+      if (value != 1 && value != 2) return fail(I6G_EINVAL, "set_option: streams must be 1 or 2");
+      m->streams = (int)value;
+      return I6G_OK;
   }
   return fail(I6G_EINVAL, "set_option: unknown option %d", option);
 }
@@ -635,7 +660,22 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)m->hd));
   const int64_t e0 = window_end(0, P, L, S);
 
-  for (int64_t k0 = 0; k0 < K; k0 += Wb) {
+  // Batches alternate between the caller's stream and the model's second
+  // stream (each with its own scratch set), so that one batch's memory-bound
+  // kernels can overlap the other's compute-bound ones; the second stream
+  // starts after the caller's prior work and the caller's stream waits for
+  // it before the final reduction.
+  const hipStream_t s_caller = s;
+  const bool two = m->streams == 2 && K > Wb;
+  if (two) {
+    HIP_TRY(hipEventRecord(m->ev_fork, s_caller));
+    HIP_TRY(hipStreamWaitEvent(m->aux, m->ev_fork, 0));
+  }
+  int64_t batch = 0;
+  for (int64_t k0 = 0; k0 < K; k0 += Wb, ++batch) {
+    const bool odd = two && (batch & 1);
+    s = odd ? m->aux : s_caller;
+    auto& sc = m->sc[odd ? 1 : 0];
     const int W = (int)std::min<int64_t>(Wb, K - k0);
     const int M = W * Lp;
     // predictions scored by this batch
@@ -661,7 +701,7 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
     ea.embed = m->embed.p; ea.embed_f32 = m->embed_f32;
     ea.bigram = m->buckets > 0 ? m->bigram.as<float>() : nullptr; ea.buckets = m->buckets;
     ea.vocab = m->V; ea.d = d; ea.nt = nt;
-    ea.x = m->x.as<float>(); ea.xb = m->xb.as<bf16>(); ea.ss = m->ss.as<float>();
+    ea.x = sc.x.as<float>(); ea.xb = sc.xb.as<bf16>(); ea.ss = sc.ss.as<float>();
     ea.flags = m->flags.as<int32_t>();
     if ((rc = timed(m, I6G_K_EMBED, s, 0.0, real_rows * d * 6.0, [&] { return launch_embed(ea, s); })))
       return rc;
@@ -671,22 +711,22 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
       const bool last = (e + 1 == m->n_eff);
       if (m->lora_r > 0) {
         LoraArgs la{};
-        la.x = m->x.as<float>(); la.M = M; la.d = d; la.r = m->lora_r; la.eps = eps;
+        la.x = sc.x.as<float>(); la.M = M; la.d = d; la.r = m->lora_r; la.eps = eps;
         la.aq = m->lora_aq.as<float>() + (size_t)e * m->lora_r * d;
         la.av = m->lora_av.as<float>() + (size_t)e * m->lora_r * d;
-        la.u = m->lora_u.as<float>();
+        la.u = sc.lora_u.as<float>();
         if ((rc = timed(m, I6G_K_LORA, s, 4.0 * real_rows * m->lora_r * d, real_rows * d * 4.0,
                         [&] { return launch_lora_down(la, s); })))
           return rc;
       }
       GemmArgs g{};
-      g.A = m->xb.as<bf16>(); g.B = B.qkv_codes.as<int8_t>(); g.scale = B.qkv_scales.as<uint16_t>();
-      g.M = M; g.N = m->nqkv; g.K = d; g.ss_in = m->ss.as<float>(); g.nt_in = nt; g.eps = eps;
-      g.q = m->q.as<bf16>(); g.k = m->k.as<bf16>(); g.vt = m->vt.as<bf16>();
+      g.A = sc.xb.as<bf16>(); g.B = B.qkv_codes.as<int8_t>(); g.scale = B.qkv_scales.as<uint16_t>();
+      g.M = M; g.N = m->nqkv; g.K = d; g.ss_in = sc.ss.as<float>(); g.nt_in = nt; g.eps = eps;
+      g.q = sc.q.as<bf16>(); g.k = sc.k.as<bf16>(); g.vt = sc.vt.as<bf16>();
       g.n_heads = m->Hq; g.n_kv = m->Hkv; g.hd = m->hd; g.Lp = Lp; g.rope = m->rope.as<float2>();
       g.rope_dims = m->rope_dims;
       if (m->lora_r > 0) {
-        g.lora_u = m->lora_u.as<float>(); g.lora_r = m->lora_r;
+        g.lora_u = sc.lora_u.as<float>(); g.lora_r = m->lora_r;
         g.lora_bq = m->lora_bq.as<float>() + (size_t)e * d * m->lora_r;
         g.lora_bv = m->lora_bv.as<float>() + (size_t)e * kvd * m->lora_r;
       }
@@ -697,7 +737,7 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
 
       const bool pr = last && prune;
       AttnArgs at{};
-      at.q = m->q.as<bf16>(); at.k = m->k.as<bf16>(); at.vt = m->vt.as<bf16>(); at.o = m->o.as<bf16>();
+      at.q = sc.q.as<bf16>(); at.k = sc.k.as<bf16>(); at.vt = sc.vt.as<bf16>(); at.o = sc.o.as<bf16>();
       at.W = W; at.n_heads = m->Hq; at.n_kv = m->Hkv; at.hd = m->hd; at.Lp = Lp; at.scale_log2 = scale_log2;
       at.prune = pr; at.k0 = k0; at.P = P; at.L = (int32_t)L; at.S = (int32_t)S;
       at.xsa = e >= m->n_eff - m->xsa_last_n;
@@ -708,22 +748,22 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
 
       // attention output projection, residual add
       GemmArgs go{};
-      go.A = m->o.as<bf16>(); go.B = B.o_codes.as<int8_t>(); go.scale = B.o_scales.as<uint16_t>();
-      go.M = M; go.N = d; go.K = d; go.x = m->x.as<float>();
-      if (!m->parallel) { go.xb = m->xb.as<bf16>(); go.ss_out = m->ss.as<float>(); }
+      go.A = sc.o.as<bf16>(); go.B = B.o_codes.as<int8_t>(); go.scale = B.o_scales.as<uint16_t>();
+      go.M = M; go.N = d; go.K = d; go.x = sc.x.as<float>();
+      if (!m->parallel) { go.xb = sc.xb.as<bf16>(); go.ss_out = sc.ss.as<float>(); }
 
       GemmArgs gf{};
-      gf.A = m->xb.as<bf16>(); gf.B = B.fc_codes.as<int8_t>(); gf.scale = B.fc_scales.as<uint16_t>();
-      gf.M = M; gf.N = F; gf.K = d; gf.ss_in = m->ss.as<float>(); gf.nt_in = nt; gf.eps = eps;
-      gf.h = m->h.as<bf16>(); gf.leaky = m->leaky;
+      gf.A = sc.xb.as<bf16>(); gf.B = B.fc_codes.as<int8_t>(); gf.scale = B.fc_scales.as<uint16_t>();
+      gf.M = M; gf.N = F; gf.K = d; gf.ss_in = sc.ss.as<float>(); gf.nt_in = nt; gf.eps = eps;
+      gf.h = sc.h.as<bf16>(); gf.leaky = m->leaky;
 
       GemmArgs gp{};
-      gp.A = m->h.as<bf16>(); gp.B = B.proj_codes.as<int8_t>(); gp.scale = B.proj_scales.as<uint16_t>();
-      gp.M = M; gp.N = d; gp.K = F; gp.x = m->x.as<float>();
-      if (!last) { gp.xb = m->xb.as<bf16>(); gp.ss_out = m->ss.as<float>(); }
-      if (m->push_after[e]) gp.push_dst = m->slots.as<float>() + (size_t)m->push_slot[e] * M * d;
+      gp.A = sc.h.as<bf16>(); gp.B = B.proj_codes.as<int8_t>(); gp.scale = B.proj_scales.as<uint16_t>();
+      gp.M = M; gp.N = d; gp.K = F; gp.x = sc.x.as<float>();
+      if (!last) { gp.xb = sc.xb.as<bf16>(); gp.ss_out = sc.ss.as<float>(); }
+      if (m->push_after[e]) gp.push_dst = sc.slots.as<float>() + (size_t)m->push_slot[e] * M * d;
       if (!last && m->pop_before[e + 1] >= 0) {
-        gp.pop_src = m->slots.as<float>() + (size_t)m->pop_slot[e + 1] * M * d;
+        gp.pop_src = sc.slots.as<float>() + (size_t)m->pop_slot[e + 1] * M * d;
         gp.pop_w = m->skip_w.as<float>() + (size_t)m->pop_before[e + 1] * d;
       }
       if (pr) {
@@ -770,7 +810,7 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
     }
 
     HeadArgs ha{};
-    ha.x = m->x.as<float>();
+    ha.x = sc.x.as<float>();
     ha.E = m->embed_f32 ? m->embed16.as<_Float16>() : m->embed.as<_Float16>();
     ha.tokens = tokens_dev; ha.nats = nats_dev;
     ha.p0 = p0;
@@ -783,6 +823,11 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
       return rc;
   }
 
+  s = s_caller;
+  if (two) {
+    HIP_TRY(hipEventRecord(m->ev_join, m->aux));
+    HIP_TRY(hipStreamWaitEvent(s_caller, m->ev_join, 0));
+  }
   ReduceArgs ra{};
   ra.nats = nats_dev; ra.bytes = bytes_dev; ra.P = P;
   ra.part_nats = m->part_n.as<double>(); ra.part_bytes = m->part_b.as<long long>();
@@ -809,6 +854,7 @@ int i6g_get_timing(i6g_model* m, int kernel_class, double* total_ms, int64_t* la
   if (!m || kernel_class < 0 || kernel_class >= I6G_K_COUNT) return fail(I6G_EINVAL, "get_timing");
   if (!m->recs.empty()) {
     HIP_TRY(hipStreamSynchronize(m->timed_stream));
+    if (m->aux) HIP_TRY(hipStreamSynchronize(m->aux));
     for (auto& r : m->recs) {
       float ms = 0.f;
       HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));

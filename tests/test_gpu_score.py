@@ -17,14 +17,16 @@ from gpu_common import (BPB_ATOL, NATS_RTOL, compare_nats, gpu_model, make_case,
 pytestmark = pytest.mark.gpu
 
 
-def _run(g, name, L, S, n_tokens, seed=1337, model_kw=None, batch_windows=None, **ov):
+def _run(g, name, L, S, n_tokens, seed=1337, model_kw=None, batch_windows=None, streams=None, **ov):
     import torch
     cfg, model = make_case(name, seed=seed, model_kw=model_kw, **ov)
     tokens, nbytes = synth.make_stream(cfg, seed=seed, n_tokens=n_tokens)
-    print_case("score", name, ov, "L", L, "S", S, "N", n_tokens, model_kw or "")
+    print_case("score", name, ov, "L", L, "S", S, "N", n_tokens, model_kw or "", "streams", streams)
     gm, _ = gpu_model(g, model)
     if batch_windows:
         gm.set_batch_windows(batch_windows)
+    if streams:
+        gm.set_streams(streams)
     nats, totals = gm.score(torch.from_numpy(tokens).cuda(), torch.from_numpy(nbytes).cuda(), L, S)
     torch.cuda.synchronize()
     return cfg, model, tokens, nbytes, nats.cpu().numpy(), totals.cpu().numpy()
@@ -82,6 +84,18 @@ def test_batching_does_not_change_results():
     runs = [_run(g, "11l", 128, 32, 600, batch_windows=b)[4] for b in (1, 3, 64)]
     np.testing.assert_array_equal(runs[0], runs[1])
     np.testing.assert_array_equal(runs[0], runs[2])
+
+
+@pytest.mark.parametrize("name,L,S,N,bw", [("11l", 128, 32, 600, 3), ("midcycle", 128, 64, 700, 2),
+                                         ("11l_next", 256, 64, 1500, 5), ("largevocab", 200, 50, 900, 4)])
+def test_two_streams_give_identical_results(name, L, S, N, bw):
+    """Batches alternating over two streams (separate scratch) give the same
+    bits as one stream, for U-Net, stem/tail, cyclic and parallel models."""
+    g = need_gpu()
+    one = _run(g, name, L, S, N, batch_windows=bw, streams=1)
+    two = _run(g, name, L, S, N, batch_windows=bw, streams=2)
+    np.testing.assert_array_equal(one[4], two[4])
+    np.testing.assert_array_equal(one[5], two[5])
 
 
 @pytest.mark.parametrize("kw,label", [
