@@ -170,7 +170,7 @@ def main():
     tot = totals.cpu().numpy()
 
     roofline = None
-    gemm_frac = None
+    gemm_frac = attn_frac = e2e_frac = head = None
     if dom:
         ms, n, fl, by = gm.timing(dom)
         gm.set_timing(False)
@@ -191,6 +191,18 @@ def main():
         gsum_fl = sum(kernels[c]["tflops"] * kernels[c]["ms_total"] for c in ("qkv", "oproj", "fc", "proj")
                       if c in kernels)
         gemm_frac = (gsum_fl / gsum_ms) / PEAK_BF16_TFLOPS if gsum_ms else None
+        # attention and the whole pass the same way: algorithmic FLOPs over
+        # the kernel time of the instrumented warmup step, against the bf16
+        # MFMA peak; and the head + cross-entropy kernel's HBM and FLOP rates
+        if "attn" in kernels:
+            attn_frac = kernels["attn"]["tflops"] / PEAK_BF16_TFLOPS
+        all_ms = sum(v["ms_total"] for v in kernels.values())
+        all_fl = sum((v["tflops"] or 0.0) * v["ms_total"] for v in kernels.values())
+        e2e_frac = (all_fl / all_ms) / PEAK_BF16_TFLOPS if all_ms else None
+        if "head" in kernels:
+            hk = kernels["head"]
+            head = {"avg_us": hk["avg_us"], "gbs": hk["gbs"], "tflops": hk["tflops"],
+                    "frac_hbm": hk["gbs"] / PEAK_HBM_GBS, "frac_mfma": hk["tflops"] / PEAK_BF16_TFLOPS}
 
     # Stand-alone HBM-bound kernels are timed cold: before every repetition a
     # read of 512 MiB evicts their data from the 256 MB Infinity Cache (a
@@ -226,7 +238,7 @@ def main():
     if not args.no_timing:
         n_w = sum(w.numel() for wb in w_dev for w in wb.values())
         n_r = sum(w.shape[0] for wb in w_dev for w in wb.values())
-        us, warm = timed(quantize_all)
+        us, warm = timed(quantize_all, reps=100)
         quant = dict(matrices=sum(len(wb) for wb in w_dev), weights=n_w,
                      **hbm_entry(us, warm, 5.0 * n_w + 2.0 * n_r))
         quant["us_per_pass"] = us
@@ -331,6 +343,9 @@ def main():
                    "parallelism": "single GPU"},
         "bpb": float(tot[3]),
         "gemm_mfma_frac": gemm_frac,
+        "attention_mfma_frac": attn_frac,
+        "end_to_end_mfma_frac": e2e_frac,
+        "head_ce": head,
         "roofline": roofline,
         "kernels_warmup_step": kernels,
         "quantize_rows": quant,
@@ -386,7 +401,17 @@ def cpu_baseline(model, tokens, L, S, n_windows):
     dt = time.perf_counter() - t0
     scored = int(mask.sum())
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": scored / dt, "unit": "scored tokens/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model, "nproc": os.cpu_count(),
             "sample": f"{n_windows} full windows ({scored} scored predictions) from the middle of the "
                       f"stream, float64 NumPy, {dt:.1f} s"}
 
