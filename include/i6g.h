@@ -305,8 +305,16 @@ int i6g_plan_windows(int64_t n_tokens, int32_t window, int32_t stride, int64_t* 
  *                          second stream waits for the caller's earlier work
  *                          and the caller's stream waits for it before the
  *                          totals are reduced.  Results are identical.
+ *   I6G_OPT_REGISTER_CODES 1 (default): the fc and proj GEMMs load their
+ *                          weight codes, rearranged into fragment order when
+ *                          the model is loaded, straight into registers; 0:
+ *                          they stage the row-major codes through LDS like
+ *                          the q/k/v and output projections.  The
+ *                          MFMAs are the same; the per-row sums of squares
+ *                          for the next norm are added in another order, so
+ *                          results agree to fp32 rounding.
  * Errors: I6G_EINVAL for an unknown option or a value out of range. */
-enum { I6G_OPT_BATCH_WINDOWS = 0, I6G_OPT_PRUNE_LAST = 1, I6G_OPT_STREAMS = 2 };
+enum { I6G_OPT_BATCH_WINDOWS = 0, I6G_OPT_PRUNE_LAST = 1, I6G_OPT_STREAMS = 2, I6G_OPT_REGISTER_CODES = 3 };
 int i6g_set_option(i6g_model* m, int option, int64_t value);
 
 /* Per-launch kernel timing with HIP events, for measurement.  Kernel

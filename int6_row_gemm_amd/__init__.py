@@ -263,6 +263,12 @@ class Model:
         alternate with a second stream owned by the model."""
         _check(lib().i6g_set_option(self._h, 2, int(n)))
 
+    def set_register_codes(self, on):
+        """True (default): the fc and proj GEMMs load their codes,
+        rearranged at load time, straight into registers; False: they stage
+        the row-major codes through LDS."""
+        _check(lib().i6g_set_option(self._h, 3, int(bool(on))))
+
     def score(self, tokens, nbytes, window, stride, nats=None, totals=None, check=True):
         """Score a device token stream; returns (nats [N-1] fp32, totals [4] fp64)
         with totals = (sum nats, sum bytes, scored predictions, bits per byte)."""

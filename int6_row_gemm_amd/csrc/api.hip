@@ -69,6 +69,10 @@ struct DevBuf {
 
 struct BlockDev {
   DevBuf qkv_codes, qkv_scales, o_codes, o_scales, fc_codes, fc_scales, proj_codes, proj_scales;
+  // fc and proj codes in the fragment order of the register-fed GEMM path
+  // (the output projection, K = d, stays LDS-staged: its short K loop does
+  // not repay the register-fed tile's longer residual epilogue)
+  DevBuf fc_frag, proj_frag;
 };
 
 struct TimeRec {
@@ -117,6 +121,7 @@ struct i6g_model {
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   int batch_windows = 0;
   int prune_last = 1;
+  int register_codes = 1;
   // timing
   bool timing = false;
   uint32_t timing_mask = 0;
@@ -561,6 +566,11 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
         (rc = copy_in(bd.proj_codes, B.proj.codes, (size_t)d * F, s)) ||
         (rc = copy_in(bd.proj_scales, B.proj.scales, (size_t)d * 2, s)))
       return cleanup(rc);
+    if (bd.fc_frag.ensure((size_t)F * d) != hipSuccess || bd.proj_frag.ensure((size_t)d * F) != hipSuccess)
+      return cleanup(fail(I6G_ENOMEM, "load_model: out of device memory"));
+    if (launch_shuffle_codes(bd.fc_codes.as<int8_t>(), F, d, bd.fc_frag.as<int8_t>(), s) != hipSuccess ||
+        launch_shuffle_codes(bd.proj_codes.as<int8_t>(), d, F, bd.proj_frag.as<int8_t>(), s) != hipSuccess)
+      return cleanup(fail(I6G_EDEVICE, "load_model: rearranging the codes failed"));
   }
   const size_t esz = m->embed_f32 ? 4 : 2;
   if ((rc = copy_in(m->embed, D.embed, (size_t)m->V * d * esz, s))) return cleanup(rc);
@@ -621,6 +631,9 @@ int i6g_set_option(i6g_model* m, int option, int64_t value) {
     case I6G_OPT_STREAMS:
       if (value != 1 && value != 2) return fail(I6G_EINVAL, "set_option: streams must be 1 or 2");
       m->streams = (int)value;
+      return I6G_OK;
+    case I6G_OPT_REGISTER_CODES:
+      m->register_codes = value != 0;
       return I6G_OK;
   }
   return fail(I6G_EINVAL, "set_option: unknown option %d", option);
@@ -754,11 +767,13 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
 
       GemmArgs gf{};
       gf.A = sc.xb.as<bf16>(); gf.B = B.fc_codes.as<int8_t>(); gf.scale = B.fc_scales.as<uint16_t>();
+      if (m->register_codes) gf.Bp = B.fc_frag.as<int8_t>();
       gf.M = M; gf.N = F; gf.K = d; gf.ss_in = sc.ss.as<float>(); gf.nt_in = nt; gf.eps = eps;
       gf.h = sc.h.as<bf16>(); gf.leaky = m->leaky;
 
       GemmArgs gp{};
       gp.A = sc.h.as<bf16>(); gp.B = B.proj_codes.as<int8_t>(); gp.scale = B.proj_scales.as<uint16_t>();
+      if (m->register_codes) gp.Bp = B.proj_frag.as<int8_t>();
       gp.M = M; gp.N = d; gp.K = F; gp.x = sc.x.as<float>();
       if (!last) { gp.xb = sc.xb.as<bf16>(); gp.ss_out = sc.ss.as<float>(); }
       if (m->push_after[e]) gp.push_dst = sc.slots.as<float>() + (size_t)m->push_slot[e] * M * d;

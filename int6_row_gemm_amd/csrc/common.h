@@ -82,6 +82,10 @@ enum EpiKind { EPI_QKV = 0, EPI_RELU2 = 1, EPI_RES = 2 };
 struct GemmArgs {
   const bf16* A;          // [M, K]
   const int8_t* B;        // [N, K]
+  // the same codes rearranged by launch_shuffle_codes, or null; when set, the
+  // row-major epilogues (EPI_RELU2, EPI_RES) feed them from global memory
+  // straight into registers instead of staging them through LDS
+  const int8_t* Bp;
   const uint16_t* scale;  // [N] binary16
   int32_t M, N, K;
   // RMS factor of the A rows (EPI_QKV, EPI_RELU2): rinv = 1/sqrt(sum_t ss[m,t]/K + eps)
@@ -114,6 +118,9 @@ struct GemmArgs {
   int64_t p0, k0, n_win, e0;
   int32_t L, S;
 };
+// Rearranges int8 codes [N, K] (N % 128 == 0, K % 64 == 0) into the
+// fragment order of the register-fed GEMM path; Bp holds N * K bytes.
+hipError_t launch_shuffle_codes(const int8_t* B, int32_t N, int32_t K, int8_t* Bp, hipStream_t s);
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
 
 // Row of prediction p in a batch of windows k0.. laid out Lp rows apart:

@@ -13,6 +13,15 @@
 // Tiling: 256 threads = 4 waves in a 2 x 2 grid; workgroup tile BM x BN,
 // K step 64 through one XOR-swizzled LDS tile with register prefetch one K
 // step ahead; each wave issues v_mfma_f32_16x16x32_bf16 on (BM/2) x (BN/2).
+// Register-fed variant (the MLP GEMMs, when the caller passes the codes
+// rearranged by launch_shuffle_codes): only the A tile goes through LDS;
+// the waves split the tile 1 x 4 (128 x 32 each) and load their own code
+// fragments with one coalesced 16-byte load per lane and K step, widening
+// them in registers.  This halves the LDS writes of a K step, which bound
+// the staged loop on gfx950 (timing copies without the staging stores run
+// the loop at the full MFMA rate), and was measured 4-6 % faster on fc and
+// proj in the full pass; the output projection (K = 512) stays staged, its
+// short loop does not repay the longer 8-row epilogue.
 // Rows are placed in LDS so that every lane ends up owning runs of
 // consecutive output columns of one row (C^T accumulation: two runs of 8,
 // or whole rotation pairs of a q/k head), or, for the transposed V output,
@@ -88,6 +97,23 @@ __device__ inline int pair_phys(int u) {
   return 16 * (2 * (u >> 5) + ((u >> 2) & 1)) + 4 * ((u >> 3) & 3) + (u & 3);
 }
 
+// Inverse of pair_phys on a 32-column slice (pair_phys keeps each half of a
+// 64-column slice in place): the logical column stored at physical row p.
+__device__ inline int pair_logical32(int p) {
+  return (p & 3) | (((p >> 4) & 1) << 2) | (((p >> 2) & 3) << 3);
+}
+
+// Eight int8 codes (one 8-byte half of a 16-byte fragment chunk) widened to
+// the bf16 MFMA operand; exact for integers of magnitude <= 128.
+__device__ inline bf16x8 widen8(uint32_t lo, uint32_t hi) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t o = {pack_bf16x2_from_int((int)(int8_t)(lo & 0xff), (int)(int8_t)((lo >> 8) & 0xff)),
+                     pack_bf16x2_from_int((int)(int8_t)((lo >> 16) & 0xff), (int)(int8_t)(lo >> 24)),
+                     pack_bf16x2_from_int((int)(int8_t)(hi & 0xff), (int)(int8_t)((hi >> 8) & 0xff)),
+                     pack_bf16x2_from_int((int)(int8_t)((hi >> 16) & 0xff), (int)(int8_t)(hi >> 24))};
+  return __builtin_bit_cast(bf16x8, o);
+}
+
 // Rotation pairs of one q or k head with R rotated dims (partial RoPE):
 // pair p < R/2 is (p, p + R/2); the others pair up the unrotated dims as
 // (R + w, R + (hd - R)/2 + w), w = p - R/2, and turn by the identity.  For
@@ -118,9 +144,9 @@ __device__ inline int rope_phys(int u, int R) {
   return 16 * (t >> 2) + 4 * (p / Q8) + (t & 3);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, bool RB>
 struct Smem {
-  static constexpr int kBytes = (BM + BN) * LDK * 2;   // one A and one B tile
+  static constexpr int kBytes = (BM + (RB ? 0 : BN)) * LDK * 2;   // one A and (unless RB) one B tile
 };
 
 template <int N>
@@ -141,19 +167,25 @@ __device__ inline void store_bf16_run(bf16* dst, const uint16_t (&y)[N]) {
 }
 
 // Main loop and epilogue of one tile.  CT: accumulate C^T (every epilogue
-// except the V heads of the q/k/v projection, which keep C).
-template <int BM, int BN, int EPI, bool CT>
+// except the V heads of the q/k/v projection, which keep C).  RB: the
+// weight codes come pre-arranged in fragment order (shuffle_codes) and go
+// from global memory straight into each wave's registers; only the A tile
+// is staged through LDS, and the four waves split the tile 1 x 4 (128 rows
+// x 32 columns each) so that every code is still loaded once per tile.
+template <int BM, int BN, int EPI, bool CT, bool RB>
 __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs, float* rinv_s,
                                           float* scale_s, float* popw_s, float (*ss_part)[BM],
                                           int tid, int wave, int m0, int n0, int tn) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WM = RB ? BM : BM / 2, WN = RB ? BN / 4 : BN / 2;
+  constexpr int NWN = BN / WN;                // waves across the columns
   constexpr int FM = WM / 16, FN = WN / 16;
   constexpr int A_CHUNKS = BM * BK / 8;       // 16-byte chunks of bf16
-  constexpr int B_CHUNKS = BN * BK / 16;      // 16-byte chunks of int8
+  constexpr int B_CHUNKS = RB ? 0 : BN * BK / 16;   // 16-byte chunks of int8 staged through LDS
   constexpr int A_PER = (A_CHUNKS + 255) / 256;
   constexpr int B_PER = (B_CHUNKS + 255) / 256;
+  static_assert(!RB || (CT && EPI != EPI_QKV && WN == 32), "register-fed codes: row-major epilogues only");
   const int lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = RB ? 0 : wave >> 1, wn = RB ? wave : wave & 1;
   const int dq = a.n_heads * WN, dkv = a.n_kv * WN;
 
   // Global -> register staging into named scalars (arrays of them end up
@@ -236,6 +268,21 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // RB: the wave's codes of one K tile are FN chunks of 16 bytes per lane
+  // (both 32-wide halves of its fragment rows), contiguous per wave
+  uint4 bq0 = make_uint4(0, 0, 0, 0), bq1 = make_uint4(0, 0, 0, 0);
+  const int8_t* bp_wave = nullptr;
+  if constexpr (RB) {
+    static_assert(FN == 2, "two code chunks per lane");
+    bp_wave = a.Bp + ((int64_t)tn * (a.K / BK) * NWN + wn) * (FN * 64 * 16) + lane * 16;
+  }
+#define GM_BQ_LOAD(kt)                                                                \
+  if constexpr (RB) {                                                                 \
+    const int8_t* p_ = bp_wave + (int64_t)(kt) * (NWN * FN * 64 * 16);                \
+    bq0 = *reinterpret_cast<const uint4*>(p_);                                        \
+    bq1 = *reinterpret_cast<const uint4*>(p_ + 64 * 16);                              \
+  }
+
   const int lr = lane & 15, lg = lane >> 4;
   // MF_C: acc block (i, j) = C (A rows x weight rows); MF_T: its transpose.
 #define MF_C(x, w, c) __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, w, c, 0, 0, 0)
@@ -248,9 +295,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
         const int r_ = wm * WM + i * 16 + lr;                                         \
         af[i] = *reinterpret_cast<const bf16x8*>(As + r_ * LDK + swz(r_, ks * 4 + lg) * 8); \
       }                                                                               \
-      _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                \
-        const int r_ = wn * WN + j * 16 + lr;                                         \
-        bfg[j] = *reinterpret_cast<const bf16x8*>(Bs + r_ * LDK + swz(r_, ks * 4 + lg) * 8); \
+      if constexpr (RB) {                                                             \
+        bfg[0] = ks == 0 ? wb0[0] : wb1[0];                                           \
+        bfg[1] = ks == 0 ? wb0[1] : wb1[1];                                           \
+      } else {                                                                        \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j) {                              \
+          const int r_ = wn * WN + j * 16 + lr;                                       \
+          bfg[j] = *reinterpret_cast<const bf16x8*>(Bs + r_ * LDK + swz(r_, ks * 4 + lg) * 8); \
+        }                                                                             \
       }                                                                               \
       _Pragma("unroll") for (int i = 0; i < FM; ++i)                                  \
         _Pragma("unroll") for (int j = 0; j < FN; ++j)                                \
@@ -270,6 +322,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
 #define GM_STEP(kt)                                                                   \
   {                                                                                   \
     GM_LOAD(min((kt) + 1, nk - 1), 0);                                                \
+    bf16x8 wb0[2], wb1[2];   /* RB: widened codes of this K tile, by 32-wide half */  \
+    if constexpr (RB) {                                                               \
+      wb0[0] = widen8(bq0.x, bq0.y); wb1[0] = widen8(bq0.z, bq0.w);                   \
+      wb0[1] = widen8(bq1.x, bq1.y); wb1[1] = widen8(bq1.z, bq1.w);                   \
+      GM_BQ_LOAD(min((kt) + 1, nk - 1));                                              \
+    }                                                                                 \
     GM_COMPUTE_ANY();                                                                 \
     if ((kt) + 1 < nk) {                                                              \
       __syncthreads();                                                                \
@@ -279,6 +337,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
   }
 
   GM_LOAD(0, 0);
+  GM_BQ_LOAD(0);
   {
     // the per-column weight scales and per-row RMS factors (read by the
     // epilogue only) load while the first K tile is in flight
@@ -307,6 +366,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) GM_STEP(kt);
 #undef GM_STEP
+#undef GM_BQ_LOAD
 #undef GM_COMPUTE_ANY
 #undef GM_COMPUTE
 #undef MF_T
@@ -323,11 +383,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
   // and the 4 weight rows the placement above gives output rows 4lg..4lg+3
   // of fragment j; in the C orientation (v heads) it holds weight row
   // wn*WN + 16j + lr and the 16 consecutive A rows wm*WM + 16*lg + 4i + e.
-  const int lrow = 16 * (lr >> 2) + (lr & 3);   // + 4i: the lane's A row in C^T blocks
+  const int lrow = 16 * (lr >> 2) + (lr & 3);
+  // the lane's A row in C^T block i: 64-row slices of four blocks each
+  auto arow = [&](int i) { return 64 * (i >> 2) + lrow + 4 * (i & 3); };
   if constexpr (EPI == EPI_RELU2) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int ml = wm * WM + lrow + 4 * i;
+      const int ml = wm * WM + arow(i);
       const int m = m0 + ml;
       if (m >= a.M) continue;
       const float ri = rinv_s[ml];
@@ -354,22 +416,23 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
     const bool pop_self = pop && a.pop_src == a.push_dst;
     // the lane's columns: block j holds the 4 starting at colj(j)
     auto colj = [&](int j) { return wn * WN + 32 * (j >> 1) + 8 * lg + 4 * (j & 1); };
-    int64_t off[FM];
-    bool ok[FM];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int m = m0 + wm * WM + lrow + 4 * i;
-      ok[i] = m < a.M;
-      const int mm = min(m, a.M - 1);   // rows past M recompute row M-1 and store nothing
-      const int64_t mr = a.e_map ? scored_row(a.p0 + mm, a.k0, a.n_win, a.e0, a.L, a.S, a.Lp) : mm;
-      off[i] = mr * a.N + n0;
-    }
-    // the residual rows in two halves of FM/2 row blocks, each half's loads
-    // in flight together
+    // the residual rows in groups of FH row blocks (eight float4 per lane),
+    // each group's loads in flight together; row offsets per group
+    constexpr int FH = 8 / FN;
     float sq[FM];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      constexpr int FH = FM / 2;
+    for (int hh = 0; hh < FM / FH; ++hh) {
+      int64_t off[FM];
+      bool ok[FM];
+#pragma unroll
+      for (int ii = 0; ii < FH; ++ii) {
+        const int i = hh * FH + ii;
+        const int m = m0 + wm * WM + arow(i);
+        ok[i] = m < a.M;
+        const int mm = min(m, a.M - 1);   // rows past M recompute row M-1 and store nothing
+        const int64_t mr = a.e_map ? scored_row(a.p0 + mm, a.k0, a.n_win, a.e0, a.L, a.S, a.Lp) : mm;
+        off[i] = mr * a.N + n0;
+      }
       float4 xv[FH][FN];
 #pragma unroll
       for (int ii = 0; ii < FH; ++ii)
@@ -455,14 +518,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
       for (int i = 0; i < FM; ++i) {
         sq[i] += __shfl_xor(sq[i], 16);
         sq[i] += __shfl_xor(sq[i], 32);
-        if (lg == 0) ss_part[wn][wm * WM + lrow + 4 * i] = sq[i];
+        if (lg == 0) ss_part[wn][wm * WM + arow(i)] = sq[i];
       }
       __syncthreads();
       for (int r = tid; r < BM; r += 256) {
         const int m = m0 + r;
         if (m >= a.M) continue;
         const int64_t mr = a.e_map ? scored_row(a.p0 + m, a.k0, a.n_win, a.e0, a.L, a.S, a.Lp) : m;
-        a.ss_out[mr * (a.N / 128) + tn] = ss_part[0][r] + ss_part[1][r];
+        float t_ = ss_part[0][r];
+#pragma unroll
+        for (int u = 1; u < NWN; ++u) t_ += ss_part[u][r];
+        a.ss_out[mr * (a.N / 128) + tn] = t_;
       }
     }
   } else {  // EPI_QKV: BN = 2 * head_dim, each wave holds one whole head
@@ -486,7 +552,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int ml = wm * WM + lrow + 4 * i;
+        const int ml = wm * WM + arow(i);
         const int m = m0 + ml;
         if (m >= a.M) continue;
         const float ri = rinv_s[ml];
@@ -566,18 +632,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
   }
 }
 
-template <int BM, int BN, int EPI>
+template <int BM, int BN, int EPI, bool RB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BN > 128 ? 2 : 4)))
 void gemm_kernel(GemmArgs a) {
   static_assert(BM / 2 == 64, "the row placement works on 64-row slices");
   static_assert(EPI == EPI_QKV || BN / 2 == 64, "the column placement works on 64-column slices");
-  __shared__ __attribute__((aligned(16))) char smem[Smem<BM, BN>::kBytes];
+  __shared__ __attribute__((aligned(16))) char smem[Smem<BM, BN, RB>::kBytes];
   __shared__ __attribute__((aligned(16))) float rinv_s[BM];
   __shared__ __attribute__((aligned(16))) float scale_s[BN];
   __shared__ __attribute__((aligned(16))) float popw_s[BN];
-  __shared__ float ss_part[2][BM];
+  __shared__ float ss_part[RB ? 4 : 2][BM];
   bf16* As = reinterpret_cast<bf16*>(smem);
-  bf16* Bs = As + BM * LDK;
+  bf16* Bs = RB ? nullptr : As + BM * LDK;
 
   const int tid = threadIdx.x & 255;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -589,19 +655,46 @@ void gemm_kernel(GemmArgs a) {
   // q/k/v projection: BN = 2 * head_dim and the v block starts on a tile
   // boundary (an even number of kv heads), so a tile is all q/k or all v
   if (EPI == EPI_QKV && n0 >= (a.n_heads + a.n_kv) * (BN / 2))
-    gemm_body<BM, BN, EPI, false>(a, As, Bs, rinv_s, scale_s, popw_s, ss_part, tid, wave, m0, n0, tn);
+    gemm_body<BM, BN, EPI, false, false>(a, As, Bs, rinv_s, scale_s, popw_s, ss_part, tid, wave, m0, n0, tn);
   else
-    gemm_body<BM, BN, EPI, true>(a, As, Bs, rinv_s, scale_s, popw_s, ss_part, tid, wave, m0, n0, tn);
+    gemm_body<BM, BN, EPI, true, RB>(a, As, Bs, rinv_s, scale_s, popw_s, ss_part, tid, wave, m0, n0, tn);
 }
 
-template <int BM, int BN, int EPI>
+template <int BM, int BN, int EPI, bool RB = false>
 hipError_t run(const GemmArgs& a, hipStream_t s) {
   int tiles = ((a.M + BM - 1) / BM) * (a.N / BN);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI>), dim3(tiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI, RB>), dim3(tiles), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
+// Weight codes rearranged for the register-fed path: 16-byte chunk c of the
+// output is lane c % 64 of code fragment (c / 64) % 2 of wave (c / 128) % 4
+// in K tile (c / 512) % nk of column tile c / (512 nk); it holds, for the
+// logical column 32 * wave + pair_logical32(16 * fragment + lane % 16), the
+// codes of k = 64 * tile + 8 * (lane / 16) + 0..7 and the same + 32.
+__global__ __launch_bounds__(256) void shuffle_codes_kernel(const int8_t* __restrict__ B, int32_t N, int32_t K,
+                                                            int8_t* __restrict__ Bp) {
+  const int nk = K / BK;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= (int64_t)(N / 128) * nk * 512) return;
+  const int lane = (int)(c & 63), j = (int)((c >> 6) & 1), wv = (int)((c >> 7) & 3);
+  const int64_t q = c >> 9;
+  const int kt = (int)(q % nk), tn = (int)(q / nk);
+  const int row = tn * 128 + 32 * wv + pair_logical32(16 * j + (lane & 15));
+  const int8_t* src = B + (int64_t)row * K + kt * BK + 8 * (lane >> 4);
+  const uint2 lo = *reinterpret_cast<const uint2*>(src);
+  const uint2 hi = *reinterpret_cast<const uint2*>(src + 32);
+  *reinterpret_cast<uint4*>(Bp + c * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 }  // namespace
+
+hipError_t launch_shuffle_codes(const int8_t* B, int32_t N, int32_t K, int8_t* Bp, hipStream_t s) {
+  if (N <= 0 || K <= 0 || N % 128 != 0 || K % BK != 0) return hipErrorInvalidValue;
+  const int64_t chunks = (int64_t)(N / 128) * (K / BK) * 512;
+  hipLaunchKernelGGL(shuffle_codes_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, B, N, K, Bp);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   switch (epi) {
@@ -612,9 +705,9 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
       if (a.hd == 80) return run<128, 160, EPI_QKV>(a, s);
       return hipErrorInvalidValue;
     case EPI_RELU2:
-      return run<128, 128, EPI_RELU2>(a, s);
+      return a.Bp ? run<128, 128, EPI_RELU2, true>(a, s) : run<128, 128, EPI_RELU2>(a, s);
     case EPI_RES:
-      return run<128, 128, EPI_RES>(a, s);
+      return a.Bp ? run<128, 128, EPI_RES, true>(a, s) : run<128, 128, EPI_RES>(a, s);
   }
   return hipErrorInvalidValue;
 }

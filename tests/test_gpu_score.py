@@ -17,16 +17,20 @@ from gpu_common import (BPB_ATOL, NATS_RTOL, compare_nats, gpu_model, make_case,
 pytestmark = pytest.mark.gpu
 
 
-def _run(g, name, L, S, n_tokens, seed=1337, model_kw=None, batch_windows=None, streams=None, **ov):
+def _run(g, name, L, S, n_tokens, seed=1337, model_kw=None, batch_windows=None, streams=None,
+         register_codes=None, **ov):
     import torch
     cfg, model = make_case(name, seed=seed, model_kw=model_kw, **ov)
     tokens, nbytes = synth.make_stream(cfg, seed=seed, n_tokens=n_tokens)
-    print_case("score", name, ov, "L", L, "S", S, "N", n_tokens, model_kw or "", "streams", streams)
+    print_case("score", name, ov, "L", L, "S", S, "N", n_tokens, model_kw or "", "streams", streams,
+               "register_codes", register_codes)
     gm, _ = gpu_model(g, model)
     if batch_windows:
         gm.set_batch_windows(batch_windows)
     if streams:
         gm.set_streams(streams)
+    if register_codes is not None:
+        gm.set_register_codes(register_codes)
     nats, totals = gm.score(torch.from_numpy(tokens).cuda(), torch.from_numpy(nbytes).cuda(), L, S)
     torch.cuda.synchronize()
     return cfg, model, tokens, nbytes, nats.cpu().numpy(), totals.cpu().numpy()
@@ -96,6 +100,29 @@ def test_two_streams_give_identical_results(name, L, S, N, bw):
     two = _run(g, name, L, S, N, batch_windows=bw, streams=2)
     np.testing.assert_array_equal(one[4], two[4])
     np.testing.assert_array_equal(one[5], two[5])
+
+
+@pytest.mark.parametrize("name,L,S,N,ov", [("11l", 256, 64, 1000, {}), ("midcycle", 128, 128, 257, {}),
+                                          ("largevocab", 200, 50, 700, {}), ("tiny", 256, 64, 700, {}),
+                                          ("11l_next", 256, 64, 1000, {}), ("10l_int5mlp", 256, 64, 1000, {}),
+                                          ("baseline", 128, 128, 400, {"leaky_slope": 0.5})])
+def test_register_fed_codes_match_lds_staged(name, L, S, N, ov):
+    """The fc and proj GEMMs agree whether their codes come rearranged
+    straight into registers or row-major through LDS, with
+    skip pushes and pops, parallel lanes, pruning and LeakyReLU^2 covered.
+    The MFMAs are the same; only the per-row sums of squares for the next
+    norm are added in another order (four waves of 32 columns instead of two
+    of 64), so the results agree to fp32 rounding, well inside the oracle
+    tolerance, and both match the oracle."""
+    g = need_gpu()
+    lds = _run(g, name, L, S, N, register_codes=False, **ov)
+    reg = _run(g, name, L, S, N, register_codes=True, **ov)
+    np.testing.assert_allclose(reg[4], lds[4], rtol=1e-3, atol=0)
+    assert reg[5][1] == lds[5][1] and reg[5][2] == lds[5][2]
+    assert abs(reg[5][3] - lds[5][3]) <= 1e-5
+    ref, _ = _full_oracle(reg[1], reg[2], reg[3], L, S)
+    compare_nats(lds[4], ref, label=f"{name} LDS-staged codes")
+    compare_nats(reg[4], ref, label=f"{name} register-fed codes")
 
 
 @pytest.mark.parametrize("kw,label", [
