@@ -12,7 +12,7 @@ Sources (page, section):
   * pwwt.cn "parameter-golf 16MB 极限压缩实战 …", 后训练量化导出: one fp16
     scale per row; tensors below the passthrough size stay fp16.
 
-Readings (listed in the design doc): an int6 code c (a multiple of 4 in
+Readings of the pages: an int6 code c (a multiple of 4 in
 [-128, 124]) packs as the 6-bit value u = c/4 + 32; four values u0..u3 form
 the 24-bit word u0 | u1 << 6 | u2 << 12 | u3 << 18 stored as 3 bytes, least
 significant first; a tail of fewer than four codes is padded with code 0;

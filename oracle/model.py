@@ -18,7 +18,7 @@ divided by a temperature; LeakyReLU(slope)^2 in place of ReLU^2; RoPE on the
 first R dims of each head; exclusive self attention on the last N effective
 layers.
 
-Readings (listed in the design doc): pre-norm RMSNorm without gain, eps 1e-6, and a
+Readings of the pages: pre-norm RMSNorm without gain, eps 1e-6, and a
 final norm before the tied head; attention scale 1/sqrt(head_dim), no other
 logit transforms; query head h reads KV head floor(h*Hkv/Hq); RoPE on all
 head dims with half-split pairs (i, i+hd/2), theta_i = base^(-2i/hd), at

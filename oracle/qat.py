@@ -13,7 +13,7 @@ Sources (page, section):
     per row (amax floored at 1e-12), noise = (U[0, 1) - 0.5) * step; the
     write-up's closing notes name amax / 15 as the int5-matched step.
 
-Readings (listed in DESIGN.md):
+Readings of the pages:
   * fake quantisation uses the quantiser's codes at the given clip quantile
     (1.0 = the plain absolute maximum of the training-time simulation) and
     the fp32 scale, not its binary16 rounding (the training forward never

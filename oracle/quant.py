@@ -12,7 +12,7 @@ value follows the Noisy-QAT code block of the kwkr.cn PR #363 write-up
 ATTN_INT5 in its run commands), and its closing notes give the int5 step as
 amax / 15 against int8's amax / 127.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * the percentile is of |w| over the row, linear interpolation between order
     statistics (pos = q*(n-1) in binary64, lo = floor(pos), hi = min(lo+1, n-1),
     f = fp32(pos - lo));

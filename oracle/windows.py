@@ -7,7 +7,7 @@ with up to a full window of context; the plain chunked eval cuts the stream
 into independent chunks) and the pigsec.cn openai/parameter-golf README
 mirror (the score is tokenizer-agnostic bits per byte).
 
-Readings (listed in the design doc): window k starts at s_k = k*S and ends at
+Readings of the pages: window k starts at s_k = k*S and ends at
 e_k = min(s_k + L, P) with P = N-1 predictions; it scores predictions
 p in [max(s_k, e_{k-1}), e_k) (e_{-1} = 0) so window 0 scores all of its
 positions, later full windows their last S, and every prediction is scored
