@@ -102,21 +102,26 @@ def test_two_streams_give_identical_results(name, L, S, N, bw):
     np.testing.assert_array_equal(one[5], two[5])
 
 
-@pytest.mark.parametrize("name,L,S,N,ov", [("11l", 256, 64, 1000, {}), ("midcycle", 128, 128, 257, {}),
-                                          ("largevocab", 200, 50, 700, {}), ("tiny", 256, 64, 700, {}),
-                                          ("11l_next", 256, 64, 1000, {}), ("10l_int5mlp", 256, 64, 1000, {}),
-                                          ("baseline", 128, 128, 400, {"leaky_slope": 0.5})])
-def test_register_fed_codes_match_lds_staged(name, L, S, N, ov):
+@pytest.mark.parametrize("name,L,S,N,ov,kw", [
+    ("11l", 256, 64, 1000, {}, None), ("midcycle", 128, 128, 257, {}, None),
+    ("largevocab", 200, 50, 700, {}, None), ("tiny", 256, 64, 700, {}, None),
+    ("11l_next", 256, 64, 1000, {}, None), ("10l_int5mlp", 256, 64, 1000, {}, None),
+    ("baseline", 128, 128, 400, {"leaky_slope": 0.5}, None),
+    ("baseline", 128, 128, 400, {"rope_dims": 16}, None), ("baseline", 128, 128, 400, {"rope_dims": 48}, None),
+    ("11l", 256, 64, 600, {"lora_rank": 4}, dict(lora_b_std=1.0)),
+])
+def test_register_fed_codes_match_lds_staged(name, L, S, N, ov, kw):
     """The fc and proj GEMMs agree whether their codes come rearranged
-    straight into registers or row-major through LDS, with
-    skip pushes and pops, parallel lanes, pruning and LeakyReLU^2 covered.
+    straight into registers or row-major through LDS, across schedules
+    (skip pushes and pops, stem/tail, parallel lanes), pruning, partial
+    RoPE, amplified LoRA, int5 MLP codes and LeakyReLU^2.
     The MFMAs are the same; only the per-row sums of squares for the next
     norm are added in another order (four waves of 32 columns instead of two
     of 64), so the results agree to fp32 rounding, well inside the oracle
     tolerance, and both match the oracle."""
     g = need_gpu()
-    lds = _run(g, name, L, S, N, register_codes=False, **ov)
-    reg = _run(g, name, L, S, N, register_codes=True, **ov)
+    lds = _run(g, name, L, S, N, model_kw=kw, register_codes=False, **ov)
+    reg = _run(g, name, L, S, N, model_kw=kw, register_codes=True, **ov)
     np.testing.assert_allclose(reg[4], lds[4], rtol=1e-3, atol=0)
     assert reg[5][1] == lds[5][1] and reg[5][2] == lds[5][2]
     assert abs(reg[5][3] - lds[5][3]) <= 1e-5
