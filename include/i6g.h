@@ -260,7 +260,9 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out);
  *             scored predictions (P), bits per byte = sum_nats / (ln 2 *
  *             sum_bytes).
  * Errors (returned now): I6G_EINVAL for n_tokens < 2, window < 1,
- * stride < 1 or > window, NULL arrays; I6G_ENOMEM; I6G_EDEVICE.
+ * stride < 1 or > window, NULL arrays, or a current HIP device other than
+ * the one the model was loaded on (the model's memory lives there);
+ * I6G_ENOMEM; I6G_EDEVICE.
  * Errors detected on the device (token outside [0, vocab): that token is
  * read as id 0; negative byte count: counted as 0) are latched in the
  * model and returned by i6g_model_status().

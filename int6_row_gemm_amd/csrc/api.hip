@@ -656,6 +656,13 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
   if (!tokens_dev || !bytes_dev || !nats_dev || !totals_dev) return fail(I6G_EINVAL, "score_tokens: NULL array");
   if (n_tokens < 2 || window < 1 || stride < 1 || stride > window)
     return fail(I6G_EINVAL, "score_tokens: need n_tokens >= 2 and 1 <= stride <= window");
+  {
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev != m->device)
+      return fail(I6G_EINVAL, "score_tokens: the model was loaded on device %d but device %d is current", m->device,
+                  dev);
+  }
   hipStream_t s = (hipStream_t)stream;
   const int64_t P = n_tokens - 1;
   const int64_t L = window, S = stride;
