@@ -80,47 +80,67 @@ __global__ __launch_bounds__(256) void lora_down_kernel(LoraArgs a) {
 // (pwwt.cn "parameter-golf 16MB 极限压缩实战 …": tied input/output embedding;
 // 滑动窗口评估: only the scored positions of a window reach the loss).
 // A workgroup takes 16 scored predictions.  Their rows are normalised (final
-// RMSNorm) into fp16 in LDS and held by every wave as the B operand; the 4
+// RMSNorm) into fp16 in LDS and held by every wave as the B operand; the NW
 // waves split the vocabulary and stream the binary16 embedding as the A
 // operand of v_mfma_f32_16x16x32_f16, so logits^T arrive with one prediction
 // per lane column: each lane keeps an online log-sum-exp and the target
 // logit, merged over lane groups and then over the waves through LDS.
-// Logits never reach memory.
+// Logits never reach memory.  The normalised rows carry a factor log2(e), so
+// the logits come out in base 2 and each probability is one exp2; the nats
+// are ln 2 times the base-2 result.  Work per batch is small (about 1,500
+// predictions): eight waves per workgroup (two per SIMD) halve each wave's
+// chain of embedding blocks, and a wave loads all its rows for the norm at
+// once.
 constexpr int HEAD_ROWS = 16;
 
-template <int NKS>   // d / 32
-__global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
+template <int NKS, int NW>   // d / 32, waves per workgroup
+__global__ __launch_bounds__(64 * NW) void head_kernel(HeadArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 zs[HEAD_ROWS * (640 + 8)];   // d <= 640
-  __shared__ float part_m[4][HEAD_ROWS], part_s[4][HEAD_ROWS], part_t[4][HEAD_ROWS];
-  __shared__ int part_g[4][HEAD_ROWS];
-  const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
+  __shared__ float part_m[NW][HEAD_ROWS], part_s[NW][HEAD_ROWS], part_t[NW][HEAD_ROWS];
+  __shared__ int part_g[NW][HEAD_ROWS];
+  constexpr int RPW = HEAD_ROWS / NW;    // rows normalised per wave
+  constexpr int CPL = NKS / 2;           // row elements per lane (d / 64)
+  constexpr float kLog2e = 1.44269504088896340736f;
+  constexpr float kLn2 = 0.69314718055994530942f;
+  const int tid = threadIdx.x & (64 * NW - 1), lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int zld = a.d + 8;
   const int64_t pb = a.p0 + (int64_t)blockIdx.x * HEAD_ROWS;
 
-  // final norm of 4 rows per wave
-  for (int rr = wave * 4; rr < wave * 4 + 4; ++rr) {
-    const int64_t p = pb + rr;
-    _Float16* zrow = zs + rr * zld;
-    if (p < a.p1) {
-      int64_t row;
-      if (a.compact) {
-        row = p - a.p0;
-      } else {
-        int64_t k = (p < a.e0) ? 0 : (p - a.L) / a.S + 1;
-        if (k > a.K - 1) k = a.K - 1;
-        row = (k - a.k0) * a.Lp + (p - k * a.S);
+  // final norm: the wave's rows are loaded together, then reduced
+  {
+    float xv[RPW][CPL];
+    bool ok[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int64_t p = pb + wave * RPW + r;
+      ok[r] = p < a.p1;
+      int64_t row = 0;
+      if (ok[r]) {
+        if (a.compact) {
+          row = p - a.p0;
+        } else {
+          int64_t k = (p < a.e0) ? 0 : (p - a.L) / a.S + 1;
+          if (k > a.K - 1) k = a.K - 1;
+          row = (k - a.k0) * a.Lp + (p - k * a.S);
+        }
       }
       const float* xr = a.x + row * a.d;
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) xv[r][u] = ok[r] ? xr[lane + 64 * u] : 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      _Float16* zrow = zs + (wave * RPW + r) * zld;
       float sq = 0.f;
-      for (int c = lane; c < a.d; c += 64) sq += xr[c] * xr[c];
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) sq += xv[r][u] * xv[r][u];
       sq = wave_sum(sq);
       // the evaluation temperature divides every logit, so it scales the
-      // normed row once instead
-      const float rinv = 1.0f / sqrtf(sq / (float)a.d + a.eps) * a.inv_temp;
-      for (int c = lane; c < a.d; c += 64) zrow[c] = (_Float16)(xr[c] * rinv);
-    } else {
-      for (int c = lane; c < a.d; c += 64) zrow[c] = (_Float16)0.0f;
+      // normed row once instead, as does the base-2 factor
+      const float rinv = 1.0f / sqrtf(sq / (float)a.d + a.eps) * a.inv_temp * kLog2e;
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) zrow[lane + 64 * u] = (_Float16)(ok[r] ? xv[r][u] * rinv : 0.0f);
     }
   }
   __syncthreads();
@@ -137,7 +157,7 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) zf[ks] = *reinterpret_cast<const f16x8*>(zs + lr * zld + ks * 32 + 8 * lg);
 
-  const int vper = a.vocab / 4;
+  const int vper = a.vocab / NW;
   const int vlo = wave * vper, vhi = vlo + vper;
   float mrun = -1e30f, srun = 0.f, tl = 0.f;
   int got = 0;
@@ -156,8 +176,9 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
     const int vbase = vb + 4 * lg;
     const float mt = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
     const float mn = fmaxf(mrun, mt);
-    srun = srun * expf(mrun - mn) + expf(acc[0] - mn) + expf(acc[1] - mn) + expf(acc[2] - mn) +
-           expf(acc[3] - mn);
+    srun = srun * __builtin_amdgcn_exp2f(mrun - mn) + __builtin_amdgcn_exp2f(acc[0] - mn) +
+           __builtin_amdgcn_exp2f(acc[1] - mn) + __builtin_amdgcn_exp2f(acc[2] - mn) +
+           __builtin_amdgcn_exp2f(acc[3] - mn);
     mrun = mn;
     if (tgt >= vbase && tgt < vbase + 4) {
       const int i = tgt - vbase;
@@ -181,7 +202,7 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
     const float to = __shfl_xor(tl, off);
     const int go = __shfl_xor(got, off);
     const float mn = fmaxf(mrun, mo);
-    srun = srun * expf(mrun - mn) + so * expf(mo - mn);
+    srun = srun * __builtin_amdgcn_exp2f(mrun - mn) + so * __builtin_amdgcn_exp2f(mo - mn);
     mrun = mn;
     if (go) { tl = to; got = 1; }
   }
@@ -194,14 +215,14 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a) {
   __syncthreads();
   if (wave == 0 && lg == 0 && have) {
     float m = part_m[0][lr], s = part_s[0][lr], t = got ? tl : 0.f;
-    for (int w2 = 1; w2 < 4; ++w2) {
+    for (int w2 = 1; w2 < NW; ++w2) {
       const float mo = part_m[w2][lr];
       const float mn = fmaxf(m, mo);
-      s = s * expf(m - mn) + part_s[w2][lr] * expf(mo - mn);
+      s = s * __builtin_amdgcn_exp2f(m - mn) + part_s[w2][lr] * __builtin_amdgcn_exp2f(mo - mn);
       m = mn;
       if (part_g[w2][lr]) t = part_t[w2][lr];
     }
-    a.nats[p_mine] = m + logf(s) - t;
+    a.nats[p_mine] = (m + log2f(s) - t) * kLn2;
   }
 }
 
@@ -311,14 +332,21 @@ hipError_t launch_head(const HeadArgs& a, hipStream_t s) {
   int64_t rows = a.p1 - a.p0;
   if (rows <= 0) return hipSuccess;
   const dim3 grid(nblk(rows, HEAD_ROWS));
+  // eight waves when each gets whole 16-row vocabulary blocks and the
+  // registers allow two waves per SIMD (d <= 512), else four
+  const bool w8 = a.vocab % 128 == 0 && a.d <= 512;
+#define HEAD_LAUNCH(NKS)                                                                          \
+  if (w8) hipLaunchKernelGGL((head_kernel<NKS, 8>), grid, dim3(512), 0, s, a);                     \
+  else hipLaunchKernelGGL((head_kernel<NKS, 4>), grid, dim3(256), 0, s, a)
   switch (a.d) {
-    case 128: hipLaunchKernelGGL(head_kernel<4>, grid, dim3(256), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(head_kernel<8>, grid, dim3(256), 0, s, a); break;
-    case 384: hipLaunchKernelGGL(head_kernel<12>, grid, dim3(256), 0, s, a); break;
-    case 512: hipLaunchKernelGGL(head_kernel<16>, grid, dim3(256), 0, s, a); break;
-    case 640: hipLaunchKernelGGL(head_kernel<20>, grid, dim3(256), 0, s, a); break;
+    case 128: HEAD_LAUNCH(4); break;
+    case 256: HEAD_LAUNCH(8); break;
+    case 384: HEAD_LAUNCH(12); break;
+    case 512: HEAD_LAUNCH(16); break;
+    case 640: HEAD_LAUNCH(20); break;
     default: return hipErrorInvalidValue;
   }
+#undef HEAD_LAUNCH
   return hipGetLastError();
 }
 
