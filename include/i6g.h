@@ -262,7 +262,10 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out);
  * Errors (returned now): I6G_EINVAL for n_tokens < 2, window < 1,
  * stride < 1 or > window, NULL arrays, or a current HIP device other than
  * the one the model was loaded on (the model's memory lives there);
- * I6G_ENOMEM; I6G_EDEVICE.
+ * I6G_EUNSUPPORTED when one window of min(window, n_tokens - 1) positions,
+ * rounded up to 64, reaches 2^31 / max(d_model + 2*n_kv_heads*head_dim,
+ * d_ff, 2*lora_rank) rows (the kernels address a batch with 32-bit
+ * offsets); I6G_ENOMEM; I6G_EDEVICE.
  * Errors detected on the device (token outside [0, vocab): that token is
  * read as id 0; negative byte count: counted as 0) are latched in the
  * model and returned by i6g_model_status().
@@ -295,7 +298,10 @@ int i6g_plan_windows(int64_t n_tokens, int32_t window, int32_t stride, int64_t* 
 /* Model options (tuning and testing; results do not depend on them beyond
  * floating-point rounding):
  *   I6G_OPT_BATCH_WINDOWS  windows per batch in i6g_score_tokens (0 = the
- *                          default, about 49152 rows per batch);
+ *                          default, about 49152 rows per batch); an upper
+ *                          bound: a batch is also kept below 2^31 /
+ *                          max(d_model + 2*n_kv_heads*head_dim, d_ff,
+ *                          2*lora_rank) rows;
  *   I6G_OPT_PRUNE_LAST     1 (default): the final layer computes queries,
  *                          the output projection and the MLP only for the
  *                          scored rows; 0: for every row.

@@ -19,6 +19,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <climits>
 #include <string>
 #include <vector>
 
@@ -667,11 +668,20 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
   const int64_t P = n_tokens - 1;
   const int64_t L = window, S = stride;
   const int64_t K = window_count(P, L, S);
-  const int Lp = (int)((std::min<int64_t>(L, P) + 63) / 64 * 64);
+  const int64_t Lp64 = (std::min<int64_t>(L, P) + 63) / 64 * 64;
+  // The kernels address a batch's arrays with 32-bit offsets, so a batch's
+  // rows times its widest per-row array (the q|k|v projection output, the MLP
+  // hidden activations or the LoRA down-projections) must stay below 2^31.
+  const int64_t widest = std::max<int64_t>({(int64_t)m->d + 2 * m->kvd, m->F, 2 * (int64_t)m->lora_r});
+  const int64_t max_rows = INT32_MAX / widest;
+  if (Lp64 > max_rows)
+    return fail(I6G_EUNSUPPORTED, "score_tokens: a window of %lld positions exceeds the %lld rows a batch can hold "
+                "for this model", (long long)Lp64, (long long)max_rows);
+  const int Lp = (int)Lp64;
   // default batch: 49152 rows (24 windows of 2048), which splits the GEMM
   // tiles evenly over the workgroups the device holds at once
   int Wb = m->batch_windows > 0 ? m->batch_windows : std::max(1, 49152 / Lp);
-  Wb = (int)std::min<int64_t>(Wb, K);
+  Wb = (int)std::min<int64_t>({(int64_t)Wb, K, max_rows / Lp});
   int rc = ensure_scratch(m, Wb, Lp, s);
   if (rc) return rc;
 
