@@ -136,10 +136,12 @@ def artifact_bytes(matrices, passthrough_elements: int, bits=None) -> int:
 def dequantize_f32(codes: np.ndarray, scale16: np.ndarray) -> np.ndarray:
     """code * scale per row (fp32).  The product of an int8 code and a
     binary16 scale has at most 19 significant bits, so the fp32 result is
-    the exact product (computed in fp64, then converted)."""
+    the exact product (computed in fp64, then converted).  A zero code times
+    an infinite scale is NaN, as IEEE multiplication defines it."""
     c = np.asarray(codes, dtype=np.float64)
     s = np.asarray(scale16, dtype=np.float16).astype(np.float64)
-    return (c * s[:, None]).astype(np.float32)
+    with np.errstate(invalid="ignore"):
+        return (c * s[:, None]).astype(np.float32)
 
 
 def dequantize_bf16(codes: np.ndarray, scale16: np.ndarray) -> np.ndarray:
