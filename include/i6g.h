@@ -263,9 +263,10 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out);
  * stride < 1 or > window, NULL arrays, or a current HIP device other than
  * the one the model was loaded on (the model's memory lives there);
  * I6G_EUNSUPPORTED when one window of min(window, n_tokens - 1) positions,
- * rounded up to 64, reaches 2^31 / max(d_model + 2*n_kv_heads*head_dim,
- * d_ff, 2*lora_rank) rows (the kernels address a batch with 32-bit
- * offsets); I6G_ENOMEM; I6G_EDEVICE.
+ * rounded up to 64, exceeds the rows a batch can hold (row and tile
+ * indices are 32-bit in the kernels): at most 2^24 - 1, and at most
+ * 128 * floor((2^31 - 1) / ceil(w / 64)) for w = max(d_model +
+ * 2*n_kv_heads*head_dim, d_ff); I6G_ENOMEM; I6G_EDEVICE.
  * Errors detected on the device (token outside [0, vocab): that token is
  * read as id 0; negative byte count: counted as 0) are latched in the
  * model and returned by i6g_model_status().
@@ -299,9 +300,8 @@ int i6g_plan_windows(int64_t n_tokens, int32_t window, int32_t stride, int64_t* 
  * floating-point rounding):
  *   I6G_OPT_BATCH_WINDOWS  windows per batch in i6g_score_tokens (0 = the
  *                          default, about 49152 rows per batch); an upper
- *                          bound: a batch is also kept below 2^31 /
- *                          max(d_model + 2*n_kv_heads*head_dim, d_ff,
- *                          2*lora_rank) rows;
+ *                          bound: a batch is also kept within the rows
+ *                          i6g_score_tokens can index (at most 2^24 - 1);
  *   I6G_OPT_PRUNE_LAST     1 (default): the final layer computes queries,
  *                          the output projection and the MLP only for the
  *                          scored rows; 0: for every row.

@@ -669,11 +669,13 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
   const int64_t L = window, S = stride;
   const int64_t K = window_count(P, L, S);
   const int64_t Lp64 = (std::min<int64_t>(L, P) + 63) / 64 * 64;
-  // The kernels address a batch's arrays with 32-bit offsets, so a batch's
-  // rows times its widest per-row array (the q|k|v projection output, the MLP
-  // hidden activations or the LoRA down-projections) must stay below 2^31.
-  const int64_t widest = std::max<int64_t>({(int64_t)m->d + 2 * m->kvd, m->F, 2 * (int64_t)m->lora_r});
-  const int64_t max_rows = INT32_MAX / widest;
+  // Element offsets are 64-bit in the kernels, but row indices, a window's
+  // position x head_dim offsets (head_dim <= 80) and GEMM tile indices
+  // (rows / 128 down, tiles at least 64 columns wide across) are 32-bit: a
+  // batch holds fewer than 2^24 rows and fewer than 2^31 tiles of its widest
+  // GEMM.
+  const int64_t widest = std::max<int64_t>((int64_t)m->d + 2 * m->kvd, m->F);
+  const int64_t max_rows = std::min<int64_t>(INT32_MAX / 128, 128 * (INT32_MAX / ((widest + 63) / 64)));
   if (Lp64 > max_rows)
     return fail(I6G_EUNSUPPORTED, "score_tokens: a window of %lld positions exceeds the %lld rows a batch can hold "
                 "for this model", (long long)Lp64, (long long)max_rows);

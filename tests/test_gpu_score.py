@@ -90,35 +90,42 @@ def test_batching_does_not_change_results():
     np.testing.assert_array_equal(runs[0], runs[2])
 
 
-def test_batch_rows_capped_for_32bit_offsets():
-    """The kernels address one batch with 32-bit offsets.  With a 65536-wide
-    MLP a batch holds at most 2^31 // 65536 = 32767 rows, so windows of 16384
-    positions run one per batch whatever the batch option asks (three would
-    address 3.2e9 hidden elements): the bits equal an explicit one-window
-    batch, and window 0's first 256 predictions equal the oracle on that
-    prefix (causally they see nothing later).  A window of 32768 positions
-    is refused before anything runs."""
+def test_batch_rows_capped_at_the_index_limit():
+    """Row and tile indices are 32-bit in the kernels, so a batch holds at
+    most 2^24 - 1 rows.  A stream of 2^24 + 1024 tokens in windows of 64,
+    with 2^20 windows per batch asked for, runs as a batch of 262,143
+    windows (16,777,152 rows) and one of 17: the bits equal the default
+    batching (768 windows per batch), sampled windows on both sides of the
+    batch boundary equal the oracle, and a window of 2^24 positions is
+    refused."""
     import torch
     g = need_gpu()
-    cfg, model = make_case("tiny", mlp_mult=512)
-    L, n = 16384, 3 * 16384 + 1
-    tokens, nbytes = synth.make_stream(cfg, seed=7, n_tokens=n)
+    cfg, model = make_case("tiny")
+    n, L = (1 << 24) + 1024, 64
+    tokens, nbytes = synth.make_stream(cfg, seed=11, n_tokens=n)
     gm, _ = gpu_model(g, model)
     t, b = torch.from_numpy(tokens).cuda(), torch.from_numpy(nbytes).cuda()
-    print_case("score", "tiny", "d_ff", cfg["arch"]["d_ff"], "L", L, "S", L, "N", n, "batch default, then 1")
+    print_case("score", "tiny", "L", L, "S", L, "N", n, "batch default")
     nats_d, tot_d = gm.score(t, b, L, L)
-    gm.set_batch_windows(1)
-    nats_1, tot_1 = gm.score(t, b, L, L)
-    torch.cuda.synchronize()
-    np.testing.assert_array_equal(nats_d.cpu().numpy(), nats_1.cpu().numpy())
-    np.testing.assert_array_equal(tot_d.cpu().numpy(), tot_1.cpu().numpy())
-    assert tot_d[2].item() == n - 1
-    ref, mask = ow.score(oracle_quantized(model), tokens[:257], 256, 256)
-    assert mask.all()
-    compare_nats(nats_d[:256].cpu().numpy(), ref, label="d_ff 65536, window 16384, first 256")
-    print_case("score", "tiny", "d_ff", cfg["arch"]["d_ff"], "L", 2 * L, "refused")
-    with pytest.raises(g.I6GError, match="exceeds the 32767 rows"):
-        gm.score(t[:2 * L + 1], b[:2 * L + 1], 2 * L, 2 * L)
+    nats_d, tot_d = nats_d.cpu().numpy(), tot_d.cpu().numpy()
+    gm.set_batch_windows(1 << 20)
+    print_case("score", "tiny", "L", L, "S", L, "N", n, "batch 2^20 windows asked")
+    nats_c, tot_c = gm.score(t, b, L, L)
+    nats_c, tot_c = nats_c.cpu().numpy(), tot_c.cpu().numpy()
+    np.testing.assert_array_equal(nats_d, nats_c)
+    np.testing.assert_array_equal(tot_d, tot_c)
+    P = n - 1
+    assert tot_c[2] == P
+    qm = oracle_quantized(model)
+    K = 1 + -(-(P - L) // L)
+    for k in (0, 262142, 262143, K - 1):
+        s0, e = L * k, min(L * k + L, P)
+        ref, mask = ow.score(qm, tokens[s0:e + 1], L, L)
+        assert mask.all()
+        compare_nats(nats_c[s0:e], ref, label=f"window {k} of {K}")
+    print_case("score", "tiny", "L", 1 << 24, "refused")
+    with pytest.raises(g.I6GError, match="exceeds the 16777215 rows"):
+        gm.score(t, b, 1 << 24, 1 << 24)
 
 
 @pytest.mark.parametrize("name,L,S,N,bw", [("11l", 128, 32, 600, 3), ("midcycle", 128, 64, 700, 2),
