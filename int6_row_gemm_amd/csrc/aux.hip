@@ -62,16 +62,33 @@ __global__ __launch_bounds__(256) void lora_down_kernel(LoraArgs a) {
   const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= a.M) return;
   const float* xr = a.x + m * a.d;
-  float sq = 0.f;
-  for (int c = lane; c < a.d; c += 64) sq += xr[c] * xr[c];
-  sq = wave_sum(sq);
-  const float rinv = 1.0f / sqrtf(sq / (float)a.d + a.eps);
-  for (int t = 0; t < 2 * a.r; ++t) {
-    const float* ar = (t < a.r ? a.aq + t * a.d : a.av + (t - a.r) * a.d);
-    float acc = 0.f;
-    for (int c = lane; c < a.d; c += 64) acc += xr[c] * ar[c];
-    acc = wave_sum(acc);
-    if (lane == 0) a.u[m * 2 * a.r + t] = acc * rinv;
+  const int nt = 2 * a.r;
+  float rinv = 0.f;
+  // The row is read once per group of eight adapter rows (once for rank <= 4)
+  // with 8-byte loads (d is a multiple of 128), and the eight dot products
+  // and the sum of squares are reduced over the wave together.
+  for (int t0 = 0; t0 < nt; t0 += 8) {
+    float acc[8] = {};
+    float sq = 0.f;
+    for (int c = 2 * lane; c < a.d; c += 128) {
+      const float2 xv = *reinterpret_cast<const float2*>(xr + c);
+      sq += xv.x * xv.x + xv.y * xv.y;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = t0 + j;
+        if (t < nt) {
+          const float* ar = t < a.r ? a.aq + (int64_t)t * a.d : a.av + (int64_t)(t - a.r) * a.d;
+          const float2 av = *reinterpret_cast<const float2*>(ar + c);
+          acc[j] += xv.x * av.x + xv.y * av.y;
+        }
+      }
+    }
+    if (t0 == 0) rinv = 1.0f / sqrtf(wave_sum(sq) / (float)a.d + a.eps);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = wave_sum(acc[j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (lane == j && t0 + j < nt) a.u[m * nt + t0 + j] = acc[j] * rinv;
   }
 }
 

@@ -565,15 +565,24 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
           x2[t] = acc[i][(t + Q8) >> 2][(t + Q8) & 3] * sc2[t] * ri;
         }
         if (lora) {
+          // rank <= 8: the row's u and each column's B row are read with
+          // unrolled, guarded loads so that they are all in flight at once
           const float* uu = a.lora_u + (int64_t)m * 2 * a.lora_r;
+          float ur[8] = {};
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            if (r < a.lora_r) ur[r] = uu[r];
 #pragma unroll
           for (int t = 0; t < Q8; ++t) {
-            const int g1 = colbase + f0 + t, g2 = colbase + s0 + t;
+            const float* b1 = a.lora_bq + (int64_t)(colbase + f0 + t) * a.lora_r;
+            const float* b2 = a.lora_bq + (int64_t)(colbase + s0 + t) * a.lora_r;
             float s1 = 0.f, s2 = 0.f;
-            for (int r = 0; r < a.lora_r; ++r) {
-              s1 += uu[r] * a.lora_bq[g1 * a.lora_r + r];
-              s2 += uu[r] * a.lora_bq[g2 * a.lora_r + r];
-            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+              if (r < a.lora_r) {
+                s1 += ur[r] * b1[r];
+                s2 += ur[r] * b2[r];
+              }
             x1[t] += s1;
             x2[t] += s2;
           }
@@ -609,6 +618,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
         for (int j = 0; j < FN; ++j) {
           const int dd = 16 * j + lr;
           const float sc = scale_s[wn * HD + dd];
+          // rank <= 8: the column's B row once, then each row's u, with
+          // unrolled, guarded loads (all in flight at once)
+          float bvr[8] = {};
+          if (lora) {
+            const float* bv = a.lora_bv + (int64_t)(head * HD + dd) * a.lora_r;
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+              if (r < a.lora_r) bvr[r] = bv[r];
+          }
           uint16_t y[16];
 #pragma unroll
           for (int t = 0; t < 16; ++t) {
@@ -616,7 +634,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
             if (lora) {
               const float* uu = a.lora_u + (int64_t)(mb + t) * 2 * a.lora_r + a.lora_r;
               float sl = 0.f;
-              for (int r = 0; r < a.lora_r; ++r) sl += uu[r] * a.lora_bv[(head * HD + dd) * a.lora_r + r];
+#pragma unroll
+              for (int r = 0; r < 8; ++r)
+                if (r < a.lora_r) sl += uu[r] * bvr[r];
               v += sl;
             }
             y[t] = f2bf_bits(v);
