@@ -65,21 +65,36 @@ __global__ __launch_bounds__(256) void lora_down_kernel(LoraArgs a) {
   const int nt = 2 * a.r;
   float rinv = 0.f;
   // The row is read once per group of eight adapter rows (once for rank <= 4)
-  // with 8-byte loads (d is a multiple of 128), and the eight dot products
-  // and the sum of squares are reduced over the wave together.
+  // in blocks of 1024 columns, each lane's eight 8-byte loads of a block
+  // issued together (d is a multiple of 128); the eight dot products and the
+  // sum of squares are reduced over the wave together.
   for (int t0 = 0; t0 < nt; t0 += 8) {
     float acc[8] = {};
     float sq = 0.f;
-    for (int c = 2 * lane; c < a.d; c += 128) {
-      const float2 xv = *reinterpret_cast<const float2*>(xr + c);
-      sq += xv.x * xv.x + xv.y * xv.y;
+    for (int c0 = 0; c0 < a.d; c0 += 1024) {
+      float2 xv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        xv[i] = make_float2(0.f, 0.f);
+        const int c = c0 + 128 * i + 2 * lane;
+        if (c < a.d) xv[i] = *reinterpret_cast<const float2*>(xr + c);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sq += xv[i].x * xv[i].x + xv[i].y * xv[i].y;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int t = t0 + j;
         if (t < nt) {
           const float* ar = t < a.r ? a.aq + (int64_t)t * a.d : a.av + (int64_t)(t - a.r) * a.d;
-          const float2 av = *reinterpret_cast<const float2*>(ar + c);
-          acc[j] += xv.x * av.x + xv.y * av.y;
+          float2 av[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            av[i] = make_float2(0.f, 0.f);
+            const int c = c0 + 128 * i + 2 * lane;
+            if (c < a.d) av[i] = *reinterpret_cast<const float2*>(ar + c);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[j] += xv[i].x * av[i].x + xv[i].y * av[i].y;
         }
       }
     }
