@@ -86,7 +86,9 @@ enum { I6G_DTYPE_F16 = 0, I6G_DTYPE_F32 = 1, I6G_DTYPE_BF16 = 2 };
  * scales_dev     [rows] binary16 bit patterns output, device (caller-owned).
  * flags_dev      optional device int32; I6G_FLAG_NONFINITE is OR-ed in when
  *                a row holds NaN/Inf (that row's codes are then 0 and its
- *                scale is the binary16 NaN 0x7e00).  May be NULL.
+ *                scale is the binary16 NaN 0x7e00).  May be NULL: the flag
+ *                then goes to the library's own latch on the current device,
+ *                which i6g_weights_status() reports as I6G_ENONFINITE.
  * Errors: I6G_EINVAL for rows/cols < 1, bits not in {5, 6, 8}, quantile out of
  * (0, 1] or a NULL array; I6G_EUNSUPPORTED if cols - floor(pos) > 8 (the
  * kernel keeps the 8 largest |w| of a row) or cols > 65536.
@@ -117,6 +119,18 @@ int i6g_quantize_rows_many(const i6g_quant_job* jobs, int32_t n_jobs, int bits, 
                            int32_t* flags_dev, void* stream);
 
 /*
+ * i6g_weights_status -- synchronise `stream`, then report and clear the
+ * library's non-finite latch of the current device: I6G_ENONFINITE if any
+ * i6g_quantize_rows, i6g_quantize_rows_many, i6g_fake_quantize_rows or
+ * i6g_noisy_weights call made with flags_dev NULL on this device met a
+ * NaN/Inf weight since the last report ([11L] 后训练量化导出: every exported
+ * row has a finite binary16 scale, so such a row cannot be exported), else
+ * I6G_OK.  The latch is shared by every caller on the device.
+ * Errors: I6G_EDEVICE if the runtime calls fail.
+ */
+int i6g_weights_status(void* stream);
+
+/*
  * Forward-only quantisation-aware weights (the training forward's view of a
  * weight matrix; no backward pass is involved).
  *
@@ -126,8 +140,8 @@ int i6g_quantize_rows_many(const i6g_quant_job* jobs, int32_t n_jobs, int bits, 
  * the plain absolute maximum of the training-time simulation) but the fp32
  * scale, not its binary16 rounding: out = code * scale in fp32 (one
  * rounding), or that value rounded to bfloat16 (nearest even).  A row with
- * NaN/Inf gives NaN outputs and sets I6G_FLAG_NONFINITE in *flags_dev (may
- * be NULL).  out_dev [rows, cols] fp32 or bf16.  Errors as
+ * NaN/Inf gives NaN outputs and sets I6G_FLAG_NONFINITE in *flags_dev (NULL:
+ * in the latch read by i6g_weights_status).  out_dev [rows, cols] fp32 or bf16.  Errors as
  * i6g_quantize_rows, and I6G_EINVAL for an unknown out_dtype.
  */
 int i6g_fake_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int bits, double clip_quantile,
@@ -141,7 +155,8 @@ int i6g_fake_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int b
  * Moraes, Dror, Shaw, SC 2011) at key (seed low 32 bits, seed high 32 bits)
  * and counter (i / 4 low 32 bits, i / 4 high 32 bits, 0, 0), i = r * cols + c.
  * Output fp32, or bfloat16 (nearest even).  A row with NaN/Inf gives NaN
- * outputs and sets I6G_FLAG_NONFINITE.  w_dev and out_dev must be 16-byte
+ * outputs and sets I6G_FLAG_NONFINITE in *flags_dev (NULL: in the latch read
+ * by i6g_weights_status).  w_dev and out_dev must be 16-byte
  * aligned.  Errors: I6G_EINVAL for rows/cols < 1, levels not positive and
  * finite, an unknown out_dtype or a NULL array; I6G_EUNSUPPORTED for
  * misaligned buffers.
@@ -196,7 +211,7 @@ typedef struct {
  * Evaluation variants ([363]: EVAL_TEMPERATURE, LeakyReLU, Partial RoPE
  * 16/64, XSA on the last layers); zero selects the base model:
  * logit_temperature  the logits are divided by it before the log-softmax
- *                    (0 or 1 = off; otherwise > 0).
+ *                    (0 or 1 = off; otherwise >= 0.01).
  * leaky_slope        MLP activation leaky_relu(z, slope)^2 (0 = ReLU^2).
  * rope_dims          RoPE on the first rope_dims dims of each head: pairs
  *                    (i, i + rope_dims/2), theta_i = base^(-2i/rope_dims);
@@ -235,7 +250,12 @@ typedef struct i6g_model i6g_model; /* opaque, owned by the library */
  * free everything `desc` points to once the stream has synchronised.
  * Errors: I6G_EINVAL (inconsistent sizes, bad schedule or skip plan, NULL
  * tensors), I6G_EUNSUPPORTED (head_dim, head ratio or tile alignment not
- * supported), I6G_ENOMEM, I6G_EDEVICE.  On error *out is NULL.
+ * supported; a logit_temperature in (0, 0.01): the head holds the normed
+ * row times log2(e) / temperature in binary16), I6G_ENONFINITE (a NaN or Inf
+ * row scale, embedding value, skip weight, LoRA factor or bigram value:
+ * checked on the host before any allocation for tensors in host memory, and
+ * on the device after the copy for the others), I6G_ENOMEM, I6G_EDEVICE.
+ * On error *out is NULL.
  */
 int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out);
 

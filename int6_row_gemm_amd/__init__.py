@@ -22,7 +22,7 @@ SKIP_KINDS = {"none": 0, "unet": 1, "stem_tail": 2}
 KERNEL_CLASSES = ["embed", "qkv", "attn", "oproj", "fc", "proj", "head", "reduce", "lora"]
 
 EXPORTED = [
-    "i6g_quantize_rows", "i6g_quantize_rows_many", "i6g_load_model", "i6g_score_tokens", "i6g_model_status",
+    "i6g_quantize_rows", "i6g_quantize_rows_many", "i6g_weights_status", "i6g_load_model", "i6g_score_tokens", "i6g_model_status",
     "i6g_free_model", "i6g_last_error", "i6g_plan_windows", "i6g_set_option",
     "i6g_set_timing", "i6g_get_timing",
     "i6g_pack_codes", "i6g_unpack_codes", "i6g_dequantize_rows", "i6g_dequantize_packed",
@@ -86,6 +86,7 @@ def lib():
         vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
         L.i6g_quantize_rows.argtypes = [vp, i64, i64, ctypes.c_int, dbl, vp, vp, vp, vp]
         L.i6g_quantize_rows_many.argtypes = [vp, i32, ctypes.c_int, dbl, vp, vp]
+        L.i6g_weights_status.argtypes = [vp]
         L.i6g_load_model.argtypes = [vp, vp, ctypes.POINTER(vp)]
         L.i6g_score_tokens.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, vp]
         L.i6g_model_status.argtypes = [vp, vp]
@@ -134,10 +135,19 @@ def plan_windows(n_tokens, window, stride):
     return st, en, sf
 
 
-def quantize_rows(w, bits, clip_quantile, flags=None):
+def weights_status():
+    """Synchronise the current stream and raise I6GError (I6G_ENONFINITE)
+    if a quantiser or QAT call made without a flag tensor met NaN / Inf."""
+    _check(lib().i6g_weights_status(_stream()))
+
+
+def quantize_rows(w, bits, clip_quantile, flags=None, check=True):
     """Row-quantise a device fp32 matrix.  Returns (codes int8, scales) where
     ``scales`` is an int16 tensor holding binary16 bit patterns
-    (``scales.view(torch.float16)`` reads them)."""
+    (``scales.view(torch.float16)`` reads them).  Without a ``flags`` tensor
+    a NaN / Inf row raises I6GError (I6G_ENONFINITE) after a stream
+    synchronisation (``check=False`` leaves that to a later
+    weights_status())."""
     import torch
     if not (w.is_cuda and w.dtype == torch.float32 and w.dim() == 2):
         raise ValueError("w must be a 2-D float32 CUDA tensor")
@@ -147,6 +157,8 @@ def quantize_rows(w, bits, clip_quantile, flags=None):
     scales = torch.empty((rows,), dtype=torch.int16, device=w.device)
     _check(lib().i6g_quantize_rows(_ptr(w), rows, cols, bits, float(clip_quantile),
                                    _ptr(codes), _ptr(scales), _ptr(flags), _stream()))
+    if flags is None and check:
+        weights_status()
     return codes, scales
 
 
@@ -316,7 +328,8 @@ def matrix_bits(arch, name):
 
 def quantize_model(model, flags=None):
     """Quantise every block matrix of a synthetic model on the GPU; returns
-    a list of dicts name -> (codes, scales) of device tensors."""
+    a list of dicts name -> (codes, scales) of device tensors.  Without a
+    ``flags`` tensor a NaN / Inf weight raises I6GError (I6G_ENONFINITE)."""
     import torch
     arch = model["arch"]
     out = []
@@ -324,8 +337,10 @@ def quantize_model(model, flags=None):
         qb = {}
         for name, w in blk.items():
             wt = _dev(w, torch.float32)
-            qb[name] = quantize_rows(wt, matrix_bits(arch, name), arch["clip_q"], flags)
+            qb[name] = quantize_rows(wt, matrix_bits(arch, name), arch["clip_q"], flags, check=False)
         out.append(qb)
+    if flags is None:
+        weights_status()
     return out
 
 
@@ -515,6 +530,8 @@ def fake_quantize_rows(w, bits, clip_quantile=1.0, dtype=None, flags=None):
     out = torch.empty(w.shape, dtype=dtype, device=w.device)
     _check(lib().i6g_fake_quantize_rows(_ptr(w), w.shape[0], w.shape[1], bits, float(clip_quantile),
                                         _dq_dtype(dtype), _ptr(out), _ptr(flags), _stream()))
+    if flags is None:
+        weights_status()
     return out
 
 
@@ -529,4 +546,6 @@ def noisy_weights(w, levels, seed, dtype=None, flags=None):
     out = torch.empty(w.shape, dtype=dtype, device=w.device)
     _check(lib().i6g_noisy_weights(_ptr(w), w.shape[0], w.shape[1], float(levels), int(seed) & (2 ** 64 - 1),
                                    _dq_dtype(dtype), _ptr(out), _ptr(flags), _stream()))
+    if flags is None:
+        weights_status()
     return out

@@ -20,6 +20,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -88,6 +89,66 @@ int64_t window_count(int64_t P, int64_t L, int64_t S) {
 
 int64_t window_end(int64_t k, int64_t P, int64_t L, int64_t S) {
   return std::min(k * S + L, P);
+}
+
+// Library-owned non-finite latch, one copy per device: the quantiser and the
+// forward-QAT kernels OR I6G_FLAG_NONFINITE into it when the caller passes
+// no flag word of its own; i6g_weights_status() reports and clears it.  Host
+// code uses the address hipGetSymbolAddress returns for the current device.
+__device__ int32_t g_weight_latch;
+constexpr int kMaxDevices = 64;
+std::mutex g_latch_mu;
+int32_t* g_latch_ptr[kMaxDevices] = {};
+
+int latch_address(int32_t** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(I6G_EDEVICE, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_latch_mu);
+  if (!g_latch_ptr[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(g_weight_latch)));
+    g_latch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_latch_ptr[dev];
+  return I6G_OK;
+}
+
+// The caller's flag word, or the current device's latch when it passes none.
+int flag_word(int32_t* flags_dev, int32_t** out) {
+  if (flags_dev) {
+    *out = flags_dev;
+    return I6G_OK;
+  }
+  return latch_address(out);
+}
+
+// True when p is plain or pinned host memory (or the HIP runtime cannot
+// tell, which means no device memory exists to be confused with): such
+// tensors of a model descriptor are checked for NaN / Inf on the host before
+// anything is allocated; device tensors are checked on the device after the
+// copy.
+bool host_readable(const void* p) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return at.type == hipMemoryTypeHost || at.type == hipMemoryTypeUnregistered;
+}
+
+bool host_nonfinite_f16(const uint16_t* p, int64_t n) {
+  if (!p || !host_readable(p)) return false;
+  for (int64_t i = 0; i < n; ++i)
+    if ((p[i] & 0x7c00u) == 0x7c00u) return true;
+  return false;
+}
+
+bool host_nonfinite_f32(const float* p, int64_t n) {
+  if (!p || !host_readable(p)) return false;
+  for (int64_t i = 0; i < n; ++i)
+    if (!std::isfinite(p[i])) return true;
+  return false;
 }
 
 }  // namespace
@@ -305,11 +366,13 @@ int i6g_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int bits, 
   int rc = quant_plan("quantize_rows", w_dev, codes_dev, scales_dev, rows, cols, bits, clip_quantile,
                       &topk, &frac);
   if (rc) return rc;
+  int32_t* flags = nullptr;
+  if ((rc = flag_word(flags_dev, &flags))) return rc;
   QuantArgs a{};
   a.w = w_dev;
   a.codes = codes_dev;
   a.scales = scales_dev;
-  a.flags = flags_dev;
+  a.flags = flags;
   a.rows = rows;
   a.cols = (int32_t)cols;
   a.bits = bits;
@@ -333,11 +396,13 @@ int i6g_quantize_rows_many(const i6g_quant_job* jobs, int32_t n_jobs, int bits, 
     plan[j].w = J.w; plan[j].codes = J.codes; plan[j].scales = J.scales;
     plan[j].cols = (int32_t)J.cols;
   }
+  int32_t* flags = nullptr;
+  if (int rc = flag_word(flags_dev, &flags)) return rc;
   for (int j0 = 0; j0 < n_jobs; j0 += kQuantJobs) {
     QuantManyArgs a{};
     a.n = std::min(kQuantJobs, n_jobs - j0);
     a.bits = bits;
-    a.flags = flags_dev;
+    a.flags = flags;
     a.row0[0] = 0;
     for (int j = 0; j < a.n; ++j) {
       a.job[j] = plan[j0 + j];
@@ -359,9 +424,11 @@ int i6g_fake_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int b
   if (rc) return rc;
   if (out_dtype != I6G_DTYPE_F32 && out_dtype != I6G_DTYPE_BF16)
     return fail(I6G_EINVAL, "fake_quantize_rows: out_dtype must be I6G_DTYPE_F32 or I6G_DTYPE_BF16");
+  int32_t* flags = nullptr;
+  if ((rc = flag_word(flags_dev, &flags))) return rc;
   QuantArgs a{};
   a.w = w_dev;
-  a.flags = flags_dev;
+  a.flags = flags;
   a.rows = rows;
   a.cols = (int32_t)cols;
   a.bits = bits;
@@ -383,10 +450,12 @@ int i6g_noisy_weights(const float* w_dev, int64_t rows, int64_t cols, double lev
     return fail(I6G_EINVAL, "noisy_weights: out_dtype must be I6G_DTYPE_F32 or I6G_DTYPE_BF16");
   if (!aligned(w_dev, 16) || !aligned(out_dev, 16))
     return fail(I6G_EUNSUPPORTED, "noisy_weights: w and out must be 16-byte aligned");
+  int32_t* flags = nullptr;
+  if (int rc = flag_word(flags_dev, &flags)) return rc;
   NoisyArgs a{};
   a.w = w_dev;
   a.out = out_dev;
-  a.flags = flags_dev;
+  a.flags = flags;
   a.rows = rows;
   a.cols = (int32_t)cols;
   a.out_bf16 = out_dtype == I6G_DTYPE_BF16;
@@ -394,6 +463,17 @@ int i6g_noisy_weights(const float* w_dev, int64_t rows, int64_t cols, double lev
   a.key0 = (uint32_t)seed;
   a.key1 = (uint32_t)(seed >> 32);
   HIP_TRY(launch_noisy_weights(a, (hipStream_t)stream));
+  return I6G_OK;
+}
+
+int i6g_weights_status(void* stream) {
+  int32_t* latch = nullptr;
+  if (int rc = latch_address(&latch)) return rc;
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream));
+  int32_t f = 0;
+  HIP_TRY(hipMemcpy(&f, latch, 4, hipMemcpyDeviceToHost));
+  if (f) HIP_TRY(hipMemset(latch, 0, 4));
+  if (f & I6G_FLAG_NONFINITE) return fail(I6G_ENONFINITE, "a weight row held NaN or Inf");
   return I6G_OK;
 }
 
@@ -511,6 +591,11 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
       return fail(I6G_EINVAL, "load_model: schedule[%d] = %d out of range", e, D.schedule[e]);
   if (!(D.logit_temperature >= 0.0) || !std::isfinite(D.logit_temperature))
     return fail(I6G_EINVAL, "load_model: logit_temperature must be finite and >= 0 (0 = off)");
+  // The head scales each normed row (elements up to sqrt(d_model) <= 25.3)
+  // by log2(e) / temperature and holds it in binary16 (largest finite 65504):
+  // temperatures of at least 0.01 keep that product below 3,700.
+  if (D.logit_temperature != 0.0 && D.logit_temperature < 0.01)
+    return fail(I6G_EUNSUPPORTED, "load_model: logit_temperature below 0.01 is not supported");
   if (!std::isfinite(D.leaky_slope)) return fail(I6G_EINVAL, "load_model: leaky_slope must be finite");
   if (D.xsa_last_n < 0 || D.xsa_last_n > D.n_eff)
     return fail(I6G_EINVAL, "load_model: xsa_last_n must be in 0..n_eff");
@@ -518,6 +603,33 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
     return fail(I6G_EINVAL, "load_model: rope_dims must be in 0..head_dim");
   if (D.rope_dims != 0 && D.rope_dims % (D.head_dim / 4))
     return fail(I6G_EUNSUPPORTED, "load_model: rope_dims %d is not a multiple of head_dim/4", D.rope_dims);
+
+  // NaN / Inf in a tensor held in host memory: refused before anything is
+  // allocated (device tensors are checked on the device after their copy)
+  {
+    const int kvd = D.n_kv_heads * D.head_dim;
+    for (int b = 0; b < D.n_unique; ++b) {
+      const i6g_block& B = D.blocks[b];
+      const i6g_matrix* mats[6] = {&B.q, &B.k, &B.v, &B.o, &B.fc, &B.proj};
+      const int rows[6] = {D.d_model, kvd, kvd, D.d_model, D.d_ff, D.d_model};
+      for (int i = 0; i < 6; ++i)
+        if (host_nonfinite_f16(mats[i]->scales, rows[i]))
+          return fail(I6G_ENONFINITE, "load_model: block %d matrix %d has a NaN or Inf scale", b, i);
+    }
+    const int64_t nE = (int64_t)D.vocab * D.d_model;
+    if (D.embed_dtype == I6G_DTYPE_F32 ? host_nonfinite_f32((const float*)D.embed, nE)
+                                       : host_nonfinite_f16((const uint16_t*)D.embed, nE))
+      return fail(I6G_ENONFINITE, "load_model: the embedding holds NaN or Inf");
+    const int64_t ne = D.n_eff, r = D.lora_rank;
+    if ((D.skip_kind != I6G_SKIP_NONE && host_nonfinite_f16(D.skip_weights, (int64_t)D.n_skip * D.d_model)) ||
+        (r > 0 && (host_nonfinite_f16(D.lora_aq, ne * r * D.d_model) ||
+                   host_nonfinite_f16(D.lora_bq, ne * D.d_model * r) ||
+                   host_nonfinite_f16(D.lora_av, ne * r * D.d_model) || host_nonfinite_f16(D.lora_bv, ne * kvd * r))) ||
+        (D.bigram_buckets > 0 &&
+         (host_nonfinite_f16(D.bigram_table, (int64_t)D.bigram_buckets * D.bigram_dim) ||
+          host_nonfinite_f16(D.bigram_proj, (int64_t)D.d_model * D.bigram_dim))))
+      return fail(I6G_ENONFINITE, "load_model: a skip, LoRA or bigram tensor holds NaN or Inf");
+  }
 
   i6g_model* m = new i6g_model();
   m->V = D.vocab; m->d = D.d_model; m->Hq = D.n_heads; m->Hkv = D.n_kv_heads; m->hd = D.head_dim;
@@ -541,6 +653,17 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
 
   auto cleanup = [&](int code) { delete m; return code; };
   const int d = m->d, F = m->F, kvd = m->kvd;
+  if (m->flags.ensure(4) != hipSuccess || m->part_n.ensure(256 * 8) != hipSuccess ||
+      m->part_b.ensure(256 * 8) != hipSuccess)
+    return cleanup(fail(I6G_ENOMEM, "out of device memory"));
+  if (hipMemsetAsync(m->flags.p, 0, 4, s) != hipSuccess) return cleanup(fail(I6G_EDEVICE, "memset"));
+  int32_t* fl = m->flags.as<int32_t>();
+  // the device copies of every floating-point tensor are checked for NaN /
+  // Inf (bit 1 of the model's flag word), read back at the end of the load
+  auto check = [&](const DevBuf& b, int64_t n, bool f32) -> int {
+    if (launch_check_finite(b.p, n, f32, fl, s) != hipSuccess) return fail(I6G_EDEVICE, "finite check failed");
+    return I6G_OK;
+  };
   m->blocks.resize(m->n_unique);
   for (int b = 0; b < m->n_unique; ++b) {
     const i6g_block& B = D.blocks[b];
@@ -572,9 +695,13 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
     if (launch_shuffle_codes(bd.fc_codes.as<int8_t>(), F, d, bd.fc_frag.as<int8_t>(), s) != hipSuccess ||
         launch_shuffle_codes(bd.proj_codes.as<int8_t>(), d, F, bd.proj_frag.as<int8_t>(), s) != hipSuccess)
       return cleanup(fail(I6G_EDEVICE, "load_model: rearranging the codes failed"));
+    if ((rc = check(bd.qkv_scales, m->nqkv, false)) || (rc = check(bd.o_scales, d, false)) ||
+        (rc = check(bd.fc_scales, F, false)) || (rc = check(bd.proj_scales, d, false)))
+      return cleanup(rc);
   }
   const size_t esz = m->embed_f32 ? 4 : 2;
   if ((rc = copy_in(m->embed, D.embed, (size_t)m->V * d * esz, s))) return cleanup(rc);
+  if ((rc = check(m->embed, (int64_t)m->V * d, m->embed_f32 != 0))) return cleanup(rc);
   if (m->embed_f32) {
     if (m->embed16.ensure((size_t)m->V * d * 2) != hipSuccess) return cleanup(fail(I6G_ENOMEM, "embed16"));
     if (launch_f32_to_f16(m->embed.as<float>(), m->embed16.as<_Float16>(), (int64_t)m->V * d, s) != hipSuccess)
@@ -587,6 +714,7 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
     if (dst.ensure((size_t)n * 4) != hipSuccess) return fail(I6G_ENOMEM, "out of device memory");
     if (launch_f16_to_f32(tmp.as<uint16_t>(), dst.as<float>(), n, s) != hipSuccess)
       return fail(I6G_EDEVICE, "f16 conversion failed");
+    if (int r2 = check(dst, n, true)) return r2;
     if (hipStreamSynchronize(s) != hipSuccess) return fail(I6G_EDEVICE, "sync failed");
     return I6G_OK;
   };
@@ -606,13 +734,18 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
     if (launch_bigram_table(tmp.as<uint16_t>(), t2.as<uint16_t>(), m->bigram.as<float>(), m->buckets,
                             m->bigram_dim, d, s) != hipSuccess)
       return cleanup(fail(I6G_EDEVICE, "bigram table kernel failed"));
+    // a NaN or Inf in the table or the projection reaches the product table
+    if ((rc = check(m->bigram, (int64_t)m->buckets * d, true))) return cleanup(rc);
     if (hipStreamSynchronize(s) != hipSuccess) return cleanup(fail(I6G_EDEVICE, "sync failed"));
   }
-  if (m->flags.ensure(4) != hipSuccess || m->part_n.ensure(256 * 8) != hipSuccess ||
-      m->part_b.ensure(256 * 8) != hipSuccess)
-    return cleanup(fail(I6G_ENOMEM, "out of device memory"));
-  if (hipMemsetAsync(m->flags.p, 0, 4, s) != hipSuccess) return cleanup(fail(I6G_EDEVICE, "memset"));
   if (hipStreamSynchronize(s) != hipSuccess) return cleanup(fail(I6G_EDEVICE, "sync failed"));
+  {
+    int32_t f = 0;
+    if (hipMemcpy(&f, fl, 4, hipMemcpyDeviceToHost) != hipSuccess) return cleanup(fail(I6G_EDEVICE, "flag read"));
+    if (f & I6G_FLAG_NONFINITE)
+      return cleanup(fail(I6G_ENONFINITE, "load_model: a scale, the embedding or a skip, LoRA or bigram tensor "
+                                          "holds NaN or Inf"));
+  }
   *out = m;
   return I6G_OK;
 }

@@ -1,6 +1,7 @@
 // Embedding gather, LoRA down-projection, tied head + cross-entropy, the
 // bits-per-byte reduction, and the constant tables built at load time.
 #include "common.h"
+#include <algorithm>
 
 namespace i6g {
 namespace {
@@ -344,6 +345,23 @@ __global__ void f32_to_f16_kernel(const float* in, _Float16* out, int64_t n) {
   if (i < n) out[i] = (_Float16)in[i];
 }
 
+// OR I6G_FLAG_NONFINITE into *flags when any of n values is NaN or Inf
+// (binary16 bit patterns or fp32): a loaded model must not hold non-finite
+// scales or passthrough tensors.
+__global__ void nonfinite_f16_kernel(const uint16_t* p, int64_t n, int32_t* flags) {
+  int bad = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    bad |= (p[i] & 0x7c00u) == 0x7c00u;
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flags, 1);
+}
+
+__global__ void nonfinite_f32_kernel(const float* p, int64_t n, int32_t* flags) {
+  int bad = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    bad |= (__builtin_bit_cast(uint32_t, p[i]) & 0x7f800000u) == 0x7f800000u;
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(flags, 1);
+}
+
 inline unsigned nblk(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
 
 }  // namespace
@@ -414,6 +432,14 @@ hipError_t launch_f16_to_f32(const uint16_t* in, float* out, int64_t n, hipStrea
 hipError_t launch_f32_to_f16(const float* in, _Float16* out, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(f32_to_f16_kernel, dim3(nblk(n, 256)), dim3(256), 0, s, in, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_finite(const void* p, int64_t n, bool f32, int32_t* flags, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<int64_t>(nblk(n, 256), 1024);
+  if (f32) hipLaunchKernelGGL(nonfinite_f32_kernel, dim3(blocks), dim3(256), 0, s, (const float*)p, n, flags);
+  else hipLaunchKernelGGL(nonfinite_f16_kernel, dim3(blocks), dim3(256), 0, s, (const uint16_t*)p, n, flags);
   return hipGetLastError();
 }
 

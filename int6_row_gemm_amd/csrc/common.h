@@ -207,6 +207,9 @@ hipError_t launch_bigram_table(const uint16_t* table, const uint16_t* proj, floa
                                int32_t buckets, int32_t dim, int32_t d, hipStream_t s);
 hipError_t launch_f16_to_f32(const uint16_t* in, float* out, int64_t n, hipStream_t s);
 hipError_t launch_f32_to_f16(const float* in, _Float16* out, int64_t n, hipStream_t s);
+// ORs bit 1 (I6G_FLAG_NONFINITE) into *flags if any of n binary16 (f32 =
+// false) or fp32 values is NaN or Inf.
+hipError_t launch_check_finite(const void* p, int64_t n, bool f32, int32_t* flags, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Export side: bit packing of int6 codes (3 bytes per 4) and int5 codes (5

@@ -202,3 +202,64 @@ def test_qat_entry_points_validate_without_gpu():
     assert L.i6g_noisy_weights(fake, 4, 4, 127.0, 1, 3, fake, null, null) == -1
     assert L.i6g_noisy_weights(odd, 4, 4, 127.0, 1, 1, fake, null, null) == -6
     assert L.i6g_noisy_weights(fake, 4, 4, 127.0, 1, 1, odd, null, null) == -6
+
+
+def _host_desc(g, nan_at=None):
+    """A well-formed 512-wide, one-block descriptor whose tensors are all in
+    host memory; ``nan_at`` puts one NaN into the named tensor."""
+    V, d, Hq, Hkv, hd, F = 1024, 512, 8, 4, 64, 1536
+    kvd = Hkv * hd
+    keep = []
+    blocks = (g._Block * 1)()
+    for name, (rows, cols) in dict(q=(d, d), k=(kvd, d), v=(kvd, d), o=(d, d), fc=(F, d), proj=(d, F)).items():
+        c = np.zeros((rows, cols), np.int8)
+        s = np.full(rows, 0.01, np.float16)
+        if nan_at == name:
+            s[rows // 2] = np.nan
+        keep += [c, s]
+        setattr(blocks[0], name, g._Matrix(c.ctypes.data, s.ctypes.data))
+    emb = np.full((V, d), 0.02, np.float16)
+    if nan_at == "embed":
+        emb[3, 7] = np.inf
+    skip = np.ones((1, d), np.float16)
+    if nan_at == "skip":
+        skip[0, 0] = -np.inf
+    sched = (ctypes.c_int32 * 2)(0, 0)
+    keep += [emb, skip, sched]
+    D = g._Desc()
+    D.vocab, D.d_model, D.n_heads, D.n_kv_heads, D.head_dim, D.d_ff = V, d, Hq, Hkv, hd, F
+    D.rope_base, D.norm_eps = 10000.0, 1e-6
+    D.n_unique, D.n_eff = 1, 2
+    D.schedule = ctypes.cast(sched, ctypes.c_void_p)
+    D.blocks = ctypes.cast(blocks, ctypes.c_void_p)
+    D.embed_dtype, D.embed = 0, emb.ctypes.data
+    D.skip_kind, D.n_skip, D.skip_weights = 1, 1, skip.ctypes.data
+    return D, (blocks, keep)
+
+
+@pytest.mark.parametrize("where", ["q", "v", "fc", "proj", "embed", "skip"])
+def test_load_model_rejects_nonfinite_host_tensors(where):
+    """A NaN or Inf row scale, embedding value or skip weight in host memory
+    is refused with I6G_ENONFINITE before anything is allocated (so this
+    runs without a GPU): [11L] 后训练量化导出 gives every row one finite
+    binary16 scale."""
+    g, L = _lib()
+    D, keep = _host_desc(g, nan_at=where)
+    out = ctypes.c_void_p(0)
+    assert L.i6g_load_model(ctypes.byref(D), None, ctypes.byref(out)) == -4
+    assert out.value is None
+    assert "NaN or Inf" in L.i6g_last_error().decode()
+
+
+def test_load_model_temperature_floor():
+    """Temperatures in (0, 0.01) are refused: the head keeps the normed row
+    times log2(e) / temperature in binary16, which would overflow."""
+    g, L = _lib()
+    D, keep = _host_desc(g, nan_at="q")
+    out = ctypes.c_void_p(0)
+    for t in (0.005, 1e-4):
+        D.logit_temperature = t
+        assert L.i6g_load_model(ctypes.byref(D), None, ctypes.byref(out)) == -6
+        assert "temperature" in L.i6g_last_error().decode()
+    D.logit_temperature = 0.01          # accepted: the NaN scale is what fails next
+    assert L.i6g_load_model(ctypes.byref(D), None, ctypes.byref(out)) == -4

@@ -103,3 +103,31 @@ def test_many_matrices_in_one_call_bit_exact():
                 rc, rs = oq.quantize_rows(wn, bits, q)
                 np.testing.assert_array_equal(codes.cpu().numpy(), rc)
                 np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint16), rs.view(np.uint16))
+
+
+def test_default_binding_path_raises_on_nonfinite_weights():
+    """Without a flag tensor the quantiser's NaN/Inf flag goes to the
+    library's latch and the binding raises I6G_ENONFINITE; the latch is then
+    clear, so the next finite model quantises without error."""
+    import synth
+    g = need_gpu()
+    cfg = synth.config("tiny")
+    model = synth.make_model(cfg["arch"], seed=5)
+    model["blocks"][1]["fc"][7, 3] = np.nan
+    print_case("quantize_model", "tiny with a NaN weight, default flags")
+    with pytest.raises(g.I6GError) as ei:
+        g.quantize_model(model)
+    assert ei.value.code == -4
+    model["blocks"][1]["fc"][7, 3] = 0.0
+    q = g.quantize_model(model)
+    g.weights_status()
+    # a NaN scale on the device is refused by load_model
+    bad = [dict(qb) for qb in q]
+    s = bad[0]["o"][1].clone()
+    s[5] = 0x7e00
+    bad[0]["o"] = (bad[0]["o"][0], s)
+    print_case("load", "tiny with a NaN scale on the device")
+    with pytest.raises(g.I6GError) as ei:
+        g.load(model, bad)
+    assert ei.value.code == -4
+    g.load(model, q)

@@ -469,3 +469,107 @@ def test_cyclic_schedule_config():
     push, pop = om.skip_plan(a)
     assert push == [True] * 5 + [False] * 6
     assert pop == [-1] * 5 + [0, 1, 2, 3, 4, -1]
+
+
+# ---------------------------------------------------------------------------
+# Hand-worked pins for three readings that end-to-end comparisons cannot see:
+# the parallel residual lanes (pigsec.cn README mirror, leaderboard: parallel
+# attention/MLP residual lanes), no bigram term at window position 0
+# (kwkr.cn PR #363 write-up, BigramHash: the hash needs the previous token),
+# and the final weightless RMSNorm before the tied head (pwwt.cn 11L write-up,
+# 架构: tied input/output embedding).
+# ---------------------------------------------------------------------------
+
+def _context_free_qmodel(E, bigram=None, buckets=0, dim=0):
+    """A d = 2, one-block model whose six matrices all have zero codes, so
+    every block adds exactly 0 to the residual stream (q = k = v = 0, the
+    attention output is 0, relu(0)^2 = 0): its logits depend only on the
+    embedding layer, the bigram term and the head."""
+    V, d = E.shape
+    arch = dict(vocab=V, d_model=d, n_heads=1, n_kv_heads=1, head_dim=d, d_ff=d, rope_base=10000.0,
+                norm_eps=0.0, schedule=[0], n_unique=1, n_eff=1, skip_kind="none", n_skip=0,
+                parallel=False, lora_rank=0, bigram_buckets=buckets, bigram_dim=dim, temperature=1.0,
+                leaky_slope=0.0, rope_dims=None, xsa_last_n=0)
+    one = np.ones(d, dtype=np.float16)
+    qb = {n: (np.zeros((d, d), dtype=np.int8), one) for n in ("q", "k", "v", "o", "fc", "proj")}
+    return dict(arch=arch, qblocks=[qb], embed=E, skip_w=None, lora=None, bigram=bigram)
+
+
+_E4 = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0], [2.0, -1.0]])
+
+
+def test_parallel_lanes_hand_example():
+    """d = 2, one token, eps = 0, x = (3, 4): a = N(x) = (3, 4)/sqrt(12.5) =
+    (0.6 sqrt2, 0.8 sqrt2).  With one position the softmax weight is 1, so
+    with Wv = I the attention output is a, and Wo = [[0, 1], [1, 0]] swaps it:
+    attn = (0.8 sqrt2, 0.6 sqrt2).  fc = diag(1, -1), proj = I:
+    MLP(a) = (relu(0.6 sqrt2)^2, 0) = (0.72, 0).
+    Parallel lanes: x + attn + MLP(a) = (3.72 + 0.8 sqrt2, 4 + 0.6 sqrt2)
+    = (4.851370850, 4.848528137).
+    The sequential form feeds the MLP N(x + attn) = N(4.131371, 4.848528)
+    instead, giving (4.9726585, 4.8485281); a mutation that re-normalises
+    after attention, drops either lane, or adds a lane twice fails here."""
+    r2 = math.sqrt(2.0)
+    W = {"q": np.eye(2), "k": np.eye(2), "v": np.eye(2), "o": np.array([[0.0, 1.0], [1.0, 0.0]]),
+         "fc": np.diag([1.0, -1.0]), "proj": np.eye(2)}
+    arch = dict(n_heads=1, n_kv_heads=1, head_dim=2, norm_eps=0.0, rope_base=10000.0, parallel=True)
+    x = np.array([[3.0, 4.0]])
+    par = om.block_forward(x, W, arch)
+    np.testing.assert_allclose(par, [[3.72 + 0.8 * r2, 4.0 + 0.6 * r2]], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(par, [[4.851370850, 4.848528137]], rtol=0, atol=1e-9)
+    seq = om.block_forward(x, W, dict(arch, parallel=False))
+    x1 = np.array([3.0 + 0.8 * r2, 4.0 + 0.6 * r2])
+    n1 = x1[0] / math.sqrt((x1[0] ** 2 + x1[1] ** 2) / 2.0)
+    np.testing.assert_allclose(seq, [[x1[0] + n1 * n1, x1[1]]], rtol=0, atol=1e-13)
+    assert abs(seq[0, 0] - par[0, 0]) > 0.1
+    # the large-vocabulary configuration is the one that runs parallel lanes
+    assert synth.config("largevocab")["arch"]["parallel"] is True
+    assert all(not synth.config(n)["arch"]["parallel"] for n in ("tiny", "baseline", "11l", "midcycle"))
+
+
+def test_bigram_absent_at_window_position_zero():
+    """Context-free model, V = 4, d = 2, bigram table of 8 buckets x 1 with
+    every row non-zero (B[h] = (h + 1) / 2) and projection P = (1, -1)^T.
+    Window u = (1, 2): position 1 hashes (1 * 1000003 + 2) mod 8 = 5, so
+    x0[1] = E[2] + P B[5] = (1, 1) + 3 (1, -1) = (4, -2); position 0 has no
+    previous token and keeps x0[0] = E[1] = (0, 1) exactly (a term from any
+    bucket would change it).  Logits are N(x0) E^T:
+    row 0 = sqrt2 (0, 1, 1, -1); row 1 = (4, -2)/sqrt10 . E^T
+    = (4, -2, 2, 10)/sqrt10."""
+    table = ((np.arange(8, dtype=np.float64) + 1.0) / 2.0)[:, None]
+    proj = np.array([[1.0], [-1.0]])
+    qm = _context_free_qmodel(_E4, {"table": table, "proj": proj}, buckets=8, dim=1)
+    assert (1 * 1000003 + 2) % 8 == 5
+    lg = om.window_logits(qm, np.array([1, 2]))
+    r2, r10 = math.sqrt(2.0), math.sqrt(10.0)
+    np.testing.assert_allclose(lg[0], [0.0, r2, r2, -r2], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lg[1], np.array([4.0, -2.0, 2.0, 10.0]) / r10, rtol=0, atol=1e-14)
+    # the same window without the bigram: row 1 becomes N(1, 1) E^T = (1, 1, 2, 1)
+    lg0 = om.window_logits(_context_free_qmodel(_E4), np.array([1, 2]))
+    np.testing.assert_allclose(lg0[1], [1.0, 1.0, 2.0, 1.0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lg0[0], lg[0], rtol=0, atol=0)
+
+
+def test_final_norm_before_tied_head_hand_example():
+    """Context-free model: the logits are N(E[u]) E^T with the weightless
+    RMSNorm of the final residual.  u = (3, 0): E[3] = (2, -1),
+    N = (2, -1)/sqrt(2.5), logits = (2, -1, 1, 5)/sqrt(2.5)
+    = (1.2649111, -0.6324555, 0.6324555, 3.1622777); E[0] = (1, 0),
+    N = (sqrt2, 0), logits = sqrt2 (1, 0, 1, 2).  Without the final norm they
+    would be (2, -1, 1, 5) and (1, 0, 1, 2).  The nats of predicting token 0
+    after u0 = 3 are logsumexp(row 0) - row0[0], computed here by hand."""
+    qm = _context_free_qmodel(_E4)
+    lg = om.window_logits(qm, np.array([3, 0]))
+    s = math.sqrt(2.5)
+    np.testing.assert_allclose(lg[0], [2.0 / s, -1.0 / s, 1.0 / s, 5.0 / s], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lg[0], [1.2649111, -0.6324555, 0.6324555, 3.1622777], rtol=0, atol=1e-7)
+    np.testing.assert_allclose(lg[1], [math.sqrt(2.0), 0.0, math.sqrt(2.0), 2.0 * math.sqrt(2.0)],
+                               rtol=0, atol=1e-14)
+    tokens = np.array([3, 0, 2])
+    nats, mask = ow.score(qm, tokens, 2, 2)
+    assert mask.all()
+    row0 = [2.0 / s, -1.0 / s, 1.0 / s, 5.0 / s]
+    want0 = math.log(sum(math.exp(v) for v in row0)) - row0[0]
+    row1 = [math.sqrt(2.0), 0.0, math.sqrt(2.0), 2.0 * math.sqrt(2.0)]
+    want1 = math.log(sum(math.exp(v) for v in row1)) - row1[2]
+    np.testing.assert_allclose(nats, [want0, want1], rtol=0, atol=1e-13)
