@@ -50,7 +50,7 @@ typedef enum {
 
 /* Bits of the device flag word written by kernels (see i6g_quantize_rows and
  * i6g_model_status). */
-enum { I6G_FLAG_NONFINITE = 1, I6G_FLAG_TOKEN = 2, I6G_FLAG_BYTES = 4, I6G_FLAG_CODE = 8 };
+enum { I6G_FLAG_NONFINITE = 1, I6G_FLAG_TOKEN = 2, I6G_FLAG_BYTES = 4, I6G_FLAG_CODE = 8, I6G_FLAG_RANGE = 16 };
 
 enum { I6G_SKIP_NONE = 0, I6G_SKIP_UNET = 1, I6G_SKIP_STEM_TAIL = 2 };
 enum { I6G_DTYPE_F16 = 0, I6G_DTYPE_F32 = 1, I6G_DTYPE_BF16 = 2 };
@@ -297,7 +297,12 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
                      double* totals_dev, void* stream);
 
 /* Synchronise `stream`, then return and clear the device-side error latch of
- * `m`: I6G_ETOKEN, I6G_EBYTES or I6G_OK. */
+ * `m`: I6G_ETOKEN, I6G_EBYTES, I6G_EUNSUPPORTED or I6G_OK.  I6G_EUNSUPPORTED
+ * (I6G_FLAG_RANGE): the scoring pass holds its GEMM inputs, q, k, v, the
+ * attention probabilities and output and the MLP hidden values in binary16
+ * (fp32 accumulation; the residual stream itself is fp32), and a residual
+ * row whose sum of squares reached 65504^2 or an MLP hidden value of 65504
+ * or more was met; the nats of that call are not valid. */
 int i6g_model_status(i6g_model* m, void* stream);
 
 /* Release a model and its scratch.  NULL is ignored.  The caller must have
@@ -341,15 +346,25 @@ int i6g_plan_windows(int64_t n_tokens, int32_t window, int32_t stride, int64_t* 
  *                          MFMAs are the same; the per-row sums of squares
  *                          for the next norm are added in another order, so
  *                          results agree to fp32 rounding.
+ *   I6G_OPT_FUSED_TAIL     1 (default): for d_model = 512 (and streams of
+ *                          fewer than 2^31 tokens) each block's output
+ *                          projection, norm and MLP run as one kernel per
+ *                          128-row tile, the hidden activations never
+ *                          leaving the chip; 0: as three GEMM launches.  The
+ *                          same products in another rounding order: results
+ *                          agree to fp32 rounding of the residual.
  * Errors: I6G_EINVAL for an unknown option or a value out of range. */
-enum { I6G_OPT_BATCH_WINDOWS = 0, I6G_OPT_PRUNE_LAST = 1, I6G_OPT_STREAMS = 2, I6G_OPT_REGISTER_CODES = 3 };
+enum {
+  I6G_OPT_BATCH_WINDOWS = 0, I6G_OPT_PRUNE_LAST = 1, I6G_OPT_STREAMS = 2, I6G_OPT_REGISTER_CODES = 3,
+  I6G_OPT_FUSED_TAIL = 4
+};
 int i6g_set_option(i6g_model* m, int option, int64_t value);
 
 /* Per-launch kernel timing with HIP events, for measurement.  Kernel
  * classes: */
 enum {
   I6G_K_EMBED = 0, I6G_K_QKV = 1, I6G_K_ATTN = 2, I6G_K_OPROJ = 3, I6G_K_FC = 4,
-  I6G_K_PROJ = 5, I6G_K_HEAD = 6, I6G_K_REDUCE = 7, I6G_K_LORA = 8, I6G_K_COUNT = 9
+  I6G_K_PROJ = 5, I6G_K_HEAD = 6, I6G_K_REDUCE = 7, I6G_K_LORA = 8, I6G_K_TAIL = 9, I6G_K_COUNT = 10
 };
 /* enable != 0 records an event pair around every launch of the classes in
  * `class_mask` (bit i = class i) in later i6g_score_tokens calls; counters

@@ -19,7 +19,7 @@ I6G_OK = 0
 STATUS = {0: "I6G_OK", -1: "I6G_EINVAL", -2: "I6G_ENOMEM", -3: "I6G_EDEVICE",
           -4: "I6G_ENONFINITE", -5: "I6G_ETOKEN", -6: "I6G_EUNSUPPORTED", -7: "I6G_EBYTES"}
 SKIP_KINDS = {"none": 0, "unet": 1, "stem_tail": 2}
-KERNEL_CLASSES = ["embed", "qkv", "attn", "oproj", "fc", "proj", "head", "reduce", "lora"]
+KERNEL_CLASSES = ["embed", "qkv", "attn", "oproj", "fc", "proj", "head", "reduce", "lora", "tail"]
 
 EXPORTED = [
     "i6g_quantize_rows", "i6g_quantize_rows_many", "i6g_weights_status", "i6g_load_model", "i6g_score_tokens", "i6g_model_status",
@@ -280,6 +280,11 @@ class Model:
         rearranged at load time, straight into registers; False: they stage
         the row-major codes through LDS."""
         _check(lib().i6g_set_option(self._h, 3, int(bool(on))))
+
+    def set_fused_tail(self, on):
+        """True (default): output projection, norm and MLP of each block as
+        one kernel (d_model 512); False: three GEMM launches."""
+        _check(lib().i6g_set_option(self._h, 4, int(bool(on))))
 
     def score(self, tokens, nbytes, window, stride, nats=None, totals=None, check=True):
         """Score a device token stream; returns (nats [N-1] fp32, totals [4] fp64)

@@ -72,9 +72,11 @@ struct DevBuf {
 struct BlockDev {
   DevBuf qkv_codes, qkv_scales, o_codes, o_scales, fc_codes, fc_scales, proj_codes, proj_scales;
   // fc and proj codes in the fragment order of the register-fed GEMM path
-  // (the output projection, K = d, stays LDS-staged: its short K loop does
-  // not repay the register-fed tile's longer residual epilogue)
-  DevBuf fc_frag, proj_frag;
+  // (the output projection, K = d, stays LDS-staged there: its short K loop
+  // does not repay the register-fed tile's longer residual epilogue); the
+  // fused block tail reads o, fc and proj in fragment order (o and proj rows
+  // with a zero scale as zero codes)
+  DevBuf fc_frag, proj_frag, o_frag;
 };
 
 struct TimeRec {
@@ -184,6 +186,7 @@ struct i6g_model {
   int batch_windows = 0;
   int prune_last = 1;
   int register_codes = 1;
+  int fused_tail = 1;
   // timing
   bool timing = false;
   uint32_t timing_mask = 0;
@@ -690,10 +693,14 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
         (rc = copy_in(bd.proj_codes, B.proj.codes, (size_t)d * F, s)) ||
         (rc = copy_in(bd.proj_scales, B.proj.scales, (size_t)d * 2, s)))
       return cleanup(rc);
-    if (bd.fc_frag.ensure((size_t)F * d) != hipSuccess || bd.proj_frag.ensure((size_t)d * F) != hipSuccess)
+    if (bd.fc_frag.ensure((size_t)F * d) != hipSuccess || bd.proj_frag.ensure((size_t)d * F) != hipSuccess ||
+        bd.o_frag.ensure((size_t)d * d) != hipSuccess)
       return cleanup(fail(I6G_ENOMEM, "load_model: out of device memory"));
-    if (launch_shuffle_codes(bd.fc_codes.as<int8_t>(), F, d, bd.fc_frag.as<int8_t>(), s) != hipSuccess ||
-        launch_shuffle_codes(bd.proj_codes.as<int8_t>(), d, F, bd.proj_frag.as<int8_t>(), s) != hipSuccess)
+    if (launch_shuffle_codes(bd.fc_codes.as<int8_t>(), F, d, nullptr, bd.fc_frag.as<int8_t>(), s) != hipSuccess ||
+        launch_shuffle_codes(bd.proj_codes.as<int8_t>(), d, F, bd.proj_scales.as<uint16_t>(),
+                             bd.proj_frag.as<int8_t>(), s) != hipSuccess ||
+        launch_shuffle_codes(bd.o_codes.as<int8_t>(), d, d, bd.o_scales.as<uint16_t>(), bd.o_frag.as<int8_t>(),
+                             s) != hipSuccess)
       return cleanup(fail(I6G_EDEVICE, "load_model: rearranging the codes failed"));
     if ((rc = check(bd.qkv_scales, m->nqkv, false)) || (rc = check(bd.o_scales, d, false)) ||
         (rc = check(bd.fc_scales, F, false)) || (rc = check(bd.proj_scales, d, false)))
@@ -769,6 +776,9 @@ int i6g_set_option(i6g_model* m, int option, int64_t value) {
     case I6G_OPT_REGISTER_CODES:
       m->register_codes = value != 0;
       return I6G_OK;
+    case I6G_OPT_FUSED_TAIL:
+      m->fused_tail = value != 0;
+      return I6G_OK;
   }
   return fail(I6G_EINVAL, "set_option: unknown option %d", option);
 }
@@ -781,6 +791,9 @@ int i6g_model_status(i6g_model* m, void* stream) {
   HIP_TRY(hipMemset(m->flags.p, 0, 4));
   if (f & I6G_FLAG_TOKEN) return fail(I6G_ETOKEN, "a token id was outside [0, vocab)");
   if (f & I6G_FLAG_BYTES) return fail(I6G_EBYTES, "negative byte count or zero total bytes");
+  if (f & I6G_FLAG_RANGE)
+    return fail(I6G_EUNSUPPORTED, "an activation left the binary16 range (a residual row with a sum of squares "
+                                  "of at least 65504^2, or an MLP hidden value of at least 65504)");
   return I6G_OK;
 }
 
@@ -813,9 +826,12 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
     return fail(I6G_EUNSUPPORTED, "score_tokens: a window of %lld positions exceeds the %lld rows a batch can hold "
                 "for this model", (long long)Lp64, (long long)max_rows);
   const int Lp = (int)Lp64;
-  // default batch: 49152 rows (24 windows of 2048), which splits the GEMM
-  // tiles evenly over the workgroups the device holds at once
-  int Wb = m->batch_windows > 0 ? m->batch_windows : std::max(1, 49152 / Lp);
+  // The fused block tail (d_model 512) runs one 128-row tile per CU: a
+  // batch of 65536 rows (32 windows of 2048) is two full waves of 256 tiles.
+  // Without it, 49152 rows (24 windows) split the separate GEMMs' tiles
+  // evenly over the workgroups the device holds at once.
+  const bool tail = m->fused_tail && m->d == 512 && m->F % 128 == 0 && P < INT32_MAX;
+  int Wb = m->batch_windows > 0 ? m->batch_windows : std::max(1, (tail ? 65536 : 49152) / Lp);
   Wb = (int)std::min<int64_t>({(int64_t)Wb, K, max_rows / Lp});
   int rc = ensure_scratch(m, Wb, Lp, s);
   if (rc) return rc;
@@ -866,7 +882,7 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
     ea.embed = m->embed.p; ea.embed_f32 = m->embed_f32;
     ea.bigram = m->buckets > 0 ? m->bigram.as<float>() : nullptr; ea.buckets = m->buckets;
     ea.vocab = m->V; ea.d = d; ea.nt = nt;
-    ea.x = sc.x.as<float>(); ea.xb = sc.xb.as<bf16>(); ea.ss = sc.ss.as<float>();
+    ea.x = sc.x.as<float>(); ea.xb = sc.xb.as<act>(); ea.ss = sc.ss.as<float>();
     ea.flags = m->flags.as<int32_t>();
     if ((rc = timed(m, I6G_K_EMBED, s, 0.0, real_rows * d * 6.0, [&] { return launch_embed(ea, s); })))
       return rc;
@@ -885,9 +901,9 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
           return rc;
       }
       GemmArgs g{};
-      g.A = sc.xb.as<bf16>(); g.B = B.qkv_codes.as<int8_t>(); g.scale = B.qkv_scales.as<uint16_t>();
+      g.A = sc.xb.as<act>(); g.B = B.qkv_codes.as<int8_t>(); g.scale = B.qkv_scales.as<uint16_t>();
       g.M = M; g.N = m->nqkv; g.K = d; g.ss_in = sc.ss.as<float>(); g.nt_in = nt; g.eps = eps;
-      g.q = sc.q.as<bf16>(); g.k = sc.k.as<bf16>(); g.vt = sc.vt.as<bf16>();
+      g.q = sc.q.as<act>(); g.k = sc.k.as<act>(); g.vt = sc.vt.as<act>();
       g.n_heads = m->Hq; g.n_kv = m->Hkv; g.hd = m->hd; g.Lp = Lp; g.rope = m->rope.as<float2>();
       g.rope_dims = m->rope_dims;
       if (m->lora_r > 0) {
@@ -902,7 +918,7 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
 
       const bool pr = last && prune;
       AttnArgs at{};
-      at.q = sc.q.as<bf16>(); at.k = sc.k.as<bf16>(); at.vt = sc.vt.as<bf16>(); at.o = sc.o.as<bf16>();
+      at.q = sc.q.as<act>(); at.k = sc.k.as<act>(); at.vt = sc.vt.as<act>(); at.o = sc.o.as<act>();
       at.W = W; at.n_heads = m->Hq; at.n_kv = m->Hkv; at.hd = m->hd; at.Lp = Lp; at.scale_log2 = scale_log2;
       at.prune = pr; at.k0 = k0; at.P = P; at.L = (int32_t)L; at.S = (int32_t)S;
       at.xsa = e >= m->n_eff - m->xsa_last_n;
@@ -913,21 +929,24 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
 
       // attention output projection, residual add
       GemmArgs go{};
-      go.A = sc.o.as<bf16>(); go.B = B.o_codes.as<int8_t>(); go.scale = B.o_scales.as<uint16_t>();
+      go.flags = m->flags.as<int32_t>();
+      go.A = sc.o.as<act>(); go.B = B.o_codes.as<int8_t>(); go.scale = B.o_scales.as<uint16_t>();
       go.M = M; go.N = d; go.K = d; go.x = sc.x.as<float>();
-      if (!m->parallel) { go.xb = sc.xb.as<bf16>(); go.ss_out = sc.ss.as<float>(); }
+      if (!m->parallel) { go.xb = sc.xb.as<act>(); go.ss_out = sc.ss.as<float>(); }
 
       GemmArgs gf{};
-      gf.A = sc.xb.as<bf16>(); gf.B = B.fc_codes.as<int8_t>(); gf.scale = B.fc_scales.as<uint16_t>();
+      gf.flags = m->flags.as<int32_t>();
+      gf.A = sc.xb.as<act>(); gf.B = B.fc_codes.as<int8_t>(); gf.scale = B.fc_scales.as<uint16_t>();
       if (m->register_codes) gf.Bp = B.fc_frag.as<int8_t>();
       gf.M = M; gf.N = F; gf.K = d; gf.ss_in = sc.ss.as<float>(); gf.nt_in = nt; gf.eps = eps;
-      gf.h = sc.h.as<bf16>(); gf.leaky = m->leaky;
+      gf.h = sc.h.as<act>(); gf.leaky = m->leaky;
 
       GemmArgs gp{};
-      gp.A = sc.h.as<bf16>(); gp.B = B.proj_codes.as<int8_t>(); gp.scale = B.proj_scales.as<uint16_t>();
+      gp.flags = m->flags.as<int32_t>();
+      gp.A = sc.h.as<act>(); gp.B = B.proj_codes.as<int8_t>(); gp.scale = B.proj_scales.as<uint16_t>();
       if (m->register_codes) gp.Bp = B.proj_frag.as<int8_t>();
       gp.M = M; gp.N = d; gp.K = F; gp.x = sc.x.as<float>();
-      if (!last) { gp.xb = sc.xb.as<bf16>(); gp.ss_out = sc.ss.as<float>(); }
+      if (!last) { gp.xb = sc.xb.as<act>(); gp.ss_out = sc.ss.as<float>(); }
       if (m->push_after[e]) gp.push_dst = sc.slots.as<float>() + (size_t)m->push_slot[e] * M * d;
       if (!last && m->pop_before[e + 1] >= 0) {
         gp.pop_src = sc.slots.as<float>() + (size_t)m->pop_slot[e + 1] * M * d;
@@ -949,6 +968,38 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
 
       const double rows_mlp = pr ? (double)R : real_rows;
       const double fl_o = 2.0 * rows_mlp * d * d, fl_fc = 2.0 * rows_mlp * F * d;
+      if (tail) {
+        // output projection, norm and MLP in one kernel: algorithmic bytes
+        // per row are the attention output, the residual read and written,
+        // its binary16 copy, skip slots, plus the codes once per launch
+        TailArgs ta{};
+        ta.flags = m->flags.as<int32_t>();
+        ta.o = sc.o.as<act>();
+        ta.o_frag = B.o_frag.as<int8_t>(); ta.o_scale = B.o_scales.as<uint16_t>();
+        ta.fc_frag = B.fc_frag.as<int8_t>(); ta.fc_scale = B.fc_scales.as<uint16_t>();
+        ta.proj_frag = B.proj_frag.as<int8_t>(); ta.proj_scale = B.proj_scales.as<uint16_t>();
+        ta.M = pr ? R : M; ta.F = F; ta.eps = eps; ta.leaky = m->leaky;
+        ta.x = sc.x.as<float>();
+        if (!last) { ta.xb = sc.xb.as<act>(); ta.ss_out = sc.ss.as<float>(); }
+        if (m->push_after[e]) ta.push_dst = sc.slots.as<float>() + (size_t)m->push_slot[e] * M * d;
+        if (!last && m->pop_before[e + 1] >= 0) {
+          ta.pop_src = sc.slots.as<float>() + (size_t)m->pop_slot[e + 1] * M * d;
+          ta.pop_w = m->skip_w.as<float>() + (size_t)m->pop_before[e + 1] * d;
+        }
+        ta.parallel = m->parallel;
+        ta.xb_in = sc.xb.as<act>(); ta.ss_in = sc.ss.as<float>(); ta.nt_in = nt;
+        if (pr) {
+          ta.row_map = 1;
+          ta.p0 = p0; ta.k0 = k0; ta.n_win = K; ta.e0 = e0;
+          ta.L = (int32_t)L; ta.S = (int32_t)S; ta.Lp = Lp;
+        }
+        double per_row = 2.0 * d + 8.0 * d + (ta.xb ? 2.0 * d : 0.0) + (ta.push_dst ? 4.0 * d : 0.0) +
+                         (ta.pop_src && ta.pop_src != ta.push_dst ? 4.0 * d : 0.0) + (m->parallel ? 2.0 * d : 0.0);
+        const double by_t = rows_mlp * per_row + (double)d * d + 2.0 * (double)F * d;
+        if ((rc = timed(m, I6G_K_TAIL, s, fl_o + 2.0 * fl_fc, by_t, [&] { return launch_tail(ta, s); })))
+          return rc;
+        continue;
+      }
       // algorithmic HBM bytes: A read, fp32 residual read + write, bf16 copy,
       // skip slot written / read, codes (scales and sums of squares are small)
       auto res_bytes = [&](const GemmArgs& g, double a_cols) {

@@ -10,7 +10,7 @@
 // the 4 waves owns 32 queries of one head.
 //
 // * The scores are formed transposed, S^T = K Q^T, with
-//   v_mfma_f32_16x16x32_bf16: a lane's accumulator holds one query and 4
+//   v_mfma_f32_16x16x32_f16: a lane's accumulator holds one query and 4
 //   keys, so a query's running max lives in one lane group and needs two
 //   cross-lane steps (gfx950 v_permlane16/32_swap, no LDS round trip).
 // * The keys feeding the S^T rows are permuted so that the probabilities a
@@ -21,7 +21,7 @@
 //   conflicts on gfx950.
 // * The softmax denominator comes out of the same MFMAs: a constant block of
 //   ones appended to V^T makes one extra O^T block equal to sum_k P[q, k]
-//   (of the bf16 P actually used), with no VALU adds.
+//   (of the binary16 P actually used), with no VALU adds.
 // * exp is the hardware exp2 with the 1/sqrt(hd) * log2(e) factor folded
 //   into one multiply-add.  Probabilities are taken relative to a reference
 //   max that only moves when a tile max exceeds it by more than 2^8, so the
@@ -35,9 +35,12 @@
 //   barrier phases (measured faster on gfx950 than keeping the next tile's
 //   scores in flight at two workgroups per CU).
 #include "common.h"
+#include "mfma_util.h"
 
 namespace i6g {
 namespace {
+
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 // 16-byte chunk j of a 128-byte LDS row r lives in slot j ^ ((r >> 1) & 7).
 __device__ inline int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
@@ -81,8 +84,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD <= 64 ? 
   constexpr int KPER = (KCH + 255) / 256;
   constexpr int VPER = (VCH + 255) / 256;
 
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][64 * KLD];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][HD * VLD];
+  __shared__ __attribute__((aligned(16))) act Ks[2][64 * KLD];
+  __shared__ __attribute__((aligned(16))) act Vs[2][HD * VLD];
 
   const int tid = threadIdx.x & 255, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -123,24 +126,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD <= 64 ? 
     for (int i = tid; i < 2 * 64 * (HDP - HD); i += 256) {
       int b = i / (64 * (HDP - HD)), rem = i % (64 * (HDP - HD));
       int r = rem / (HDP - HD), c = HD + rem % (HDP - HD);
-      Ks[b][r * KLD + c] = (bf16)0.0f;
+      Ks[b][r * KLD + c] = (act)0.0f;
     }
   }
 
-  const bf16* Qh = a.q + ((int64_t)w * a.n_heads + head) * a.Lp * HD;
-  const bf16* Kg = a.k + ((int64_t)w * a.n_kv + g) * a.Lp * HD;
-  const bf16* Vg = a.vt + ((int64_t)w * a.n_kv + g) * HD * a.Lp;
+  const act* Qh = a.q + ((int64_t)w * a.n_heads + head) * a.Lp * HD;
+  const act* Kg = a.k + ((int64_t)w * a.n_kv + g) * a.Lp * HD;
+  const act* Vg = a.vt + ((int64_t)w * a.n_kv + g) * HD * a.Lp;
 
-  bf16x8 qf[2][KS];
+  actx8 qf[2][KS];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       int d0 = ks * 32 + 8 * lg;
       if (d0 < HD)
-        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)(qbase + 16 * qb + lr) * HD + d0);
+        qf[qb][ks] = *reinterpret_cast<const actx8*>(Qh + (int64_t)(qbase + 16 * qb + lr) * HD + d0);
       else
-        qf[qb][ks] = bf16x8{};
+        qf[qb][ks] = actx8{};
     }
 
   // Register staging, up to three 16-byte chunks per thread and tile, as
@@ -178,15 +181,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD <= 64 ? 
   {                                                                                   \
     _Pragma("unroll") for (int kb = 0; kb < 4; ++kb) {                                \
       const int kr = 16 * kb + lr;                                                    \
-      bf16x8 kf[KS];                                                                  \
+      actx8 kf[KS];                                                                  \
       _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                             \
         const int ch = ks * 4 + lg;                                                   \
-        kf[ks] = *reinterpret_cast<const bf16x8*>(&Ks[buf][kr * KLD + (KSWZ ? swz(kr, ch) : ch) * 8]); \
+        kf[ks] = *reinterpret_cast<const actx8*>(&Ks[buf][kr * KLD + (KSWZ ? swz(kr, ch) : ch) * 8]); \
       }                                                                               \
       _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                              \
         f32x4 acc_ = f32x4{0.f, 0.f, 0.f, 0.f};                                       \
         _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                             \
-          acc_ = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[qb][ks], acc_, 0, 0, 0); \
+          acc_ = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ks], qf[qb][ks], acc_, 0, 0, 0); \
         dst[qb][kb] = acc_;                                                           \
       }                                                                               \
     }                                                                                 \
@@ -200,9 +203,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD <= 64 ? 
     for (int db = 0; db < DB; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     osum[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  bf16x8 ones;
+  actx8 ones;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = (bf16)1.0f;
+  for (int i = 0; i < 8; ++i) ones[i] = (act)1.0f;
   float mref[2] = {-1e30f, -1e30f};
   const float c = a.scale_log2;
 
@@ -259,28 +262,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD <= 64 ? 
         osum[qb] *= alpha;                                                            \
       }                                                                               \
     }                                                                                 \
-    bf16x8 pf[2][2];                                                                  \
+    actx8 pf[2][2];                                                                  \
     _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                                \
       const float mc = mref[qb] * c;                                                  \
       _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                              \
-        bf16x8 v;                                                                     \
+        f32x8 v;                                                                      \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                               \
-          v[i] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(SC[qb][2 * kk][i], c, -mc)); \
-          v[4 + i] = (bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(SC[qb][2 * kk + 1][i], c, -mc)); \
+          v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(SC[qb][2 * kk][i], c, -mc));   \
+          v[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(SC[qb][2 * kk + 1][i], c, -mc)); \
         }                                                                             \
-        pf[qb][kk] = v;                                                               \
+        pf[qb][kk] = __builtin_convertvector(v, actx8); /* v_cvt_pk_f16_f32, nearest even */ \
       }                                                                               \
     }                                                                                 \
     const int vb_ = (kt) & 1;                                                         \
     _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                \
       _Pragma("unroll") for (int db = 0; db < DB; ++db) {                             \
         const int vr_ = db * 16 + lr;                                                 \
-        bf16x8 vf = *reinterpret_cast<const bf16x8*>(&Vs[vb_][vr_ * VLD + swz(vr_, 4 * kk + lg) * 8]); \
+        actx8 vf = *reinterpret_cast<const actx8*>(&Vs[vb_][vr_ * VLD + swz(vr_, 4 * kk + lg) * 8]); \
         _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                              \
-          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb][kk], o[qb][db], 0, 0, 0); \
+          o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qb][kk], o[qb][db], 0, 0, 0); \
       }                                                                               \
       _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                                \
-        osum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb][kk], osum[qb], 0, 0, 0); \
+        osum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pf[qb][kk], osum[qb], 0, 0, 0); \
     }                                                                                 \
     if (!(DIAG)) {                                                                    \
       /* K[kt+1] and V[kt+1] replace tile kt-1's; the barrier publishes */            \
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD <= 64 ? 
   for (int qb = 0; qb < 2; ++qb) {
     const float inv = 1.0f / osum[qb][0];
     const int q = qbase + 16 * qb + lr;
-    bf16* dst = a.o + ((int64_t)w * a.Lp + q) * (a.n_heads * HD) + head * HD;
+    act* dst = a.o + ((int64_t)w * a.Lp + q) * (a.n_heads * HD) + head * HD;
     float ov[DB][4];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -325,7 +328,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD <= 64 ? 
       for (int i = 0; i < 4; ++i) ov[db][i] = o[qb][db][i] * inv;
     if (a.xsa) {
       // exclusive self attention ([363] XSA): remove the component along
-      // this position's value vector v (bf16, as the P.V product used it)
+      // this position's value vector v (binary16, as the P.V product used it)
       float vv[DB][4], dot = 0.0f, nn = 0.0f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -347,11 +350,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD <= 64 ? 
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      uint16_t y[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = __builtin_bit_cast(uint16_t, (bf16)ov[db][i]);
       *reinterpret_cast<uint2*>(dst + db * 16 + 4 * lg) =
-          make_uint2((uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16));
+          make_uint2(pack2h(ov[db][0], ov[db][1]), pack2h(ov[db][2], ov[db][3]));
     }
   }
 }

@@ -19,7 +19,7 @@ __device__ inline float wave_sum(float v) {
 // table is pre-multiplied by the projection at load time).  Row m of the
 // batch is position j = m % Lp of window k0 + m / Lp; positions past the end
 // of the window's inputs read token 0 and are never scored.  One wave per row;
-// it also writes bf16(x) and the row's sum of squares for the first normed
+// it also writes binary16(x) and the row's sum of squares for the first normed
 // GEMM.
 __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
   const int lane = threadIdx.x & 63;
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
                           : (float)reinterpret_cast<const _Float16*>(a.embed)[(int64_t)tok * a.d + c];
     if (brow) v += brow[c];
     a.x[m * a.d + c] = v;
-    a.xb[m * a.d + c] = (bf16)v;
+    a.xb[m * a.d + c] = (act)v;
     sq += v * v;
   }
   sq = wave_sum(sq);

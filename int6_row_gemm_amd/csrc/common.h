@@ -9,6 +9,15 @@ namespace i6g {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// Activations on the scoring path -- the GEMM inputs (the residual stream's
+// copy, the attention output, the MLP hidden values), q, k, v and the
+// attention probabilities -- are binary16: with 11 significant bits their
+// rounding error is 8x below bfloat16's, at the same MFMA rate on gfx950
+// (measured against the float64 oracle: mean per-token error about 10x
+// lower).  Residual rows beyond the binary16 range are reported (see
+// I6G_FLAG_RANGE).
+typedef _Float16 act;
+typedef _Float16 actx8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
@@ -19,6 +28,13 @@ constexpr int kWave = 64;
 // Device flag bit set by the packer for a byte that is not a code of the
 // format being packed; equals I6G_FLAG_CODE of the C ABI.
 constexpr int32_t kFlagCode = 8;
+// Device flag bit set when a value held in binary16 on the scoring path would
+// leave its range (a residual row whose sum of squares reaches 65504^2, which
+// includes every row holding an element beyond 65504, or an MLP hidden value
+// of 65504 or more); equals I6G_FLAG_RANGE of the C ABI.
+constexpr int32_t kFlagRange = 16;
+constexpr float kRangeSq = 65504.0f * 65504.0f;
+constexpr float kRangeSqrt = 255.9375f;   // sqrt(65504) rounded down: v^2 < 65504 for |v| < this
 
 // ---------------------------------------------------------------------------
 // Row quantiser
@@ -74,13 +90,13 @@ static_assert(sizeof(QuantManyArgs) <= 4096, "kernel arguments are limited to 4 
 hipError_t launch_quantize_many(const QuantManyArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------------------
-// Dequant-fused GEMM: C[m, n] = sum_k A[m, k] * code[n, k], A bf16 [M, K],
+// Dequant-fused GEMM: C[m, n] = sum_k A[m, k] * code[n, k], A binary16 [M, K],
 // codes int8 [N, K]; the per-row scale of B (and, for normed inputs, the
 // per-row RMS factor of A) is applied in the epilogue.
 enum EpiKind { EPI_QKV = 0, EPI_RELU2 = 1, EPI_RES = 2 };
 
 struct GemmArgs {
-  const bf16* A;          // [M, K]
+  const act* A;           // [M, K]
   const int8_t* B;        // [N, K]
   // the same codes rearranged by launch_shuffle_codes, or null; when set, the
   // row-major epilogues (EPI_RELU2, EPI_RES) feed them from global memory
@@ -93,7 +109,7 @@ struct GemmArgs {
   int32_t nt_in;
   float eps;
   // EPI_QKV
-  bf16* q; bf16* k; bf16* vt;
+  act* q; act* k; act* vt;
   int32_t n_heads, n_kv, hd, Lp;
   const float2* rope;     // [Lp, hd/2] (cos, sin) of rotation pair p
   int32_t rope_dims;      // rotated dims per head (pairs (i, i + rope_dims/2))
@@ -102,11 +118,11 @@ struct GemmArgs {
   const float* lora_bv;   // [Hkv*hd, r]
   int32_t lora_r;
   // EPI_RELU2: h = leaky_relu(acc, leaky)^2 (leaky 0 = ReLU^2)
-  bf16* h;                // [M, N]
+  act* h;                 // [M, N]
   float leaky;
   // EPI_RES
   float* x;               // [M, N] residual, updated in place
-  bf16* xb;               // [M, N] bf16 copy of the new x (or null)
+  act* xb;                // [M, N] binary16 copy of the new x (or null)
   float* ss_out;          // [M, N/128] partial sums of squares (or null)
   float* push_dst;        // [M, N] skip slot to store the new x into (or null)
   const float* pop_src;   // [M, N] skip slot to add (or null); may equal push_dst
@@ -117,11 +133,52 @@ struct GemmArgs {
   int32_t a_map, e_map;
   int64_t p0, k0, n_win, e0;
   int32_t L, S;
+  int32_t* flags;         // kFlagRange (EPI_RELU2, EPI_RES)
 };
 // Rearranges int8 codes [N, K] (N % 128 == 0, K % 64 == 0) into the
-// fragment order of the register-fed GEMM path; Bp holds N * K bytes.
-hipError_t launch_shuffle_codes(const int8_t* B, int32_t N, int32_t K, int8_t* Bp, hipStream_t s);
+// fragment order of the register-fed GEMM path; Bp holds N * K bytes.  When
+// zero_scale_rows (binary16 [N]) is given, rows whose scale is +-0 are
+// written as zero codes.
+hipError_t launch_shuffle_codes(const int8_t* B, int32_t N, int32_t K, const uint16_t* zero_scale_rows, int8_t* Bp,
+                                hipStream_t s);
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
+
+// Fused block tail for d_model = 512: x += o . Wo^T; then (sequential
+// block) a = N(x), or (parallel lanes) a = N(layer input);
+// x += act(a . Wfc^T)^2 . Wproj^T; then the skip push / pop of the block
+// schedule, and a binary16 copy of x plus per-128-column sums of squares for the next
+// normed GEMM.  One 128-row tile per workgroup; the hidden activations stay
+// on chip.  Codes come in the fragment order of launch_shuffle_codes (o and
+// proj rows with a zero scale as zero codes).
+struct TailArgs {
+  const act* o;             // [rows, 512] attention output
+  const int8_t* o_frag;     // Wo [512, 512]
+  const uint16_t* o_scale;  // [512] binary16
+  const int8_t* fc_frag;    // Wfc [F, 512]
+  const uint16_t* fc_scale; // [F]
+  const int8_t* proj_frag;  // Wproj [512, F]
+  const uint16_t* proj_scale;
+  int32_t M, F;
+  float eps, leaky;
+  float* x;                 // [rows, 512] residual, updated in place
+  act* xb;                  // [rows, 512] binary16 copy of the result (or null)
+  float* ss_out;            // [rows, 4] per-128-column sums of squares of the result (or null)
+  float* push_dst;          // skip slot to store the result into (or null)
+  const float* pop_src;     // skip slot added with weight pop_w (or null); may equal push_dst
+  const float* pop_w;       // [512] fp32
+  // parallel lanes: the MLP input is the layer input, read from xb_in and
+  // ss_in (nt_in partial sums per row) before xb and ss_out are written
+  int32_t parallel;
+  const act* xb_in;
+  const float* ss_in;
+  int32_t nt_in;
+  // scored-rows mode (final layer): tile row r is prediction p0 + r
+  int32_t row_map;
+  int64_t p0, k0, n_win, e0;
+  int32_t L, S, Lp;
+  int32_t* flags;           // kFlagRange
+};
+hipError_t launch_tail(const TailArgs& a, hipStream_t s);
 
 // Row of prediction p in a batch of windows k0.. laid out Lp rows apart:
 // window k scores p in [max(kS, e_{k-1}), e_k); window 0 ends at e0.
@@ -135,10 +192,10 @@ __host__ __device__ inline int64_t scored_row(int64_t p, int64_t k0, int64_t n_w
 // ---------------------------------------------------------------------------
 // Causal GQA attention over a batch of windows.
 struct AttnArgs {
-  const bf16* q;   // [W, Hq, Lp, hd]
-  const bf16* k;   // [W, Hkv, Lp, hd]
-  const bf16* vt;  // [W, Hkv, hd, Lp]
-  bf16* o;         // [W*Lp, Hq*hd]
+  const act* q;    // [W, Hq, Lp, hd]
+  const act* k;    // [W, Hkv, Lp, hd]
+  const act* vt;   // [W, Hkv, hd, Lp]
+  act* o;          // [W*Lp, Hq*hd]
   int32_t W, n_heads, n_kv, hd, Lp;
   float scale_log2;  // log2(e) / sqrt(hd)
   // exclusive self attention: remove from each output row its component
@@ -152,7 +209,7 @@ struct AttnArgs {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------------------
-// Embedding gather (+ bigram), writes x, bf16 x and row sums of squares.
+// Embedding gather (+ bigram), writes x, its binary16 copy and row sums of squares.
 struct EmbedArgs {
   const int32_t* tokens;
   int64_t n_tokens;
@@ -163,7 +220,7 @@ struct EmbedArgs {
   const float* bigram; // [buckets, d] fp32 (table * proj^T) or null
   int32_t buckets;
   int32_t vocab, d, nt;  // nt partial-sum slots per row
-  float* x; bf16* xb; float* ss;
+  float* x; act* xb; float* ss;
   int32_t* flags;
 };
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);

@@ -1,18 +1,18 @@
 // Dequant-fused GEMM on gfx950 MFMA.
 //
-// C[m, n] = sum_k A[m, k] * code[n, k] with A bf16 [M, K] (activations) and
+// C[m, n] = sum_k A[m, k] * code[n, k] with A binary16 [M, K] (activations) and
 // code int8 [N, K] (one quantised weight row per output feature, the layout
 // of a [out, in] matrix).  The weight of a linear layer is W[n, k] =
 // code[n, k] * scale[n] (pwwt.cn "parameter-golf 16MB 极限压缩实战 …",
 // 后训练量化导出: one binary16 scale per row), so the scale is a per-column
 // factor of C and is applied in the epilogue; the codes (integers in
-// [-128, 127]) are exact in bf16 and are widened on their way into LDS.
+// [-128, 127]) are exact in binary16 and are widened on their way into LDS.
 // When A holds un-normalised activations, the RMSNorm factor of each row
 // (a per-row factor of C) is applied in the epilogue as well.
 //
 // Tiling: 256 threads = 4 waves in a 2 x 2 grid; workgroup tile BM x BN,
 // K step 64 through one XOR-swizzled LDS tile with register prefetch one K
-// step ahead; each wave issues v_mfma_f32_16x16x32_bf16 on (BM/2) x (BN/2).
+// step ahead; each wave issues v_mfma_f32_16x16x32_f16 on (BM/2) x (BN/2).
 // Register-fed variant (the MLP GEMMs, when the caller passes the codes
 // rearranged by launch_shuffle_codes): only the A tile goes through LDS;
 // the waves split the tile 1 x 4 (128 x 32 each) and load their own code
@@ -30,89 +30,25 @@
 // accesses and no LDS round trip:
 //   EPI_QKV   q/k/v projection: * scale * rinv (+ rank-r LoRA), RoPE on the
 //             q and k heads, writes Q [W,Hq,Lp,hd], K [W,Hkv,Lp,hd] and
-//             V transposed [W,Hkv,hd,Lp] in bf16;
-//   EPI_RELU2 MLP up-projection: h = bf16(relu(acc * scale * rinv)^2);
+//             V transposed [W,Hkv,hd,Lp] in binary16;
+//   EPI_RELU2 MLP up-projection: h = binary16(relu(acc * scale * rinv)^2);
 //   EPI_RES   output / down projection: x += acc * scale, then the skip
-//             push/pop of the block schedule, and bf16(x) plus per-tile
+//             push/pop of the block schedule, and binary16(x) plus per-tile
 //             sums of x^2 for the next normed GEMM.
 #include "common.h"
+#include "mfma_util.h"
 
 namespace i6g {
 namespace {
 
 constexpr int BK = 64;
-constexpr int LDK = BK;      // LDS row stride in bf16 elements (128 bytes)
+constexpr int LDK = BK;      // LDS row stride in binary16 elements (128 bytes)
 
 // LDS tiles keep 128-byte rows of eight 16-byte chunks; chunk j of row r is
 // stored in slot j ^ ((r >> 1) & 7).  Measured on gfx950, this makes both the
 // MFMA fragment reads (16 rows, one chunk each) and the staging writes free of
 // bank conflicts, where a 16-byte row padding costs a two-way conflict.
 __device__ inline int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
-
-__device__ inline float h2f(uint16_t h) {
-  return (float)__builtin_bit_cast(_Float16, h);
-}
-
-__device__ inline uint32_t pack_bf16x2_from_int(int lo, int hi) {
-  // integers of magnitude <= 128 are exact in fp32 and keep only 8
-  // significant bits, so the upper half of the fp32 pattern is the bf16;
-  // one byte permute takes both upper halves (bytes 2, 3 of lo, then of hi)
-  const uint32_t a = __builtin_bit_cast(uint32_t, (float)lo);
-  const uint32_t b = __builtin_bit_cast(uint32_t, (float)hi);
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-
-// leaky_relu(v, slope); slope 0 gives relu (its square is ReLU^2)
-__device__ inline float lrelu(float v, float slope) { return v >= 0.0f ? v : slope * v; }
-
-__device__ inline uint16_t f2bf_bits(float f) {
-  return __builtin_bit_cast(uint16_t, (bf16)f);
-}
-
-// Map the launch index to a logical tile so that each XCD (the hardware
-// deals workgroups round-robin over 8 XCDs) gets a contiguous range of
-// tiles: neighbouring tiles share A rows, which then stay in one L2.
-__device__ inline int xcd_remap(int bid, int nblocks) {
-  const int q = nblocks / 8, r = nblocks % 8;
-  const int xcd = bid % 8, idx = bid / 8;
-  return xcd * q + min(xcd, r) + idx;
-}
-
-// Rows of the LDS tiles are placed so that each lane's share of the
-// accumulator is a run of consecutive rows or columns (see the epilogues).
-// Within a 64-row slice, row u is stored at perm16(u), which swaps the two
-// 2-bit fields u[5:4] and u[3:2] (so perm16 is its own inverse): the MFMA
-// fragment of block b, lane row r (physical row 16b + r) then holds logical
-// row 16 * (r >> 2) + 4b + (r & 3).
-__device__ inline int perm16(int u) {
-  return ((u & 12) << 2) | ((u >> 4) & 3) << 2 | (u & 3);
-}
-
-// Placement of the weight rows of a 64-column slice for the row-major
-// epilogues: output rows 4g + e of fragment j (lane group g) are columns
-// 32*(j>>1) + 8g + 4*(j&1) + e, so a lane holds two runs of 8 consecutive
-// columns and the four lanes of a row cover 32 consecutive columns of each
-// half (one 128-byte line of fp32, or 64 bytes of bf16, per instruction).
-__device__ inline int pair_phys(int u) {
-  return 16 * (2 * (u >> 5) + ((u >> 2) & 1)) + 4 * ((u >> 3) & 3) + (u & 3);
-}
-
-// Inverse of pair_phys on a 32-column slice (pair_phys keeps each half of a
-// 64-column slice in place): the logical column stored at physical row p.
-__device__ inline int pair_logical32(int p) {
-  return (p & 3) | (((p >> 4) & 1) << 2) | (((p >> 2) & 3) << 3);
-}
-
-// Eight int8 codes (one 8-byte half of a 16-byte fragment chunk) widened to
-// the bf16 MFMA operand; exact for integers of magnitude <= 128.
-__device__ inline bf16x8 widen8(uint32_t lo, uint32_t hi) {
-  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-  const u32x4_t o = {pack_bf16x2_from_int((int)(int8_t)(lo & 0xff), (int)(int8_t)((lo >> 8) & 0xff)),
-                     pack_bf16x2_from_int((int)(int8_t)((lo >> 16) & 0xff), (int)(int8_t)(lo >> 24)),
-                     pack_bf16x2_from_int((int)(int8_t)(hi & 0xff), (int)(int8_t)((hi >> 8) & 0xff)),
-                     pack_bf16x2_from_int((int)(int8_t)((hi >> 16) & 0xff), (int)(int8_t)(hi >> 24))};
-  return __builtin_bit_cast(bf16x8, o);
-}
 
 // Rotation pairs of one q or k head with R rotated dims (partial RoPE):
 // pair p < R/2 is (p, p + R/2); the others pair up the unrotated dims as
@@ -149,20 +85,18 @@ struct Smem {
   static constexpr int kBytes = (BM + (RB ? 0 : BN)) * LDK * 2;   // one A and (unless RB) one B tile
 };
 
+// N consecutive values stored as binary16 (N even)
 template <int N>
-__device__ inline void store_bf16_run(bf16* dst, const uint16_t (&y)[N]) {
+__device__ inline void store_h_run(act* dst, const float (&y)[N]) {
   if constexpr (N == 8) {
-    *reinterpret_cast<uint4*>(dst) = make_uint4(
-        (uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16),
-        (uint32_t)y[4] | ((uint32_t)y[5] << 16), (uint32_t)y[6] | ((uint32_t)y[7] << 16));
+    *reinterpret_cast<uint4*>(dst) =
+        make_uint4(pack2h(y[0], y[1]), pack2h(y[2], y[3]), pack2h(y[4], y[5]), pack2h(y[6], y[7]));
   } else if constexpr (N == 4) {
-    *reinterpret_cast<uint2*>(dst) =
-        make_uint2((uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16));
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack2h(y[0], y[1]), pack2h(y[2], y[3]));
   } else {
     static_assert(N % 2 == 0, "pairs");
 #pragma unroll
-    for (int e = 0; e < N; e += 2)
-      reinterpret_cast<uint32_t*>(dst)[e / 2] = (uint32_t)y[e] | ((uint32_t)y[e + 1] << 16);
+    for (int e = 0; e < N; e += 2) reinterpret_cast<uint32_t*>(dst)[e / 2] = pack2h(y[e], y[e + 1]);
   }
 }
 
@@ -173,13 +107,13 @@ __device__ inline void store_bf16_run(bf16* dst, const uint16_t (&y)[N]) {
 // is staged through LDS, and the four waves split the tile 1 x 4 (128 rows
 // x 32 columns each) so that every code is still loaded once per tile.
 template <int BM, int BN, int EPI, bool CT, bool RB>
-__device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs, float* rinv_s,
+__device__ __forceinline__ void gemm_body(const GemmArgs& a, act* As, act* Bs, float* rinv_s,
                                           float* scale_s, float* popw_s, float (*ss_part)[BM],
                                           int tid, int wave, int m0, int n0, int tn) {
   constexpr int WM = RB ? BM : BM / 2, WN = RB ? BN / 4 : BN / 2;
   constexpr int NWN = BN / WN;                // waves across the columns
   constexpr int FM = WM / 16, FN = WN / 16;
-  constexpr int A_CHUNKS = BM * BK / 8;       // 16-byte chunks of bf16
+  constexpr int A_CHUNKS = BM * BK / 8;       // 16-byte chunks of binary16
   constexpr int B_CHUNKS = RB ? 0 : BN * BK / 16;   // 16-byte chunks of int8 staged through LDS
   constexpr int A_PER = (A_CHUNKS + 255) / 256;
   constexpr int B_PER = (B_CHUNKS + 255) / 256;
@@ -249,10 +183,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
   if constexpr (B_PER > i) {                                                          \
     const uint32_t w_[4] = {R.x, R.y, R.z, R.w};                                      \
     uint32_t o_[8];                                                                   \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                   \
-      o_[2 * j] = pack_bf16x2_from_int((int)(int8_t)(w_[j] & 0xff), (int)(int8_t)((w_[j] >> 8) & 0xff)); \
-      o_[2 * j + 1] = pack_bf16x2_from_int((int)(int8_t)((w_[j] >> 16) & 0xff), (int)(int8_t)(w_[j] >> 24)); \
-    }                                                                                 \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) widen4h(w_[j], o_[2 * j], o_[2 * j + 1]); \
     *reinterpret_cast<uint4*>(Bs + bso##i##a) = make_uint4(o_[0], o_[1], o_[2], o_[3]); \
     *reinterpret_cast<uint4*>(Bs + bso##i##b) = make_uint4(o_[4], o_[5], o_[6], o_[7]); \
   }
@@ -285,15 +216,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
 
   const int lr = lane & 15, lg = lane >> 4;
   // MF_C: acc block (i, j) = C (A rows x weight rows); MF_T: its transpose.
-#define MF_C(x, w, c) __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, w, c, 0, 0, 0)
-#define MF_T(x, w, c) __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, x, c, 0, 0, 0)
+#define MF_C(x, w, c) __builtin_amdgcn_mfma_f32_16x16x32_f16(x, w, c, 0, 0, 0)
+#define MF_T(x, w, c) __builtin_amdgcn_mfma_f32_16x16x32_f16(w, x, c, 0, 0, 0)
 #define GM_COMPUTE(MF)                                                                \
   {                                                                                   \
     _Pragma("unroll") for (int ks = 0; ks < BK / 32; ++ks) {                          \
-      bf16x8 af[FM], bfg[FN];                                                         \
+      actx8 af[FM], bfg[FN];                                                         \
       _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                \
         const int r_ = wm * WM + i * 16 + lr;                                         \
-        af[i] = *reinterpret_cast<const bf16x8*>(As + r_ * LDK + swz(r_, ks * 4 + lg) * 8); \
+        af[i] = *reinterpret_cast<const actx8*>(As + r_ * LDK + swz(r_, ks * 4 + lg) * 8); \
       }                                                                               \
       if constexpr (RB) {                                                             \
         bfg[0] = ks == 0 ? wb0[0] : wb1[0];                                           \
@@ -301,7 +232,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
       } else {                                                                        \
         _Pragma("unroll") for (int j = 0; j < FN; ++j) {                              \
           const int r_ = wn * WN + j * 16 + lr;                                       \
-          bfg[j] = *reinterpret_cast<const bf16x8*>(Bs + r_ * LDK + swz(r_, ks * 4 + lg) * 8); \
+          bfg[j] = *reinterpret_cast<const actx8*>(Bs + r_ * LDK + swz(r_, ks * 4 + lg) * 8); \
         }                                                                             \
       }                                                                               \
       _Pragma("unroll") for (int i = 0; i < FM; ++i)                                  \
@@ -322,7 +253,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
 #define GM_STEP(kt)                                                                   \
   {                                                                                   \
     GM_LOAD(min((kt) + 1, nk - 1), 0);                                                \
-    bf16x8 wb0[2], wb1[2];   /* RB: widened codes of this K tile, by 32-wide half */  \
+    actx8 wb0[2], wb1[2];   /* RB: widened codes of this K tile, by 32-wide half */  \
     if constexpr (RB) {                                                               \
       wb0[0] = widen8(bq0.x, bq0.y); wb1[0] = widen8(bq0.z, bq0.w);                   \
       wb0[1] = widen8(bq1.x, bq1.y); wb1[1] = widen8(bq1.z, bq1.w);                   \
@@ -387,6 +318,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
   // the lane's A row in C^T block i: 64-row slices of four blocks each
   auto arow = [&](int i) { return 64 * (i >> 2) + lrow + 4 * (i & 3); };
   if constexpr (EPI == EPI_RELU2) {
+    float vmax = 0.0f;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int ml = wm * WM + arow(i);
@@ -403,12 +335,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
           const f32x4 c = acc[i][2 * p + h];
           const float v0 = lrelu(c[0] * s4.x * ri, a.leaky), v1 = lrelu(c[1] * s4.y * ri, a.leaky);
           const float v2 = lrelu(c[2] * s4.z * ri, a.leaky), v3 = lrelu(c[3] * s4.w * ri, a.leaky);
-          o[2 * h] = (uint32_t)f2bf_bits(v0 * v0) | ((uint32_t)f2bf_bits(v1 * v1) << 16);
-          o[2 * h + 1] = (uint32_t)f2bf_bits(v2 * v2) | ((uint32_t)f2bf_bits(v3 * v3) << 16);
+          vmax = fmaxf(vmax, fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3))));
+          o[2 * h] = pack2h(v0 * v0, v1 * v1);
+          o[2 * h + 1] = pack2h(v2 * v2, v3 * v3);
         }
         *reinterpret_cast<uint4*>(a.h + (int64_t)m * a.N + n0 + cl) = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
+    if (__any(!(vmax < kRangeSqrt)) && (tid & 63) == 0) atomicOr(a.flags, kFlagRange);
   } else if constexpr (EPI == EPI_RES) {
     static_assert(BN == 128, "partial sums of squares cover 128 columns");
     const bool push = a.push_dst != nullptr;
@@ -420,6 +354,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
     // each group's loads in flight together; row offsets per group
     constexpr int FH = 8 / FN;
     float sq[FM];
+    bool range_bad = false;   // a partial row sum of squares reaches 65504^2
 #pragma unroll
     for (int hh = 0; hh < FM / FH; ++hh) {
       int64_t off[FM];
@@ -494,6 +429,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
           t += xv[ii][j].x * xv[ii][j].x + xv[ii][j].y * xv[ii][j].y + xv[ii][j].z * xv[ii][j].z +
                xv[ii][j].w * xv[ii][j].w;
         sq[i] = t;
+        range_bad |= a.xb && ok[i] && t >= kRangeSq;
         if (ok[i]) {
 #pragma unroll
           for (int j = 0; j < FN; ++j) *reinterpret_cast<float4*>(a.x + off[i] + colj(j)) = xv[ii][j];
@@ -503,15 +439,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
               const f32x4 u0 = {xv[ii][2 * p].x, xv[ii][2 * p].y, xv[ii][2 * p].z, xv[ii][2 * p].w};
               const f32x4 u1 = {xv[ii][2 * p + 1].x, xv[ii][2 * p + 1].y, xv[ii][2 * p + 1].z, xv[ii][2 * p + 1].w};
               *reinterpret_cast<uint4*>(a.xb + off[i] + colj(2 * p)) = make_uint4(
-                  (uint32_t)f2bf_bits(u0[0]) | ((uint32_t)f2bf_bits(u0[1]) << 16),
-                  (uint32_t)f2bf_bits(u0[2]) | ((uint32_t)f2bf_bits(u0[3]) << 16),
-                  (uint32_t)f2bf_bits(u1[0]) | ((uint32_t)f2bf_bits(u1[1]) << 16),
-                  (uint32_t)f2bf_bits(u1[2]) | ((uint32_t)f2bf_bits(u1[3]) << 16));
+                  pack2h(u0[0], u0[1]), pack2h(u0[2], u0[3]), pack2h(u1[0], u1[1]), pack2h(u1[2], u1[3]));
             }
           }
         }
       }
     }
+    if (__any(range_bad) && (tid & 63) == 0) atomicOr(a.flags, kFlagRange);
     if (a.ss_out) {
       // the four lane groups of a row, then the two waves of a tile row
 #pragma unroll
@@ -540,7 +474,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
       const bool is_q = colbase < dq;
       const int head = (is_q ? colbase : colbase - dq) / HD;
       const int nh = is_q ? a.n_heads : a.n_kv;
-      bf16* const base = is_q ? a.q : a.k;
+      act* const base = is_q ? a.q : a.k;
       const bool lora = is_q && a.lora_u;
       const int c1b = lg * Q8;
       const int f0 = pair_first<HD>(c1b, a.rope_dims), s0 = pair_second<HD>(c1b, a.rope_dims);
@@ -587,18 +521,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
             x2[t] += s2;
           }
         }
-        uint16_t y1[Q8], y2[Q8];
+        float y1[Q8], y2[Q8];
 #pragma unroll
         for (int t = 0; t < Q8; t += 2) {
           const float4 cs = csp[t / 2];   // (cos, sin) of indices c1b + t and c1b + t + 1
-          y1[t] = f2bf_bits(x1[t] * cs.x - x2[t] * cs.y);
-          y2[t] = f2bf_bits(x1[t] * cs.y + x2[t] * cs.x);
-          y1[t + 1] = f2bf_bits(x1[t + 1] * cs.z - x2[t + 1] * cs.w);
-          y2[t + 1] = f2bf_bits(x1[t + 1] * cs.w + x2[t + 1] * cs.z);
+          y1[t] = x1[t] * cs.x - x2[t] * cs.y;
+          y2[t] = x1[t] * cs.y + x2[t] * cs.x;
+          y1[t + 1] = x1[t + 1] * cs.z - x2[t + 1] * cs.w;
+          y2[t + 1] = x1[t + 1] * cs.w + x2[t + 1] * cs.z;
         }
-        bf16* dst = base + (((int64_t)w * nh + head) * a.Lp + pos) * HD;
-        store_bf16_run<Q8>(dst + f0, y1);
-        store_bf16_run<Q8>(dst + s0, y2);
+        act* dst = base + (((int64_t)w * nh + head) * a.Lp + pos) * HD;
+        store_h_run<Q8>(dst + f0, y1);
+        store_h_run<Q8>(dst + s0, y2);
       }
     } else {
       // v head, C orientation, written transposed: the lane's 16 rows are
@@ -627,7 +561,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
             for (int r = 0; r < 8; ++r)
               if (r < a.lora_r) bvr[r] = bv[r];
           }
-          uint16_t y[16];
+          float y[16];
 #pragma unroll
           for (int t = 0; t < 16; ++t) {
             float v = acc[t >> 2][j][t & 3] * sc * ri[t];
@@ -639,13 +573,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, bf16* As, bf16* Bs,
                 if (r < a.lora_r) sl += uu[r] * bvr[r];
               v += sl;
             }
-            y[t] = f2bf_bits(v);
+            y[t] = v;
           }
           uint4* dst = reinterpret_cast<uint4*>(a.vt + (((int64_t)w * a.n_kv + head) * HD + dd) * a.Lp + pos);
-          dst[0] = make_uint4((uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16),
-                              (uint32_t)y[4] | ((uint32_t)y[5] << 16), (uint32_t)y[6] | ((uint32_t)y[7] << 16));
-          dst[1] = make_uint4((uint32_t)y[8] | ((uint32_t)y[9] << 16), (uint32_t)y[10] | ((uint32_t)y[11] << 16),
-                              (uint32_t)y[12] | ((uint32_t)y[13] << 16), (uint32_t)y[14] | ((uint32_t)y[15] << 16));
+          dst[0] = make_uint4(pack2h(y[0], y[1]), pack2h(y[2], y[3]), pack2h(y[4], y[5]), pack2h(y[6], y[7]));
+          dst[1] = make_uint4(pack2h(y[8], y[9]), pack2h(y[10], y[11]), pack2h(y[12], y[13]), pack2h(y[14], y[15]));
         }
       }
     }
@@ -662,8 +594,8 @@ void gemm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) float scale_s[BN];
   __shared__ __attribute__((aligned(16))) float popw_s[BN];
   __shared__ float ss_part[RB ? 4 : 2][BM];
-  bf16* As = reinterpret_cast<bf16*>(smem);
-  bf16* Bs = RB ? nullptr : As + BM * LDK;
+  act* As = reinterpret_cast<act*>(smem);
+  act* Bs = RB ? nullptr : As + BM * LDK;
 
   const int tid = threadIdx.x & 255;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -692,7 +624,11 @@ hipError_t run(const GemmArgs& a, hipStream_t s) {
 // in K tile (c / 512) % nk of column tile c / (512 nk); it holds, for the
 // logical column 32 * wave + pair_logical32(16 * fragment + lane % 16), the
 // codes of k = 64 * tile + 8 * (lane / 16) + 0..7 and the same + 32.
+// With `scale` given, rows whose binary16 scale is zero get zero codes: their
+// weights are zero, and kernels that divide by the scale (treating a zero
+// scale as 1) then add exactly nothing for them.
 __global__ __launch_bounds__(256) void shuffle_codes_kernel(const int8_t* __restrict__ B, int32_t N, int32_t K,
+                                                            const uint16_t* __restrict__ scale,
                                                             int8_t* __restrict__ Bp) {
   const int nk = K / BK;
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -702,17 +638,20 @@ __global__ __launch_bounds__(256) void shuffle_codes_kernel(const int8_t* __rest
   const int kt = (int)(q % nk), tn = (int)(q / nk);
   const int row = tn * 128 + 32 * wv + pair_logical32(16 * j + (lane & 15));
   const int8_t* src = B + (int64_t)row * K + kt * BK + 8 * (lane >> 4);
-  const uint2 lo = *reinterpret_cast<const uint2*>(src);
-  const uint2 hi = *reinterpret_cast<const uint2*>(src + 32);
+  uint2 lo = *reinterpret_cast<const uint2*>(src);
+  uint2 hi = *reinterpret_cast<const uint2*>(src + 32);
+  if (scale && (scale[row] & 0x7fffu) == 0) lo = hi = make_uint2(0, 0);
   *reinterpret_cast<uint4*>(Bp + c * 16) = make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
 }  // namespace
 
-hipError_t launch_shuffle_codes(const int8_t* B, int32_t N, int32_t K, int8_t* Bp, hipStream_t s) {
+hipError_t launch_shuffle_codes(const int8_t* B, int32_t N, int32_t K, const uint16_t* zero_scale_rows, int8_t* Bp,
+                                hipStream_t s) {
   if (N <= 0 || K <= 0 || N % 128 != 0 || K % BK != 0) return hipErrorInvalidValue;
   const int64_t chunks = (int64_t)(N / 128) * (K / BK) * 512;
-  hipLaunchKernelGGL(shuffle_codes_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, B, N, K, Bp);
+  hipLaunchKernelGGL(shuffle_codes_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, B, N, K,
+                     zero_scale_rows, Bp);
   return hipGetLastError();
 }
 

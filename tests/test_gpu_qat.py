@@ -85,7 +85,12 @@ def test_nonfinite_rows_give_nan_and_flag():
         assert np.all(np.isnan(out[[1, 4]]))
         assert np.all(np.isfinite(out[[0, 2, 3, 5]]))
     good = np.delete(w, [1, 4], axis=0)
-    out = g.noisy_weights(_dev(w), 127, 9).cpu().numpy()
+    # without a flag tensor the binding reports the rows as I6G_ENONFINITE
+    with pytest.raises(g.I6GError) as ei:
+        g.noisy_weights(_dev(w), 127, 9)
+    assert ei.value.code == -4
+    flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = g.noisy_weights(_dev(w), 127, 9, torch.float32, flags).cpu().numpy()
     # finite rows are unaffected by the bad rows (counters are by element index)
     ref = oqat.noisy_weights(np.where(np.isfinite(w), w, 0), 127, 9)
     assert np.array_equal(out[[0, 2, 3, 5]].view(np.int32), ref[[0, 2, 3, 5]].view(np.int32))

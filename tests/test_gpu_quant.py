@@ -95,7 +95,8 @@ def test_many_matrices_in_one_call_bit_exact():
         torch.cuda.synchronize()
         assert int(flags.item()) & 1
         for w, codes, scales in jobs:
-            c1, s1 = g.quantize_rows(w, bits, q)
+            f1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+            c1, s1 = g.quantize_rows(w, bits, q, flags=f1)
             torch.cuda.synchronize()
             assert torch.equal(codes, c1) and torch.equal(scales, s1)
             wn = w.cpu().numpy()
