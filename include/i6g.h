@@ -431,9 +431,24 @@ int i6g_dequantize_packed(const uint8_t* packed_dev, int bits, const uint16_t* s
  * histogram; 1 adds to it, so several matrices can share one histogram.
  * Uses 128 KiB of stream-ordered temporary device memory (hipMallocAsync /
  * hipFreeAsync on `stream`).  Errors: I6G_EINVAL for n < 0 or NULL buffers;
- * I6G_ENOMEM if the temporary memory cannot be had. */
+ * I6G_ENOMEM if the temporary memory cannot be had; I6G_EUNSUPPORTED for n
+ * beyond the codes one call covers (2^31 - 1 workgroups of 8,192 codes). */
 int i6g_code_histogram(const int8_t* codes_dev, int64_t n, int accumulate, int64_t* hist_dev,
                        void* stream);
+
+/* i6g_code_histogram_noalloc -- i6g_code_histogram (same counts) for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  It allocates
+ * nothing: its 64 partial histograms (128 KiB) live in a static device array
+ * of the library, one per device, held until the process ends; the first
+ * call on a device resolves that array's address on it.  Every call on one
+ * device shares the array and clears it first (with a kernel), so calls that
+ * overlap on one device -- on different streams or host threads -- race and
+ * must be serialised by the caller.  Errors: as i6g_code_histogram
+ * (I6G_EUNSUPPORTED for n beyond the codes one call covers: 2^31 - 1
+ * workgroups of 8,192 codes). */
+int i6g_code_histogram_noalloc(const int8_t* codes_dev, int64_t n, int accumulate, int64_t* hist_dev,
+                               void* stream);
 
 /* i6g_code_entropy -- Shannon entropy in bits per value of a 256-bin
  * histogram of non-negative counts: -sum p log2 p over the bins with a

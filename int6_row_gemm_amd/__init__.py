@@ -26,7 +26,7 @@ EXPORTED = [
     "i6g_free_model", "i6g_last_error", "i6g_plan_windows", "i6g_set_option",
     "i6g_set_timing", "i6g_get_timing",
     "i6g_pack_codes", "i6g_unpack_codes", "i6g_dequantize_rows", "i6g_dequantize_packed",
-    "i6g_code_histogram", "i6g_code_entropy", "i6g_artifact_bytes",
+    "i6g_code_histogram", "i6g_code_histogram_noalloc", "i6g_code_entropy", "i6g_artifact_bytes",
     "i6g_fake_quantize_rows", "i6g_noisy_weights",
 ]
 DTYPE_F32, DTYPE_BF16 = 1, 2
@@ -102,6 +102,7 @@ def lib():
         L.i6g_dequantize_rows.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp, vp]
         L.i6g_dequantize_packed.argtypes = [vp, ctypes.c_int, vp, i64, i64, ctypes.c_int, vp, vp]
         L.i6g_code_histogram.argtypes = [vp, i64, ctypes.c_int, vp, vp]
+        L.i6g_code_histogram_noalloc.argtypes = [vp, i64, ctypes.c_int, vp, vp]
         L.i6g_code_entropy.argtypes = [vp, vp, vp]
         L.i6g_artifact_bytes.argtypes = [vp, vp, i32, i64, vp]
         L.i6g_fake_quantize_rows.argtypes = [vp, i64, i64, ctypes.c_int, dbl, ctypes.c_int, vp, vp, vp]

@@ -533,7 +533,23 @@ int i6g_dequantize_packed(const uint8_t* packed_dev, int bits, const uint16_t* s
 int i6g_code_histogram(const int8_t* codes_dev, int64_t n, int accumulate, int64_t* hist_dev, void* stream) {
   if (n < 0 || !hist_dev || (n > 0 && !codes_dev)) return fail(I6G_EINVAL, "code_histogram: n < 0 or NULL buffer");
   if (n > 0 && !aligned(codes_dev, 16)) return fail(I6G_EUNSUPPORTED, "code_histogram: codes must be 16-byte aligned");
+  if (n > code_histogram_max_codes())
+    return fail(I6G_EUNSUPPORTED, "code_histogram: n = %lld is beyond the %lld codes one call covers", (long long)n,
+                (long long)code_histogram_max_codes());
   HIP_TRY(launch_code_histogram(codes_dev, n, accumulate != 0, hist_dev, (hipStream_t)stream));
+  return I6G_OK;
+}
+
+int i6g_code_histogram_noalloc(const int8_t* codes_dev, int64_t n, int accumulate, int64_t* hist_dev,
+                               void* stream) {
+  if (n < 0 || !hist_dev || (n > 0 && !codes_dev))
+    return fail(I6G_EINVAL, "code_histogram_noalloc: n < 0 or NULL buffer");
+  if (n > 0 && !aligned(codes_dev, 16))
+    return fail(I6G_EUNSUPPORTED, "code_histogram_noalloc: codes must be 16-byte aligned");
+  if (n > code_histogram_max_codes())
+    return fail(I6G_EUNSUPPORTED, "code_histogram_noalloc: n = %lld is beyond the %lld codes one call covers",
+                (long long)n, (long long)code_histogram_max_codes());
+  HIP_TRY(launch_code_histogram_noalloc(codes_dev, n, accumulate != 0, hist_dev, (hipStream_t)stream));
   return I6G_OK;
 }
 

@@ -280,6 +280,14 @@ hipError_t launch_unpack_codes(const uint8_t* packed, int64_t n, int bits, int8_
 hipError_t launch_dequantize(const void* src, int bits, const uint16_t* scales, int64_t rows, int64_t cols,
                              bool bf16_out, void* out, hipStream_t s);
 hipError_t launch_code_histogram(const int8_t* codes, int64_t n, bool accumulate, int64_t* hist, hipStream_t s);
+// The same histogram with its partial histograms in the library's static
+// device scratch (no allocation); code_histogram_scratch resolves that
+// scratch on the current device (first call per device: hipGetSymbolAddress).
+hipError_t launch_code_histogram_noalloc(const int8_t* codes, int64_t n, bool accumulate, int64_t* hist,
+                                         hipStream_t s);
+hipError_t code_histogram_scratch(unsigned long long** out);
+// Largest n one histogram launch covers.
+int64_t code_histogram_max_codes();
 hipError_t launch_code_entropy(const int64_t* hist, double* out, hipStream_t s);
 
 }  // namespace i6g

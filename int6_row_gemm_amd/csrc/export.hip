@@ -25,6 +25,8 @@
 // whose group index is the group count.
 #include "common.h"
 
+#include <mutex>
+
 namespace i6g {
 namespace {
 
@@ -458,19 +460,72 @@ hipError_t launch_dequantize(const void* src, int bits, const uint16_t* scales, 
   return hipGetLastError();
 }
 
+namespace {
+
+// The three launches of a histogram into the given partial histograms
+// (cleared by a kernel, not a memset, so the sequence can be captured).
+hipError_t histogram_with_parts(const int8_t* codes, int64_t n, bool accumulate, int64_t* hist,
+                                unsigned long long* parts, hipStream_t s) {
+  hipLaunchKernelGGL(zero_parts_kernel, dim3(kHistParts), dim3(256), 0, s, parts);
+  if (n > 0) hipLaunchKernelGGL(hist_kernel, dim3(grid_for(n, 16)), dim3(kThreads), 0, s, codes, n, parts);
+  hipLaunchKernelGGL(hist_finish_kernel, dim3(1), dim3(256), 0, s, parts, (int)accumulate,
+                     reinterpret_cast<long long*>(hist));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Scratch of launch_code_histogram_noalloc: the kHistParts partial
+// histograms (128 KiB).  Every device holds its own copy of this array for
+// as long as the library stays loaded; host code reaches it only through the
+// address hipGetSymbolAddress returns with that device current.
+static __device__ __align__(256) unsigned long long scratch[256 * kHistParts];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned long long* g_scratch[kMaxDevices] = {};
+}  // namespace
+
 hipError_t launch_code_histogram(const int8_t* codes, int64_t n, bool accumulate, int64_t* hist, hipStream_t s) {
   // the partial histograms live in stream-ordered memory, so calls on
   // different streams never share them
   unsigned long long* parts = nullptr;
   hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&parts), sizeof(unsigned long long) * 256 * kHistParts, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(zero_parts_kernel, dim3(kHistParts), dim3(256), 0, s, parts);
-  if (n > 0) hipLaunchKernelGGL(hist_kernel, dim3(grid_for(n, 16)), dim3(kThreads), 0, s, codes, n, parts);
-  hipLaunchKernelGGL(hist_finish_kernel, dim3(1), dim3(256), 0, s, parts, (int)accumulate,
-                     reinterpret_cast<long long*>(hist));
-  e = hipGetLastError();
+  e = histogram_with_parts(codes, n, accumulate, hist, parts, s);
   const hipError_t f = hipFreeAsync(parts, s);
   return e != hipSuccess ? e : f;
+}
+
+hipError_t code_histogram_scratch(unsigned long long** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = static_cast<unsigned long long*>(p);
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_code_histogram_noalloc(const int8_t* codes, int64_t n, bool accumulate, int64_t* hist,
+                                         hipStream_t s) {
+  unsigned long long* parts = nullptr;
+  hipError_t e = code_histogram_scratch(&parts);
+  if (e != hipSuccess) return e;
+  return histogram_with_parts(codes, n, accumulate, hist, parts, s);
+}
+
+int64_t code_histogram_max_codes() {
+  // hist_kernel's workgroups: one per kGroupsPerBlock groups of 16 codes,
+  // at most 2^31 - 1 of them in one launch
+  return (int64_t)INT32_MAX * kGroupsPerBlock * 16;
 }
 
 hipError_t launch_code_entropy(const int64_t* hist, double* out, hipStream_t s) {
