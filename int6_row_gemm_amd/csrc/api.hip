@@ -343,19 +343,28 @@ int i6g_plan_windows(int64_t n_tokens, int32_t window, int32_t stride, int64_t* 
 // Validation and the host-side quantile split shared by both quantiser
 // entry points: pos = q * (cols - 1) in binary64, lo = floor(pos), the
 // kernel keeps the cols - lo largest |w| and interpolates with f = pos - lo.
-static int quant_plan(const char* who, const void* w, const void* codes, const void* scales,
+static bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+static int quant_plan(const char* who, int job, const void* w, const void* codes, const void* scales,
                       int64_t rows, int64_t cols, int bits, double clip_quantile, int32_t* topk,
                       float* frac) {
-  if (!w || !codes || !scales) return fail(I6G_EINVAL, "%s: NULL array", who);
-  if (rows < 1 || cols < 1) return fail(I6G_EINVAL, "%s: rows and cols must be >= 1", who);
-  if (bits != 5 && bits != 6 && bits != 8) return fail(I6G_EINVAL, "%s: bits must be 5, 6 or 8", who);
+  // the caller's name (and job number), formatted only for an error
+  char name[64];
+  auto id = [&]() -> const char* {
+    if (job < 0) return who;
+    snprintf(name, sizeof name, "%s job %d", who, job);
+    return name;
+  };
+  if (!w || !codes || !scales) return fail(I6G_EINVAL, "%s: NULL array", id());
+  if (rows < 1 || cols < 1) return fail(I6G_EINVAL, "%s: rows and cols must be >= 1", id());
+  if (bits != 5 && bits != 6 && bits != 8) return fail(I6G_EINVAL, "%s: bits must be 5, 6 or 8", id());
   if (!(clip_quantile > 0.0 && clip_quantile <= 1.0))
-    return fail(I6G_EINVAL, "%s: clip_quantile must be in (0, 1]", who);
-  if (cols > 65536) return fail(I6G_EUNSUPPORTED, "%s: cols > 65536", who);
+    return fail(I6G_EINVAL, "%s: clip_quantile must be in (0, 1]", id());
+  if (cols > 65536) return fail(I6G_EUNSUPPORTED, "%s: cols > 65536", id());
   const double pos = clip_quantile * (double)(cols - 1);
   const int64_t lo = (int64_t)floor(pos);
   if (cols - lo > 8)
-    return fail(I6G_EUNSUPPORTED, "%s: quantile needs the %lld largest values (max 8)", who,
+    return fail(I6G_EUNSUPPORTED, "%s: quantile needs the %lld largest values (max 8)", id(),
                 (long long)(cols - lo));
   *topk = (int32_t)(cols - lo);
   *frac = (float)(pos - (double)lo);
@@ -366,7 +375,7 @@ int i6g_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int bits, 
                       int8_t* codes_dev, uint16_t* scales_dev, int32_t* flags_dev, void* stream) {
   int32_t topk = 0;
   float frac = 0.0f;
-  int rc = quant_plan("quantize_rows", w_dev, codes_dev, scales_dev, rows, cols, bits, clip_quantile,
+  int rc = quant_plan("quantize_rows", -1, w_dev, codes_dev, scales_dev, rows, cols, bits, clip_quantile,
                       &topk, &frac);
   if (rc) return rc;
   int32_t* flags = nullptr;
@@ -381,6 +390,7 @@ int i6g_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int bits, 
   a.bits = bits;
   a.topk = topk;
   a.frac = frac;
+  a.shape = quant_unit_shape(cols, cols % 4 == 0 && aligned(w_dev, 16) && aligned(codes_dev, 4), topk);
   HIP_TRY(launch_quantize(a, (hipStream_t)stream));
   return I6G_OK;
 }
@@ -389,15 +399,23 @@ int i6g_quantize_rows_many(const i6g_quant_job* jobs, int32_t n_jobs, int bits, 
                            int32_t* flags_dev, void* stream) {
   if (!jobs || n_jobs < 1) return fail(I6G_EINVAL, "quantize_rows_many: need n_jobs >= 1 jobs");
   std::vector<QuantJob> plan(n_jobs);
+  std::vector<int64_t> units(n_jobs);
   for (int j = 0; j < n_jobs; ++j) {
     const i6g_quant_job& J = jobs[j];
-    char who[64];
-    snprintf(who, sizeof who, "quantize_rows_many job %d", j);
-    int rc = quant_plan(who, J.w, J.codes, J.scales, J.rows, J.cols, bits, clip_quantile, &plan[j].topk,
-                        &plan[j].frac);
+    int32_t topk = 0;
+    float frac = 0.0f;
+    int rc = quant_plan("quantize_rows_many", j, J.w, J.codes, J.scales, J.rows, J.cols, bits, clip_quantile, &topk, &frac);
     if (rc) return rc;
     plan[j].w = J.w; plan[j].codes = J.codes; plan[j].scales = J.scales;
     plan[j].cols = (int32_t)J.cols;
+    plan[j].topk = (int16_t)topk;
+    plan[j].frac = frac;
+    const bool vec = J.cols % 4 == 0 && aligned(J.w, 16) && aligned(J.codes, 4);
+    const int shape = quant_unit_shape(J.cols, vec, topk);
+    const int per = quant_unit_rows(shape);
+    plan[j].shape = (uint8_t)shape;
+    plan[j].last = (uint8_t)(J.rows - (J.rows - 1) / per * per);
+    units[j] = (J.rows + per - 1) / per;
   }
   int32_t* flags = nullptr;
   if (int rc = flag_word(flags_dev, &flags)) return rc;
@@ -406,23 +424,21 @@ int i6g_quantize_rows_many(const i6g_quant_job* jobs, int32_t n_jobs, int bits, 
     a.n = std::min(kQuantJobs, n_jobs - j0);
     a.bits = bits;
     a.flags = flags;
-    a.row0[0] = 0;
+    a.unit0[0] = 0;
     for (int j = 0; j < a.n; ++j) {
       a.job[j] = plan[j0 + j];
-      a.row0[j + 1] = a.row0[j] + jobs[j0 + j].rows;
+      a.unit0[j + 1] = a.unit0[j] + units[j0 + j];
     }
     HIP_TRY(launch_quantize_many(a, (hipStream_t)stream));
   }
   return I6G_OK;
 }
 
-static bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
-
 int i6g_fake_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int bits, double clip_quantile,
                            int out_dtype, void* out_dev, int32_t* flags_dev, void* stream) {
   int32_t topk = 0;
   float frac = 0.0f;
-  int rc = quant_plan("fake_quantize_rows", w_dev, out_dev, out_dev, rows, cols, bits, clip_quantile, &topk,
+  int rc = quant_plan("fake_quantize_rows", -1, w_dev, out_dev, out_dev, rows, cols, bits, clip_quantile, &topk,
                       &frac);
   if (rc) return rc;
   if (out_dtype != I6G_DTYPE_F32 && out_dtype != I6G_DTYPE_BF16)
@@ -439,6 +455,8 @@ int i6g_fake_quantize_rows(const float* w_dev, int64_t rows, int64_t cols, int b
   a.frac = frac;
   a.fq = out_dev;
   a.fq_bf16 = out_dtype == I6G_DTYPE_BF16;
+  a.shape = quant_unit_shape(cols, cols % 4 == 0 && aligned(w_dev, 16) && aligned(out_dev, a.fq_bf16 ? 8 : 16),
+                             topk);
   HIP_TRY(launch_fake_quantize(a, (hipStream_t)stream));
   return I6G_OK;
 }

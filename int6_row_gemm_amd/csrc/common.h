@@ -50,7 +50,23 @@ struct QuantArgs {
   float frac;     // fp32 interpolation weight f
   void* fq;       // fake quantisation: [rows, cols] output, fp32 or bf16
   int32_t fq_bf16;
+  int32_t shape;  // quant_unit_shape of the matrix
 };
+
+// How a quantiser wavefront takes rows.  Vector rows (cols a multiple of 4,
+// 16-byte aligned weights, aligned outputs) of at most 2048 columns whose
+// quantile needs at most the two largest |w| are held in registers, in
+// units of one to four rows (at most 8 KiB per wave): shape 0 = four rows
+// of <= 512 columns, 1 = two rows of <= 1024, 2 = one row of <= 1536,
+// 3 = one row of <= 2048.  Other rows (kShapeRowwise) are read twice, one
+// row per wave.
+constexpr int kShapeRowwise = 4;
+__host__ __device__ inline int quant_unit_shape(int64_t cols, bool vec, int topk) {
+  if (!vec || cols > 2048 || topk > 2) return kShapeRowwise;
+  return cols <= 512 ? 0 : cols <= 1024 ? 1 : cols <= 1536 ? 2 : 3;
+}
+__host__ __device__ inline int quant_unit_rows(int shape) { return shape == 0 ? 4 : shape == 1 ? 2 : 1; }
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 // code * fp32 scale per element (fake quantisation) into a.fq
 hipError_t launch_fake_quantize(const QuantArgs& a, hipStream_t s);
@@ -69,21 +85,25 @@ struct NoisyArgs {
 };
 hipError_t launch_noisy_weights(const NoisyArgs& a, hipStream_t s);
 
-// Several matrices in one launch: row r of the concatenated rows belongs to
-// the last job j with row0[j] <= r.  The table travels in the kernel
-// arguments (at most 4 KiB), so no device buffer is needed.
+// Several matrices in one launch: job j's rows are cut into units of
+// quant_unit_rows(shape) rows (its last unit holds `last`), and unit u of
+// the concatenation belongs to the last job j with unit0[j] <= u.  The table
+// travels in the kernel arguments (at most 4 KiB), so no device buffer is
+// needed.
 constexpr int kQuantJobs = 80;   // the 66 matrices of an 11-layer model fit one launch
 struct QuantJob {
   const float* w;
   int8_t* codes;
   uint16_t* scales;
-  int32_t cols, topk;
+  int32_t cols;
+  int16_t topk;
+  uint8_t shape, last;
   float frac;
 };
 struct QuantManyArgs {
   int32_t n, bits;
   int32_t* flags;
-  int64_t row0[kQuantJobs + 1];
+  int64_t unit0[kQuantJobs + 1];
   QuantJob job[kQuantJobs];
 };
 static_assert(sizeof(QuantManyArgs) <= 4096, "kernel arguments are limited to 4 KB");

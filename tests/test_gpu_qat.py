@@ -9,7 +9,7 @@ from gpu_common import need_gpu, print_case
 
 pytestmark = pytest.mark.gpu
 
-SHAPES = [(1, 1), (3, 5), (7, 64), (16, 300), (33, 512), (1536, 512), (512, 1536), (5, 4099)]
+SHAPES = [(1, 1), (3, 5), (7, 64), (16, 300), (33, 512), (1536, 512), (512, 1536), (9, 2044), (5, 4099)]
 
 
 def _dev(a):

@@ -56,16 +56,50 @@ def test_adversarial_rows_bit_exact(cols, bits, q):
 def test_ragged_rows_and_many_rows():
     g = need_gpu()
     rng = np.random.default_rng(5)
-    for rows, cols in [(1, 1), (3, 7), (5, 65), (4097, 130)]:
+    # widths around the register-resident limit (2048 columns, in chunks of
+    # 512) and past it, where rows are read twice
+    for rows, cols in [(1, 1), (3, 7), (5, 65), (4097, 130), (6, 4), (5, 516), (3, 1028),
+                       (4, 2044), (3, 2052), (2, 4096)]:
         w = rng.normal(0, 0.02, size=(rows, cols)).astype(np.float32)
         _assert_same(g, w, 6, 0.9999984 if cols > 1 else 1.0, f"ragged/{rows}x{cols}")
+
+
+def _half_integer_rows(rng, cols, bits):
+    """Rows whose weights sit a few ulps around (n + 1/2) * scale for every
+    half-integer n of the code range, with the row maximum fixing the clip
+    value at q = 1: the quotients the kernel settles by division."""
+    top = {5: 15.0, 6: 127.0, 8: 127.0}[bits]
+    rows = []
+    for _ in range(6):
+        c = np.float32(rng.uniform(1e-4, 1.0))
+        scale = np.float32(c / np.float32(top))
+        h = (np.arange(-int(top) - 1, int(top) + 1) + 0.5).astype(np.float32)
+        v = (h * scale).astype(np.float32)
+        k = rng.integers(-4, 5, size=v.shape)
+        for i in range(v.size):
+            for _ in range(abs(int(k[i]))):
+                v[i] = np.nextafter(v[i], np.float32(np.inf if k[i] > 0 else -np.inf))
+        row = np.resize(v, cols)
+        rng.shuffle(row)
+        row[cols // 2] = c
+        rows.append(np.clip(row, -c, c))
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("cols", [100, 512, 1024, 1536, 4096])
+@pytest.mark.parametrize("bits", [5, 6, 8])
+def test_half_integer_quotients_bit_exact(cols, bits):
+    g = need_gpu()
+    rng = np.random.default_rng(1000 * bits + cols)
+    w = _half_integer_rows(rng, cols, bits)
+    _assert_same(g, w, bits, 1.0, f"half-integers/{cols}/int{bits}")
 
 
 def test_nonfinite_row_flagged():
     import torch
     g = need_gpu()
-    w = np.random.default_rng(6).normal(0, 0.02, size=(4, 64)).astype(np.float32)
-    w[2, 10] = np.inf
+    w = np.random.default_rng(6).normal(0, 0.02, size=(4, 1540)).astype(np.float32)
+    w[2, 1537] = np.inf
     flags = torch.zeros(1, dtype=torch.int32, device="cuda")
     codes, scales = g.quantize_rows(torch.from_numpy(w).cuda(), 6, 1.0, flags)
     torch.cuda.synchronize()
