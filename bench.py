@@ -191,7 +191,7 @@ def main():
             ach, peak, unit, bound, per = by / (ms * 1e6), PEAK_HBM_GBS, "GB/s", "hbm", by / n
         # the committed counters were taken on the 11-layer workload with its
         # default batching and one stream; any other set-up reports none
-        same_setup = args.config == "11l" and args.batch_windows in (0, 24) and args.streams in (0, 1)
+        same_setup = args.config == "11l" and args.batch_windows in (0, 64) and args.streams in (0, 1)
         roofline = {"kernel": dom, "bound": bound, "achieved": ach, "peak": peak, "unit": unit,
                     "frac": ach / peak, "traffic": counter_traffic(args.traffic, dom) if same_setup else None,
                     "avg_launch_us": avg_us, "launches": n, "algorithmic_per_launch": per,

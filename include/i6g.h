@@ -324,7 +324,8 @@ int i6g_plan_windows(int64_t n_tokens, int32_t window, int32_t stride, int64_t* 
 /* Model options (tuning and testing; results do not depend on them beyond
  * floating-point rounding):
  *   I6G_OPT_BATCH_WINDOWS  windows per batch in i6g_score_tokens (0 = the
- *                          default, about 49152 rows per batch); an upper
+ *                          default: about 131072 rows per batch with the
+ *                          fused block tail, 49152 without); an upper
  *                          bound: a batch is also kept within the rows
  *                          i6g_score_tokens can index (at most 2^24 - 1);
  *   I6G_OPT_PRUNE_LAST     1 (default): the final layer computes queries,
