@@ -125,14 +125,27 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // code fragments of wave w: output projection / down projection (64
   // columns = tile w/2, slices 2(w&1), 2(w&1)+1: four 1 KB fragments in a
   // row) and up projection (32 columns: slice wn of a 128-column chunk);
-  // wave-uniform bases, each lane adds its own 16 bytes.  Codes are loaded
-  // one K step ahead of the MFMAs that use them.
+  // wave-uniform bases, each lane adds its own 16 bytes.  Output- and
+  // down-projection codes are loaded half a K step ahead of the MFMAs that
+  // use them, up-projection codes two K steps ahead (in the registers the
+  // down projection's four fragments use; the up projection needs two per
+  // step).  sched_barrier fences keep the compiler from sinking those loads
+  // below the MFMAs or pulling the widening of loads in flight up among them.
   const int8_t* const o_codes = a.o_frag + ((int64_t)(w >> 1) * 8 * 4 + 2 * (w & 1)) * 2 * 64 * 16;
   const int8_t* const p_codes = a.proj_frag + ((int64_t)(w >> 1) * nk_proj * 4 + 2 * (w & 1)) * 2 * 64 * 16;
   const int8_t* const f_codes = a.fc_frag + (int64_t)wn * 2 * 64 * 16;
-  const int loff = lane * 16;
+  // the lane's 16-byte offset, recomputed at every code load (two VALU
+  // ops) rather than held for the whole kernel: under full register
+  // pressure a held copy is spilled, and its reload waits for every load in
+  // flight
+  auto loff16 = [&]() -> int {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l << 4;
+  };
   uint4 cq0, cq1, cq2, cq3;
   auto load4 = [&](const int8_t* base) {
+    const int loff = loff16();
     cq0 = *reinterpret_cast<const uint4*>(base + loff);
     cq1 = *reinterpret_cast<const uint4*>(base + loff + 1024);
     cq2 = *reinterpret_cast<const uint4*>(base + loff + 2048);
@@ -141,10 +154,29 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // (offsets below 2^31: at most F / 64 K steps of 8 KB per 128-column tile)
   auto load_o = [&](int kt) { load4(o_codes + kt * KSTEP_BYTES); };
   auto load_p = [&](int kt) { load4(p_codes + kt * KSTEP_BYTES); };
-  auto load_f = [&](int c, int kt) {   // chunk c (128 hidden columns), K step kt of 8
-    const int off = (c * 8 + kt) * KSTEP_BYTES + loff;
-    cq0 = *reinterpret_cast<const uint4*>(f_codes + off);
-    cq1 = *reinterpret_cast<const uint4*>(f_codes + off + 1024);
+  // up projection: chunk c (128 hidden columns), K step kt of 8; even steps
+  // (odd = 0) go to cq0 / cq1, odd steps to cq2 / cq3 (the loop keeps two
+  // steps in flight)
+  auto load_f = [&](int c, int kt, int odd) {
+    const int off = (c * 8 + kt) * KSTEP_BYTES + loff16();
+    if (odd) {
+      cq2 = *reinterpret_cast<const uint4*>(f_codes + off);
+      cq3 = *reinterpret_cast<const uint4*>(f_codes + off + 1024);
+    } else {
+      cq0 = *reinterpret_cast<const uint4*>(f_codes + off);
+      cq1 = *reinterpret_cast<const uint4*>(f_codes + off + 1024);
+    }
+  };
+  // half h of a down-projection step's four fragments (cq0 / cq1 or cq2 / cq3)
+  auto load_p_half = [&](int kt, int h) {
+    const int8_t* base = p_codes + kt * KSTEP_BYTES + loff16();
+    if (h) {
+      cq2 = *reinterpret_cast<const uint4*>(base + 2048);
+      cq3 = *reinterpret_cast<const uint4*>(base + 3072);
+    } else {
+      cq0 = *reinterpret_cast<const uint4*>(base);
+      cq1 = *reinterpret_cast<const uint4*>(base + 1024);
+    }
   };
 
   // A TM x 512 binary16 tile of rows m0.. into the A buffer by direct loads
@@ -200,6 +232,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // do the next step's loads take over the code registers (fewer live
   // registers than widening both halves first).
   auto wide_step = [&](const char* base, int rowbytes, int kc0, auto&& next_load) {
+    asm volatile("" : "+s"(kc0));   // LDS addresses computed where used, not held
     {
       const actx8 wf[4] = {widen8(cq0.x, cq0.y), widen8(cq1.x, cq1.y), widen8(cq2.x, cq2.y), widen8(cq3.x, cq3.y)};
 #pragma unroll
@@ -212,6 +245,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     const actx8 wf[4] = {widen8(cq0.z, cq0.w), widen8(cq1.z, cq1.w), widen8(cq2.z, cq2.w), widen8(cq3.z, cq3.w)};
     next_load();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const actx8 af = *reinterpret_cast<const actx8*>(base + (rowbytes == DM * 2 ? a_off(16 * i + lr, kc0 + 4 + lg)
@@ -221,12 +255,11 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 #pragma unroll 1
-  for (int kt = 0; kt < 8; ++kt) {
-    wide_step(As, DM * 2, 8 * kt, [&] {
-      if (kt + 1 < 8) load_o(kt + 1);
-      else load_f(0, 0);
-    });
-  }
+  for (int kt = 0; kt < 7; ++kt) wide_step(As, DM * 2, 8 * kt, [&] { load_o(kt + 1); });
+  wide_step(As, DM * 2, 56, [&] {
+    load_f(0, 0, 0);
+    load_f(0, 1, 1);
+  });
 
   // ---- x1 = acc * s_o; the MLP input and (parallel lanes) its RMS factors
   float rinv[FB];
@@ -310,27 +343,39 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int ii = 0; ii < FB; ++ii) hacc[ii][0] = hacc[ii][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     // the scales of the lane's 8 hidden columns, kept packed until used
     const uint4 sfp = *reinterpret_cast<const uint4*>(a.fc_scale + HC * c + 32 * wn + 8 * lg);
-#pragma unroll 1
-    for (int kt = 0; kt < 8; ++kt) {
-      {
-        const actx8 w0 = widen8(cq0.x, cq0.y), w1 = widen8(cq1.x, cq1.y);
-#pragma unroll
-        for (int ii = 0; ii < FB; ++ii) {
-          const actx8 af = *reinterpret_cast<const actx8*>(As + a_off(16 * (FB * wm + ii) + lr, 8 * kt + lg));
-          hacc[ii][0] = MFMA(w0, af, hacc[ii][0]);
-          hacc[ii][1] = MFMA(w1, af, hacc[ii][1]);
-        }
-      }
-      const actx8 w0 = widen8(cq0.z, cq0.w), w1 = widen8(cq1.z, cq1.w);
-      if (kt + 1 < 8) load_f(c, kt + 1);
-      else load_p(2 * c);
+    // two K steps per trip: step kt's codes sit in cq0 / cq1 and step
+    // kt + 1's in cq2 / cq3, each loaded two steps before it is used; after
+    // the last step the down projection's first step follows, half by half
+    auto fc_step = [&](uint4 ca, uint4 cb, int k8, auto&& next_load) {
+      // an opaque copy of the K offset keeps the compiler from computing
+      // every step's LDS addresses up front and holding them (it spills them)
+      asm volatile("" : "+s"(k8));
+      const actx8 w0 = widen8(ca.x, ca.y), w1 = widen8(cb.x, cb.y);
+      const actx8 w2 = widen8(ca.z, ca.w), w3 = widen8(cb.z, cb.w);
+      next_load();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ii = 0; ii < FB; ++ii) {
-        const actx8 af = *reinterpret_cast<const actx8*>(As + a_off(16 * (FB * wm + ii) + lr, 8 * kt + 4 + lg));
+        const actx8 af = *reinterpret_cast<const actx8*>(As + a_off(16 * (FB * wm + ii) + lr, k8 + lg));
         hacc[ii][0] = MFMA(w0, af, hacc[ii][0]);
         hacc[ii][1] = MFMA(w1, af, hacc[ii][1]);
       }
+#pragma unroll
+      for (int ii = 0; ii < FB; ++ii) {
+        const actx8 af = *reinterpret_cast<const actx8*>(As + a_off(16 * (FB * wm + ii) + lr, k8 + 4 + lg));
+        hacc[ii][0] = MFMA(w2, af, hacc[ii][0]);
+        hacc[ii][1] = MFMA(w3, af, hacc[ii][1]);
+      }
+      // nothing that waits on the loads above is pulled in among the MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll 1
+    for (int kt = 0; kt < 6; kt += 2) {
+      fc_step(cq0, cq1, 8 * kt, [&] { load_f(c, kt + 2, 0); });
+      fc_step(cq2, cq3, 8 * kt + 8, [&] { load_f(c, kt + 3, 1); });
     }
+    fc_step(cq0, cq1, 48, [&] { load_p_half(2 * c, 0); });
+    fc_step(cq2, cq3, 56, [&] { load_p_half(2 * c, 1); });
     // act(acc * s_fc * rinv)^2 in binary16: the lane's 8 hidden columns
     // 32 wn + 8 lg .. are chunk 4 wn + lg of physical row 16 i + lr
     float sf[8];
@@ -376,7 +421,10 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // down projection of the chunk: acc += h . code_proj^T, K = 128
     wide_step(Hs, HC * 2, 0, [&] { load_p(2 * c + 1); });
     wide_step(Hs, HC * 2, 8, [&] {
-      if (c + 1 < nchunks) load_f(c + 1, 0);
+      if (c + 1 < nchunks) {
+        load_f(c + 1, 0, 0);
+        load_f(c + 1, 1, 1);
+      }
     });
   }
 
