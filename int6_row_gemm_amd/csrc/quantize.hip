@@ -251,17 +251,18 @@ __device__ __attribute__((noinline)) void quantize_row_k(const float* w, int col
 // |t| (2^-23 + 2^-24) (1 + 2^-23) < 2^-15 of t, and fl(t) within 2^-17 of
 // t.  When p is at least 2^-14 > 2^-15 + 2^-17 from every half-integer, p,
 // t and fl(t) lie strictly between the same two half-integers and round to
-// the same integer.  `near` records the other case, where the caller redoes the
-// row with quant_code (about one int6 row of 512 in seventeen).
+// the same integer.  dist keeps the largest |p - rint(p)|; above 1/2 - 2^-14
+// the caller redoes the row with quant_code (about one int6 row of 512 in
+// seventeen).
 // Clipping: |w| > c gives |t| > 127 (int8, int6) or > 15 (int5), so the
 // clamps below yield the code of +-c, which is what clipping gives: +-127,
 // +-15, or 124 / -128 for int6 (rint(127 / 4) * 4 = 128).  Clipping keeps
 // int5 codes in [-15, 15], so that is the clamp here.
 template <int BITS>
-__device__ __attribute__((always_inline)) float fast_code(float w, float inv, bool& near) {
+__device__ __attribute__((always_inline)) float fast_code(float w, float inv, float& dist) {
   const float r = w * inv;
   const float k = rintf(r);
-  near |= fabsf(r - k) > 0.5f - 0x1p-14f;
+  dist = fmaxf(dist, fabsf(r - k));
   if (BITS == 8) return __builtin_amdgcn_fmed3f(k, -127.0f, 127.0f);
   if (BITS == 5) return __builtin_amdgcn_fmed3f(k, -15.0f, 15.0f);
   const float k4 = rintf(k * 0.25f);
@@ -380,16 +381,19 @@ __device__ __attribute__((always_inline)) void process_unit(float4 (&x)[8], int 
     rs.c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_rs.c), r));
     rs.scale = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_rs.scale), r));
     rs.inv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_rs.inv), r));
-    bool near = false;
+    float dist = 0.0f;
 #pragma unroll
     for (int q = 0; q < 2 * NCH; ++q) {
       const int col = 512 * (q / 2) + 4 * ((q & 1) * kWave + lane);
       const float4 v = x[2 * NCH * r + q];
-      const float k0 = fast_code<BITS>(v.x, rs.inv, near), k1 = fast_code<BITS>(v.y, rs.inv, near);
-      const float k2 = fast_code<BITS>(v.z, rs.inv, near), k3 = fast_code<BITS>(v.w, rs.inv, near);
+      const float k0 = fast_code<BITS>(v.x, rs.inv, dist), k1 = fast_code<BITS>(v.y, rs.inv, dist);
+      const float k2 = fast_code<BITS>(v.z, rs.inv, dist), k3 = fast_code<BITS>(v.w, rs.inv, dist);
       if (col < cols) put4<FQ>(k0, k1, k2, k3, col, rs.scale, cr, fr, fq_bf16);
+      // folded into one register here: left to itself the compiler keeps
+      // every product and its rounding alive to the end of the row
+      asm volatile("" : "+v"(dist));
     }
-    if (__builtin_expect(__any(near), 0)) {
+    if (__builtin_expect(__any(dist > 0.5f - 0x1p-14f), 0)) {
       // a quotient near a half-integer somewhere in the row: the row again
       // with the correctly rounded division (these stores follow the ones
       // above from the same lanes, so they win)
