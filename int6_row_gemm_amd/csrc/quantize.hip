@@ -258,17 +258,23 @@ __device__ __attribute__((noinline)) void quantize_row_k(const float* w, int col
 // clamps below yield the code of +-c, which is what clipping gives: +-127,
 // +-15, or 124 / -128 for int6 (rint(127 / 4) * 4 = 128).  Clipping keeps
 // int5 codes in [-15, 15], so that is the clamp here.
-template <int BITS>
+// BIAS: the code + 128 (the byte the packed store wants), in as few
+// operations as the width allows.
+template <int BITS, bool BIAS = false>
 __device__ __attribute__((always_inline)) float fast_code(float w, float inv, float& dist) {
   const float r = w * inv;
   const float k = rintf(r);
   dist = fmaxf(dist, fabsf(r - k));
-  if (BITS == 8) return __builtin_amdgcn_fmed3f(k, -127.0f, 127.0f);
-  if (BITS == 5) return __builtin_amdgcn_fmed3f(k, -15.0f, 15.0f);
+  if (BITS == 8) return BIAS ? __builtin_amdgcn_fmed3f(k + 128.0f, 1.0f, 255.0f) : __builtin_amdgcn_fmed3f(k, -127.0f, 127.0f);
+  if (BITS == 5) return BIAS ? __builtin_amdgcn_fmed3f(k + 128.0f, 113.0f, 143.0f) : __builtin_amdgcn_fmed3f(k, -15.0f, 15.0f);
   const float k4 = rintf(k * 0.25f);
-  return __builtin_amdgcn_fmed3f(k4 * 4.0f, -128.0f, 124.0f);
+  // 4 k4 + 128 is exact (|k4| is small, or the clamp takes over)
+  return BIAS ? __builtin_amdgcn_fmed3f(__builtin_fmaf(k4, 4.0f, 128.0f), 0.0f, 252.0f)
+              : __builtin_amdgcn_fmed3f(k4 * 4.0f, -128.0f, 124.0f);
 }
 
+// Four columns from the register-resident path: fake-quantised values
+// (FQ, from codes) or packed codes (from code + 128).
 template <bool FQ>
 __device__ __attribute__((always_inline)) void put4(float k0, float k1, float k2, float k3, int col, float scale,
                                                     int8_t* codes, void* fq, int fq_bf16) {
@@ -284,9 +290,13 @@ __device__ __attribute__((always_inline)) void put4(float k0, float k1, float k2
       *reinterpret_cast<float4*>(static_cast<float*>(fq) + col) = make_float4(q0, q1, q2, q3);
     }
   } else {
-    const uint32_t packed = ((uint32_t)(uint8_t)(int)k0) | ((uint32_t)(uint8_t)(int)k1 << 8) |
-                            ((uint32_t)(uint8_t)(int)k2 << 16) | ((uint32_t)(uint8_t)(int)k3 << 24);
-    *reinterpret_cast<uint32_t*>(codes + col) = packed;
+    // k0 .. k3 are code + 128 (fast_code BIAS): v_cvt_pk_u8_f32 packs each
+    // into its byte, the xor takes the bias back off
+    uint32_t b = __builtin_amdgcn_cvt_pk_u8_f32(k0, 0, 0u);
+    b = __builtin_amdgcn_cvt_pk_u8_f32(k1, 1, b);
+    b = __builtin_amdgcn_cvt_pk_u8_f32(k2, 2, b);
+    b = __builtin_amdgcn_cvt_pk_u8_f32(k3, 3, b);
+    *reinterpret_cast<uint32_t*>(codes + col) = b ^ 0x80808080u;
   }
 }
 
@@ -386,8 +396,8 @@ __device__ __attribute__((always_inline)) void process_unit(float4 (&x)[8], int 
     for (int q = 0; q < 2 * NCH; ++q) {
       const int col = 512 * (q / 2) + 4 * ((q & 1) * kWave + lane);
       const float4 v = x[2 * NCH * r + q];
-      const float k0 = fast_code<BITS>(v.x, rs.inv, dist), k1 = fast_code<BITS>(v.y, rs.inv, dist);
-      const float k2 = fast_code<BITS>(v.z, rs.inv, dist), k3 = fast_code<BITS>(v.w, rs.inv, dist);
+      const float k0 = fast_code<BITS, !FQ>(v.x, rs.inv, dist), k1 = fast_code<BITS, !FQ>(v.y, rs.inv, dist);
+      const float k2 = fast_code<BITS, !FQ>(v.z, rs.inv, dist), k3 = fast_code<BITS, !FQ>(v.w, rs.inv, dist);
       if (col < cols) put4<FQ>(k0, k1, k2, k3, col, rs.scale, cr, fr, fq_bf16);
       // folded into one register here: left to itself the compiler keeps
       // every product and its rounding alive to the end of the row
