@@ -107,8 +107,9 @@ typedef struct {
 
 /*
  * i6g_quantize_rows_many -- i6g_quantize_rows (same steps, same results) on
- * n_jobs matrices at once, every row of up to 80 matrices a wavefront of one
- * launch, so that a model's many small matrices fill the device (the export
+ * n_jobs matrices at once, the rows of up to 80 matrices in one launch (a
+ * wavefront per row or per group of up to four short rows), so that a
+ * model's many small matrices fill the device (the export
  * step of [11L] 后训练量化导出 quantises every block matrix this way).
  * jobs is a host array of n_jobs entries; bits, clip_quantile and flags_dev
  * apply to all of them.  Errors: I6G_EINVAL for n_jobs < 1 or a NULL jobs
