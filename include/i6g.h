@@ -355,10 +355,18 @@ int i6g_plan_windows(int64_t n_tokens, int32_t window, int32_t stride, int64_t* 
  *                          leaving the chip; 0: as three GEMM launches.  The
  *                          same products in another rounding order: results
  *                          agree to fp32 rounding of the residual.
+ *   I6G_OPT_QKV_TILE       1 (default): for d_model = 512, head size 64 and
+ *                          no LoRA (and windows of at least 128 positions
+ *                          after padding to 64), the q/k/v projection runs as
+ *                          one kernel per 128-row tile computing every head
+ *                          of it, with the codes rearranged into per-head
+ *                          fragment order when the model is loaded; 0: the
+ *                          LDS-staged GEMM.  The same products accumulated
+ *                          in the same order: results are identical.
  * Errors: I6G_EINVAL for an unknown option or a value out of range. */
 enum {
   I6G_OPT_BATCH_WINDOWS = 0, I6G_OPT_PRUNE_LAST = 1, I6G_OPT_STREAMS = 2, I6G_OPT_REGISTER_CODES = 3,
-  I6G_OPT_FUSED_TAIL = 4
+  I6G_OPT_FUSED_TAIL = 4, I6G_OPT_QKV_TILE = 5
 };
 int i6g_set_option(i6g_model* m, int option, int64_t value);
 

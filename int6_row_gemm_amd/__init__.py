@@ -287,6 +287,12 @@ class Model:
         one kernel (d_model 512); False: three GEMM launches."""
         _check(lib().i6g_set_option(self._h, 4, int(bool(on))))
 
+    def set_qkv_tile(self, on):
+        """True (default): the q/k/v projection as one kernel per 128-row
+        tile (d_model 512, head size 64, no LoRA); False: the LDS-staged
+        GEMM."""
+        _check(lib().i6g_set_option(self._h, 5, int(bool(on))))
+
     def score(self, tokens, nbytes, window, stride, nats=None, totals=None, check=True):
         """Score a device token stream; returns (nats [N-1] fp32, totals [4] fp64)
         with totals = (sum nats, sum bytes, scored predictions, bits per byte)."""

@@ -77,6 +77,9 @@ struct BlockDev {
   // fused block tail reads o, fc and proj in fragment order (o and proj rows
   // with a zero scale as zero codes)
   DevBuf fc_frag, proj_frag, o_frag;
+  // q/k/v codes in per-head fragment order for the one-tile q/k/v kernel
+  // (d_model 512, head size 64, no LoRA; empty otherwise)
+  DevBuf qkv_frag;
 };
 
 struct TimeRec {
@@ -187,6 +190,7 @@ struct i6g_model {
   int prune_last = 1;
   int register_codes = 1;
   int fused_tail = 1;
+  int qkv_tile = 1;
   // timing
   bool timing = false;
   uint32_t timing_mask = 0;
@@ -736,6 +740,13 @@ int i6g_load_model(const i6g_model_desc* desc, void* stream, i6g_model** out) {
         launch_shuffle_codes(bd.o_codes.as<int8_t>(), d, d, bd.o_scales.as<uint16_t>(), bd.o_frag.as<int8_t>(),
                              s) != hipSuccess)
       return cleanup(fail(I6G_EDEVICE, "load_model: rearranging the codes failed"));
+    if (qkv_tile_supported(d, m->hd, m->Hq, m->Hkv, m->rope_dims, m->lora_r)) {
+      if (bd.qkv_frag.ensure((size_t)m->nqkv * d) != hipSuccess)
+        return cleanup(fail(I6G_ENOMEM, "load_model: out of device memory"));
+      if (launch_shuffle_qkv_codes(bd.qkv_codes.as<int8_t>(), m->Hq, m->Hkv, d, m->rope_dims,
+                                   bd.qkv_frag.as<int8_t>(), s) != hipSuccess)
+        return cleanup(fail(I6G_EDEVICE, "load_model: rearranging the q/k/v codes failed"));
+    }
     if ((rc = check(bd.qkv_scales, m->nqkv, false)) || (rc = check(bd.o_scales, d, false)) ||
         (rc = check(bd.fc_scales, F, false)) || (rc = check(bd.proj_scales, d, false)))
       return cleanup(rc);
@@ -813,6 +824,9 @@ int i6g_set_option(i6g_model* m, int option, int64_t value) {
     case I6G_OPT_FUSED_TAIL:
       m->fused_tail = value != 0;
       return I6G_OK;
+    case I6G_OPT_QKV_TILE:
+      m->qkv_tile = value != 0;
+      return I6G_OK;
   }
   return fail(I6G_EINVAL, "set_option: unknown option %d", option);
 }
@@ -867,6 +881,9 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
   // Without it, 49152 rows (24 windows) split the separate GEMMs' tiles
   // evenly over the workgroups the device holds at once.
   const bool tail = m->fused_tail && m->d == 512 && m->F % 128 == 0 && P < INT32_MAX;
+  // the one-tile q/k/v kernel needs a row block of a tile to span at most
+  // two windows
+  const bool qkv_tile = m->qkv_tile && Lp >= 128;
   int Wb = m->batch_windows > 0 ? m->batch_windows : std::max(1, (tail ? 131072 : 49152) / Lp);
   Wb = (int)std::min<int64_t>({(int64_t)Wb, K, max_rows / Lp});
   int rc = ensure_scratch(m, Wb, Lp, s);
@@ -948,8 +965,10 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
         g.lora_bv = m->lora_bv.as<float>() + (size_t)e * kvd * m->lora_r;
       }
       const double fl_qkv = 2.0 * real_rows * m->nqkv * d;
+      const bool one_tile = qkv_tile && B.qkv_frag.p;
+      if (one_tile) g.Bp = B.qkv_frag.as<int8_t>();
       if ((rc = timed(m, I6G_K_QKV, s, fl_qkv, real_rows * (2.0 * d + 2.0 * m->nqkv) + (double)m->nqkv * d,
-                      [&] { return launch_gemm(EPI_QKV, g, s); })))
+                      [&] { return one_tile ? launch_qkv_tile(g, s) : launch_gemm(EPI_QKV, g, s); })))
         return rc;
 
       const bool pr = last && prune;

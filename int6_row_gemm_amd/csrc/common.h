@@ -159,6 +159,13 @@ struct GemmArgs {
 // fragment order of the register-fed GEMM path; Bp holds N * K bytes.  When
 // zero_scale_rows (binary16 [N]) is given, rows whose scale is +-0 are
 // written as zero codes.
+// q/k/v projection as one 128-row tile per workgroup (d_model 512, head size
+// 64, no LoRA): codes in per-head fragment order (launch_shuffle_qkv_codes)
+// passed as GemmArgs::Bp; the other arguments as for launch_gemm(EPI_QKV).
+bool qkv_tile_supported(int32_t d, int32_t hd, int32_t n_heads, int32_t n_kv, int32_t rope_dims, int32_t lora_r);
+hipError_t launch_shuffle_qkv_codes(const int8_t* B, int32_t n_heads, int32_t n_kv, int32_t K, int32_t rope_dims,
+                                    int8_t* Bp, hipStream_t s);
+hipError_t launch_qkv_tile(const GemmArgs& a, hipStream_t s);
 hipError_t launch_shuffle_codes(const int8_t* B, int32_t N, int32_t K, const uint16_t* zero_scale_rows, int8_t* Bp,
                                 hipStream_t s);
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);

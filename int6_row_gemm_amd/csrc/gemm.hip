@@ -50,36 +50,6 @@ constexpr int LDK = BK;      // LDS row stride in binary16 elements (128 bytes)
 // bank conflicts, where a 16-byte row padding costs a two-way conflict.
 __device__ inline int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
-// Rotation pairs of one q or k head with R rotated dims (partial RoPE):
-// pair p < R/2 is (p, p + R/2); the others pair up the unrotated dims as
-// (R + w, R + (hd - R)/2 + w), w = p - R/2, and turn by the identity.  For
-// R = hd these are the pairs (p, p + hd/2) of full RoPE.
-template <int HD>
-__device__ inline int pair_first(int p, int R) { return p < R / 2 ? p : R + (p - R / 2); }
-template <int HD>
-__device__ inline int pair_second(int p, int R) {
-  return p < R / 2 ? p + R / 2 : R + (HD - R) / 2 + (p - R / 2);
-}
-
-// Placement of the rows of one q or k head (HD rows) for the rotary
-// epilogue: the output rows 4g + e of fragment j (lane group g) are the
-// values t = 4j + e of that lane, and value t < HD/8 is the first dim of
-// pair g * HD/8 + t while value t + HD/8 is its second, so a lane holds
-// whole rotation pairs, and (R a multiple of HD/4) its first and its second
-// dims are two runs of HD/8 consecutive dims.
-template <int HD>
-__device__ inline int rope_phys(int u, int R) {
-  constexpr int Q8 = HD / 8;
-  const int h2 = R / 2, rest2 = (HD - R) / 2;
-  int p, second;
-  if (u < h2) { p = u; second = 0; }
-  else if (u < R) { p = u - h2; second = 1; }
-  else if (u < R + rest2) { p = h2 + (u - R); second = 0; }
-  else { p = h2 + (u - R - rest2); second = 1; }
-  const int t = p % Q8 + second * Q8;
-  return 16 * (t >> 2) + 4 * (p / Q8) + (t & 3);
-}
-
 template <int BM, int BN, bool RB>
 struct Smem {
   static constexpr int kBytes = (BM + (RB ? 0 : BN)) * LDK * 2;   // one A and (unless RB) one B tile
@@ -522,13 +492,19 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a, act* As, act* Bs, f
           }
         }
         float y1[Q8], y2[Q8];
+        {
+          // every product rounded on its own, no fused multiply-add (the
+          // one-tile q/k/v kernel rotates the same way, so both agree bit
+          // for bit)
+#pragma clang fp contract(off)
 #pragma unroll
-        for (int t = 0; t < Q8; t += 2) {
-          const float4 cs = csp[t / 2];   // (cos, sin) of indices c1b + t and c1b + t + 1
-          y1[t] = x1[t] * cs.x - x2[t] * cs.y;
-          y2[t] = x1[t] * cs.y + x2[t] * cs.x;
-          y1[t + 1] = x1[t + 1] * cs.z - x2[t + 1] * cs.w;
-          y2[t + 1] = x1[t + 1] * cs.w + x2[t + 1] * cs.z;
+          for (int t = 0; t < Q8; t += 2) {
+            const float4 cs = csp[t / 2];   // (cos, sin) of indices c1b + t and c1b + t + 1
+            y1[t] = x1[t] * cs.x - x2[t] * cs.y;
+            y2[t] = x1[t] * cs.y + x2[t] * cs.x;
+            y1[t + 1] = x1[t + 1] * cs.z - x2[t + 1] * cs.w;
+            y2[t + 1] = x1[t + 1] * cs.w + x2[t + 1] * cs.z;
+          }
         }
         act* dst = base + (((int64_t)w * nh + head) * a.Lp + pos) * HD;
         store_h_run<Q8>(dst + f0, y1);

@@ -67,6 +67,36 @@ __host__ __device__ inline int pair_logical32(int p) {
   return (p & 3) | (((p >> 4) & 1) << 2) | (((p >> 2) & 3) << 3);
 }
 
+// Rotation pairs of one q or k head with R rotated dims (partial RoPE):
+// pair p < R/2 is (p, p + R/2); the others pair up the unrotated dims as
+// (R + w, R + (hd - R)/2 + w), w = p - R/2, and turn by the identity.  For
+// R = hd these are the pairs (p, p + hd/2) of full RoPE.
+template <int HD>
+__host__ __device__ inline int pair_first(int p, int R) { return p < R / 2 ? p : R + (p - R / 2); }
+template <int HD>
+__host__ __device__ inline int pair_second(int p, int R) {
+  return p < R / 2 ? p + R / 2 : R + (HD - R) / 2 + (p - R / 2);
+}
+
+// Placement of the rows of one q or k head (HD rows) for the rotary
+// epilogue: the output rows 4g + e of fragment j (lane group g) are the
+// values t = 4j + e of that lane, and value t < HD/8 is the first dim of
+// pair g * HD/8 + t while value t + HD/8 is its second, so a lane holds
+// whole rotation pairs, and (R a multiple of HD/4) its first and its second
+// dims are two runs of HD/8 consecutive dims.
+template <int HD>
+__host__ __device__ inline int rope_phys(int u, int R) {
+  constexpr int Q8 = HD / 8;
+  const int h2 = R / 2, rest2 = (HD - R) / 2;
+  int p, second;
+  if (u < h2) { p = u; second = 0; }
+  else if (u < R) { p = u - h2; second = 1; }
+  else if (u < R + rest2) { p = h2 + (u - R); second = 0; }
+  else { p = h2 + (u - R - rest2); second = 1; }
+  const int t = p % Q8 + second * Q8;
+  return 16 * (t >> 2) + 4 * (p / Q8) + (t & 3);
+}
+
 // Eight int8 codes (one 8-byte half of a 16-byte fragment chunk) widened to
 // the binary16 MFMA operand; exact for integers of magnitude <= 128.
 __device__ inline actx8 widen8(uint32_t lo, uint32_t hi) {

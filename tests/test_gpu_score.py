@@ -19,14 +19,14 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(g, name, L, S, n_tokens, seed=1337, model_kw=None, batch_windows=None, streams=None,
-         register_codes=None, fused_tail=None, model_fn=None, **ov):
+         register_codes=None, fused_tail=None, qkv_tile=None, model_fn=None, **ov):
     import torch
     cfg, model = make_case(name, seed=seed, model_kw=model_kw, **ov)
     if model_fn is not None:
         model_fn(model)
     tokens, nbytes = synth.make_stream(cfg, seed=seed, n_tokens=n_tokens)
     print_case("score", name, ov, "L", L, "S", S, "N", n_tokens, model_kw or "", "streams", streams,
-               "register_codes", register_codes, "fused_tail", fused_tail, "seed", seed)
+               "register_codes", register_codes, "fused_tail", fused_tail, "qkv_tile", qkv_tile, "seed", seed)
     gm, _ = gpu_model(g, model)
     if batch_windows:
         gm.set_batch_windows(batch_windows)
@@ -36,6 +36,8 @@ def _run(g, name, L, S, n_tokens, seed=1337, model_kw=None, batch_windows=None, 
         gm.set_register_codes(register_codes)
     if fused_tail is not None:
         gm.set_fused_tail(fused_tail)
+    if qkv_tile is not None:
+        gm.set_qkv_tile(qkv_tile)
     nats, totals = gm.score(torch.from_numpy(tokens).cuda(), torch.from_numpy(nbytes).cuda(), L, S)
     torch.cuda.synchronize()
     return cfg, model, tokens, nbytes, nats.cpu().numpy(), totals.cpu().numpy()
@@ -209,6 +211,26 @@ def test_fused_tail_matches_three_kernels(name, L, S, N, ov, fn):
     compare_nats(three[4], ref, label=f"{name} three GEMM launches")
     compare_nats(fused[4], ref, label=f"{name} fused block tail")
     assert abs(fused[5][3] - ref_bpb) <= BPB_ATOL
+
+
+@pytest.mark.parametrize("name,L,S,N,ov", [
+    ("11l", 256, 64, 1000, {}), ("11l_next", 256, 64, 1000, {}), ("11l_next", 256, 16, 400, {}),
+    ("baseline", 128, 128, 400, {"rope_dims": 16}), ("baseline", 128, 128, 400, {"rope_dims": 48}),
+    ("largevocab", 200, 50, 700, {}), ("11l_int5", 256, 64, 1000, {}), ("10l_int5mlp", 256, 64, 1000, {}),
+    ("11l", 300, 7, 333, {}),            # windows padded to 320 rows: tiles straddle windows, a half tile
+    ("11l", 2048, 64, 2500, {}),         # full-length windows
+])
+def test_qkv_tile_matches_staged_gemm(name, L, S, N, ov):
+    """The one-tile q/k/v kernel (every head of a 128-row tile, codes in
+    per-head fragment order) multiplies the same binary16 operands in the
+    same K order and applies the same epilogue arithmetic as the LDS-staged
+    GEMM: the scores are bit-identical, with partial RoPE, windows that
+    straddle tiles and a half-full last tile."""
+    g = need_gpu()
+    staged = _run(g, name, L, S, N, qkv_tile=False, **ov)
+    tile = _run(g, name, L, S, N, qkv_tile=True, **ov)
+    np.testing.assert_array_equal(tile[4], staged[4])
+    np.testing.assert_array_equal(tile[5], staged[5])
 
 
 @pytest.mark.parametrize("name,L,S,N", [("11l", 256, 64, 1000), ("baseline", 128, 128, 400),
