@@ -60,19 +60,12 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int nqk = a.n_heads + a.n_kv, nall = nqk + a.n_kv;
   const int N = nall * HD;
 
-  // ---- prologue: per-row RMS factors and per-column scales (loads issued
-  // first, so that their LDS stores wait for nothing else), the A tile by
-  // direct loads into LDS, the codes of the wave's first K step
-  float ri = 0.0f;
-  if (tid < TM && m0 + tid < a.M) {
-    // t / 512 + eps rounded twice, as the LDS-staged GEMM (whose K is not a
-    // compile-time constant) computes it: no fused multiply-add
-#pragma clang fp contract(off)
-    const float* sp = a.ss_in + (int64_t)(m0 + tid) * a.nt_in;
-    float t = 0.0f;
-    for (int u = 0; u < a.nt_in; ++u) t += sp[u];
-    ri = 1.0f / sqrtf(t / (float)DM + a.eps);
-  }
+  // ---- prologue: the A tile by direct loads into LDS, the per-column
+  // scales, the codes of the wave's first K step, the per-row partial sums
+  // of squares (one 16-byte load for the four of a d_model 512 row; a loop
+  // of dependent loads here, ahead of the tile, had made two waves' share of
+  // the tile wait four memory round trips); one wait, then the RMS factors
+  // and scales into LDS
   uint4 scv = make_uint4(0, 0, 0, 0);
   if (tid < N / 8) scv = *reinterpret_cast<const uint4*>(a.scale + 8 * tid);
 #pragma unroll
@@ -99,6 +92,25 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     cq3 = *reinterpret_cast<const uint4*>(b + 3072 + l);
   };
   if (w < nall) load4(w, 0);
+  float ri = 0.0f;
+  if (tid < TM && m0 + tid < a.M) {
+    // t / 512 + eps rounded twice, as the LDS-staged GEMM (whose K is not a
+    // compile-time constant) computes it: no fused multiply-add; the
+    // partial sums added in order, as there
+#pragma clang fp contract(off)
+    const float* sp = a.ss_in + (int64_t)(m0 + tid) * a.nt_in;
+    float t = 0.0f;
+    if (a.nt_in == 4) {
+      const float4 v = *reinterpret_cast<const float4*>(sp);
+      t = t + v.x;
+      t = t + v.y;
+      t = t + v.z;
+      t = t + v.w;
+    } else {
+      for (int u = 0; u < a.nt_in; ++u) t += sp[u];
+    }
+    ri = 1.0f / sqrtf(t / (float)DM + a.eps);
+  }
   if (tid < TM) rinv_s[tid] = ri;
   if (tid < N / 8) {
     const uint32_t sw[4] = {scv.x, scv.y, scv.z, scv.w};

@@ -311,12 +311,30 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // parallel lanes: the MLP reads the layer input (binary16 copy and sums
       // of squares written by the kernel that produced it)
       load_tile(a.xb_in);
+      // the row's partial sums: one 16-byte load per row when there are
+      // four (all rows' loads in flight at once), added in order
+      if (a.nt_in == 4) {
+        float4 pv[FB];
 #pragma unroll
-      for (int ii = 0; ii < FB; ++ii) {
-        const float* sp = a.ss_in + (int64_t)grow(arow(FB * wm + ii)) * a.nt_in;
-        float t = 0.0f;
-        for (int u = 0; u < a.nt_in; ++u) t += sp[u];
-        rinv[ii] = 1.0f / sqrtf(t / (float)DM + a.eps);
+        for (int ii = 0; ii < FB; ++ii)
+          pv[ii] = *reinterpret_cast<const float4*>(a.ss_in + (int64_t)grow(arow(FB * wm + ii)) * 4);
+#pragma unroll
+        for (int ii = 0; ii < FB; ++ii) {
+          float t = 0.0f;
+          t += pv[ii].x;
+          t += pv[ii].y;
+          t += pv[ii].z;
+          t += pv[ii].w;
+          rinv[ii] = 1.0f / sqrtf(t / (float)DM + a.eps);
+        }
+      } else {
+#pragma unroll
+        for (int ii = 0; ii < FB; ++ii) {
+          const float* sp = a.ss_in + (int64_t)grow(arow(FB * wm + ii)) * a.nt_in;
+          float t = 0.0f;
+          for (int u = 0; u < a.nt_in; ++u) t += sp[u];
+          rinv[ii] = 1.0f / sqrtf(t / (float)DM + a.eps);
+        }
       }
     }
     // the accumulators now carry x1 / s_proj
