@@ -360,9 +360,14 @@ int i6g_plan_windows(int64_t n_tokens, int32_t window, int32_t stride, int64_t* 
  *                          after padding to 64), the q/k/v projection runs as
  *                          one kernel per 128-row tile computing every head
  *                          of it, with the codes rearranged into per-head
- *                          fragment order when the model is loaded; 0: the
- *                          LDS-staged GEMM.  The same products accumulated
- *                          in the same order: results are identical.
+ *                          fragment order when the model is loaded; with
+ *                          the fused block tail on, each tail but the last
+ *                          (and one whose rows are pruned) runs the same
+ *                          per-head loop on its own output rows for the
+ *                          next layer, so only the first layer's q/k/v has a
+ *                          launch of its own; 0: the LDS-staged GEMM.  The
+ *                          same products accumulated in the same order:
+ *                          results are identical.
  * Errors: I6G_EINVAL for an unknown option or a value out of range. */
 enum {
   I6G_OPT_BATCH_WINDOWS = 0, I6G_OPT_PRUNE_LAST = 1, I6G_OPT_STREAMS = 2, I6G_OPT_REGISTER_CODES = 3,

@@ -289,8 +289,9 @@ class Model:
 
     def set_qkv_tile(self, on):
         """True (default): the q/k/v projection as one kernel per 128-row
-        tile (d_model 512, head size 64, no LoRA); False: the LDS-staged
-        GEMM."""
+        tile (d_model 512, head size 64, no LoRA), and with the fused block
+        tail on, computed for the next layer inside each tail; False: the
+        LDS-staged GEMM."""
         _check(lib().i6g_set_option(self._h, 5, int(bool(on))))
 
     def score(self, tokens, nbytes, window, stride, nats=None, totals=None, check=True):

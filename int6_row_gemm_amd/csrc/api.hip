@@ -940,6 +940,8 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
     if ((rc = timed(m, I6G_K_EMBED, s, 0.0, real_rows * d * 6.0, [&] { return launch_embed(ea, s); })))
       return rc;
 
+    // set when the previous block tail computed this layer's q, k and v
+    bool qkv_done = false;
     for (int e = 0; e < m->n_eff; ++e) {
       const BlockDev& B = m->blocks[m->schedule[e]];
       const bool last = (e + 1 == m->n_eff);
@@ -967,9 +969,11 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
       const double fl_qkv = 2.0 * real_rows * m->nqkv * d;
       const bool one_tile = qkv_tile && B.qkv_frag.p;
       if (one_tile) g.Bp = B.qkv_frag.as<int8_t>();
-      if ((rc = timed(m, I6G_K_QKV, s, fl_qkv, real_rows * (2.0 * d + 2.0 * m->nqkv) + (double)m->nqkv * d,
+      if (!qkv_done &&
+          (rc = timed(m, I6G_K_QKV, s, fl_qkv, real_rows * (2.0 * d + 2.0 * m->nqkv) + (double)m->nqkv * d,
                       [&] { return one_tile ? launch_qkv_tile(g, s) : launch_gemm(EPI_QKV, g, s); })))
         return rc;
+      qkv_done = false;
 
       const bool pr = last && prune;
       AttnArgs at{};
@@ -1048,11 +1052,28 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
           ta.p0 = p0; ta.k0 = k0; ta.n_win = K; ta.e0 = e0;
           ta.L = (int32_t)L; ta.S = (int32_t)S; ta.Lp = Lp;
         }
+        // the next layer's q, k and v from this tail's output rows (its
+        // binary16 copy and sums of squares then stay on the chip unless
+        // the parallel lanes read them)
+        const BlockDev* Bn = last ? nullptr : &m->blocks[m->schedule[e + 1]];
+        const bool fuse = qkv_tile && !pr && Bn && Bn->qkv_frag.p;
+        if (fuse) {
+          ta.qkv.frag = Bn->qkv_frag.as<int8_t>(); ta.qkv.scale = Bn->qkv_scales.as<uint16_t>();
+          ta.qkv.q = sc.q.as<act>(); ta.qkv.k = sc.k.as<act>(); ta.qkv.vt = sc.vt.as<act>();
+          ta.qkv.rope = m->rope.as<float2>();
+          ta.qkv.n_heads = m->Hq; ta.qkv.n_kv = m->Hkv; ta.qkv.rope_dims = m->rope_dims;
+          ta.Lp = Lp;
+          if (!m->parallel) { ta.xb = nullptr; ta.ss_out = nullptr; }
+        }
         double per_row = 2.0 * d + 8.0 * d + (ta.xb ? 2.0 * d : 0.0) + (ta.push_dst ? 4.0 * d : 0.0) +
-                         (ta.pop_src && ta.pop_src != ta.push_dst ? 4.0 * d : 0.0) + (m->parallel ? 2.0 * d : 0.0);
-        const double by_t = rows_mlp * per_row + (double)d * d + 2.0 * (double)F * d;
-        if ((rc = timed(m, I6G_K_TAIL, s, fl_o + 2.0 * fl_fc, by_t, [&] { return launch_tail(ta, s); })))
+                         (ta.pop_src && ta.pop_src != ta.push_dst ? 4.0 * d : 0.0) + (m->parallel ? 2.0 * d : 0.0) +
+                         (fuse ? 2.0 * m->nqkv : 0.0);
+        const double by_t =
+            rows_mlp * per_row + (double)d * d + 2.0 * (double)F * d + (fuse ? (double)m->nqkv * d : 0.0);
+        const double fl_t = fl_o + 2.0 * fl_fc + (fuse ? 2.0 * real_rows * m->nqkv * d : 0.0);
+        if ((rc = timed(m, I6G_K_TAIL, s, fl_t, by_t, [&] { return launch_tail(ta, s); })))
           return rc;
+        qkv_done = fuse;
         continue;
       }
       // algorithmic HBM bytes: A read, fp32 residual read + write, bf16 copy,

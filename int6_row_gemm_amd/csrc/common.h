@@ -177,6 +177,19 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
 // normed GEMM.  One 128-row tile per workgroup; the hidden activations stay
 // on chip.  Codes come in the fragment order of launch_shuffle_codes (o and
 // proj rows with a zero scale as zero codes).
+// The q/k/v projection's codes and outputs, for the one-tile q/k/v kernel
+// and for a block tail that computes the next layer's q, k and v from its
+// own output rows (frag null: no such phase).
+struct QkvOut {
+  const int8_t* frag;       // codes in per-head fragment order (launch_shuffle_qkv_codes)
+  const uint16_t* scale;    // [(Hq + 2 Hkv) * 64] binary16
+  act* q;                   // [W, Hq, Lp, 64]
+  act* k;                   // [W, Hkv, Lp, 64]
+  act* vt;                  // [W, Hkv, 64, Lp]
+  const float2* rope;       // [Lp, 32] (cos, sin) of rotation pair p
+  int32_t n_heads, n_kv, rope_dims;
+};
+
 struct TailArgs {
   const act* o;             // [rows, 512] attention output
   const int8_t* o_frag;     // Wo [512, 512]
@@ -204,6 +217,9 @@ struct TailArgs {
   int64_t p0, k0, n_win, e0;
   int32_t L, S, Lp;
   int32_t* flags;           // kFlagRange
+  // the next layer's q/k/v projection from this tail's output rows (qkv.frag
+  // null: none); needs row_map 0, M and Lp multiples of 64, Lp >= 128
+  QkvOut qkv;
 };
 hipError_t launch_tail(const TailArgs& a, hipStream_t s);
 

@@ -27,7 +27,13 @@
 //             rinv)^2 (8 waves of 64 rows x 32 columns) -> LDS (32 KB,
 //             binary16); acc += h . code_proj^T over those 128 columns;
 //   epilogue  x2 = acc * s_proj, skip push / pop, x2, binary16(x2) and the
-//             per-128-column sums of squares to global memory.
+//             per-128-column sums of squares to global memory;
+//   q/k/v     (when the next layer's q/k/v projection is fused in)
+//             binary16(x2) into the A buffer instead of global memory, the
+//             rows' RMS factors from the sums of squares, then the per-head
+//             loop of the one-tile q/k/v kernel (qkv_phase.h) on the tile:
+//             the next layer's q, k and v without x2's binary16 copy going
+//             through HBM.
 //
 // Folding the residual into the accumulators as x / s (a zero scale counted
 // as 1, its row's codes zeroed when the fragment-order copy is made) keeps
@@ -42,6 +48,7 @@
 // chunks) touches 32 distinct 16-byte bank groups.
 #include "common.h"
 #include "mfma_util.h"
+#include "qkv_phase.h"
 
 namespace i6g {
 namespace {
@@ -464,10 +471,18 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
     __syncthreads();   // the last chunk's down projection has read Hs (partial sums go there)
+    // the fused q/k/v phase's first codes, loaded before this epilogue's
+    // stores (a load issued after a store waits for it on the single
+    // vector-memory counter)
+    const bool qkv = a.qkv.frag != nullptr;
+    if (qkv && w < a.qkv.n_heads + 2 * a.qkv.n_kv) qkvp::load4(a.qkv.frag, w, 0, cq0, cq1, cq2, cq3);
     // the row addresses are recomputed here rather than kept from the
     // prologue: an opaque copy of the tile base stops the compiler from
     // holding them in registers through the MLP (it would spill them)
-    asm volatile("" : "+s"(m0v), "+v"(lrow_v));
+    // (the lane indices too: the q/k/v phase's LDS addresses depend on
+    // nothing else and would be computed before the MLP and held)
+    int lr_e = lr, lg_e = lg;
+    asm volatile("" : "+s"(m0v), "+v"(lrow_v), "+v"(lr_e), "+v"(lg_e));
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const bool ok = m0v + arow(i) < a.M;
@@ -503,28 +518,61 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
           for (int e = 0; e < 4; ++e) t += xv[jj][e] * xv[jj][e];
+        const uint4 xbv = make_uint4(pack2h(xv[0][0], xv[0][1]), pack2h(xv[0][2], xv[0][3]),
+                                     pack2h(xv[1][0], xv[1][1]), pack2h(xv[1][2], xv[1][3]));
+        // the q/k/v phase's A tile: the same binary16 values, in the layout
+        // of the MLP input (chunks 8w + 4h + lg of physical row 16i + lr)
+        if (qkv) *reinterpret_cast<uint4*>(As + a_off(16 * i + lr_e, 8 * w + 4 * h + lg_e)) = xbv;
         if (ok) {
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj)
             *reinterpret_cast<float4*>(a.x + off + colj(2 * h + jj)) = make_float4(xv[jj][0], xv[jj][1], xv[jj][2], xv[jj][3]);
-          if (a.xb)
-            *reinterpret_cast<uint4*>(a.xb + off + colj(2 * h)) =
-                make_uint4(pack2h(xv[0][0], xv[0][1]), pack2h(xv[0][2], xv[0][3]), pack2h(xv[1][0], xv[1][1]),
-                           pack2h(xv[1][2], xv[1][3]));
+          if (a.xb) *reinterpret_cast<uint4*>(a.xb + off + colj(2 * h)) = xbv;
         }
       }
       t += __shfl_xor(t, 16);
       t += __shfl_xor(t, 32);
       if (lg == 0) ss_part[w * TM + arow(i)] = t;
-      out_of_range |= a.xb && ok && t >= kRangeSq;
+      out_of_range |= (a.xb || qkv) && ok && t >= kRangeSq;
     }
     if (__any(out_of_range) && lane == 0) atomicOr(a.flags, kFlagRange);
+    if (a.ss_out || qkv) __syncthreads();   // partial sums (and the binary16 rows) complete
     if (a.ss_out) {
-      __syncthreads();
       // TM rows x 4 column tiles of 128: threads 0 .. 4 TM - 1
       const int r = tid & (TM - 1), tn = tid / TM;
       if (tn < DM / 128 && m0v + r < a.M)
         a.ss_out[(int64_t)grow(r) * (DM / 128) + tn] = ss_part[(2 * tn) * TM + r] + ss_part[(2 * tn + 1) * TM + r];
+    }
+    if (qkv) {
+      // the rows' RMS factors as the q/k/v kernel computes them from the
+      // four per-128-column sums this kernel would otherwise write (added in
+      // order, t / 512 + eps without a fused multiply-add), and the
+      // projection's scales as floats, both after the partial sums in Hs
+      float* const rinv_s = reinterpret_cast<float*>(Hs + 4 * 8 * TM);
+      float* const sc_s = rinv_s + TM;
+      const int nall = a.qkv.n_heads + 2 * a.qkv.n_kv;
+      if (tid < TM) {
+        float ri = 0.0f;
+        if (m0v + tid < a.M) {
+#pragma clang fp contract(off)
+          float t = 0.0f;
+#pragma unroll
+          for (int tn = 0; tn < DM / 128; ++tn) t = t + (ss_part[(2 * tn) * TM + tid] + ss_part[(2 * tn + 1) * TM + tid]);
+          ri = 1.0f / sqrtf(t / (float)DM + a.eps);
+        }
+        rinv_s[tid] = ri;
+      }
+      if (tid < nall * 8) {
+        const uint4 v = *reinterpret_cast<const uint4*>(a.qkv.scale + 8 * tid);
+        const uint32_t sw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sc_s[8 * tid + 2 * e] = h2f((uint16_t)(sw[e] & 0xffff));
+          sc_s[8 * tid + 2 * e + 1] = h2f((uint16_t)(sw[e] >> 16));
+        }
+      }
+      __syncthreads();
+      qkvp::heads(a.qkv, a.M, a.Lp, As, rinv_s, sc_s, m0v, w, cq0, cq1, cq2, cq3);
     }
   }
 }
@@ -536,6 +584,10 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 hipError_t launch_tail(const TailArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   if (a.F <= 0 || a.F % HC != 0 || !a.flags || (a.parallel && (!a.ss_in || !a.xb_in || a.nt_in < 1)))
+    return hipErrorInvalidValue;
+  if (a.qkv.frag &&
+      (a.row_map || a.M % 64 != 0 || a.Lp < TM || a.Lp % 64 != 0 || !a.qkv.scale || !a.qkv.q || !a.qkv.k ||
+       !a.qkv.vt || !a.qkv.rope || !qkv_tile_supported(DM, qkvp::HD, a.qkv.n_heads, a.qkv.n_kv, a.qkv.rope_dims, 0)))
     return hipErrorInvalidValue;
   const int tiles = (a.M + TM - 1) / TM;
   if (a.parallel) hipLaunchKernelGGL(tail_kernel<true>, dim3(tiles), dim3(NTH), 0, s, a);

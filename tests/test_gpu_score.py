@@ -224,8 +224,10 @@ def test_qkv_tile_matches_staged_gemm(name, L, S, N, ov):
     """The one-tile q/k/v kernel (every head of a 128-row tile, codes in
     per-head fragment order) multiplies the same binary16 operands in the
     same K order and applies the same epilogue arithmetic as the LDS-staged
-    GEMM: the scores are bit-identical, with partial RoPE, windows that
-    straddle tiles and a half-full last tile."""
+    GEMM, and so does the same per-head loop run inside the block tail on
+    the tail's own output rows for the next layer: the scores are
+    bit-identical, with partial RoPE, windows that straddle tiles and a
+    half-full last tile."""
     g = need_gpu()
     staged = _run(g, name, L, S, N, qkv_tile=False, **ov)
     tile = _run(g, name, L, S, N, qkv_tile=True, **ov)
