@@ -369,15 +369,30 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-KERNEL_SOURCES = {"attn": "attention.hip", "qkv": "gemm.hip", "oproj": "gemm.hip", "fc": "gemm.hip",
-                  "proj": "gemm.hip", "tail": "tail.hip", "head": "aux.hip", "embed": "aux.hip",
-                  "reduce": "aux.hip"}
+# the sources each kernel class is compiled from (its file and the headers
+# holding its device code); their hash ties a counter summary to the code
+_HDRS = ("common.h", "mfma_util.h")
+KERNEL_SOURCES = {"attn": ("attention.hip",) + _HDRS, "qkv": ("qkv.hip", "qkv_phase.h", "gemm.hip") + _HDRS,
+                  "oproj": ("gemm.hip",) + _HDRS, "fc": ("gemm.hip",) + _HDRS, "proj": ("gemm.hip",) + _HDRS,
+                  "tail": ("tail.hip", "qkv_phase.h") + _HDRS, "head": ("aux.hip",) + _HDRS,
+                  "embed": ("aux.hip",) + _HDRS, "reduce": ("aux.hip",) + _HDRS}
+
+
+def sources_sha256(kernel):
+    """sha256 over the concatenated sources of a kernel class, or None."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, ()):
+        p = os.path.join(ROOT, "int6_row_gemm_amd", "csrc", f)
+        if not os.path.exists(p):
+            return None
+        h.update(open(p, "rb").read())
+    return h.hexdigest() if kernel in KERNEL_SOURCES else None
 
 
 def counter_traffic(path, kernel):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
     None when there is none or the kernel source changed since it was taken."""
-    import hashlib
     if not path or not os.path.exists(path):
         return None
     kv = {}
@@ -385,10 +400,7 @@ def counter_traffic(path, kernel):
         if ":" in line and not line.startswith(("#", "|", "`")):
             k, v = line.split(":", 1)
             kv[k.strip().lstrip("- ")] = v.strip().strip("`")
-    src = os.path.join(ROOT, "int6_row_gemm_amd", "csrc", KERNEL_SOURCES.get(kernel, ""))
-    if kv.get("kernel") != kernel or not os.path.exists(src):
-        return None
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("source_sha256"):
+    if kv.get("kernel") != kernel or sources_sha256(kernel) != kv.get("source_sha256"):
         return None
     try:
         return float(kv["bytes_per_launch"])
