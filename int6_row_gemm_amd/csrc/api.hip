@@ -176,13 +176,12 @@ struct i6g_model {
   // tables and scratch
   DevBuf rope;
   int rope_L = 0;
-  // per-batch scratch: two sets, so that consecutive batches of windows can
-  // run on two streams at once (batches are independent)
+  // per-batch scratch: a second set is allocated only when consecutive
+  // batches of windows run on two streams at once (batches are independent)
   struct Scratch {
     DevBuf x, xb, ss, q, k, vt, o, h, slots, lora_u;
   } sc[2];
   DevBuf flags, part_n, part_b;
-  int64_t scratch_rows = 0;
   int streams = 1;                 // 1: every batch on the caller's stream
   hipStream_t aux = nullptr;       // the second stream (default priority)
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
@@ -289,23 +288,25 @@ int build_plan(i6g_model* m) {
   return I6G_OK;
 }
 
-int ensure_scratch(i6g_model* m, int W, int Lp, hipStream_t s) {
+// Scratch for batches of W windows of Lp rows: the second set only when
+// batches alternate over two streams, and the hidden activations only when
+// the MLP runs as two GEMMs (the fused block tail keeps them on the chip).
+// Buffers only grow; hipFree of a smaller one waits for the device first.
+int ensure_scratch(i6g_model* m, int W, int Lp, hipStream_t s, int n_sets, bool need_h) {
   const int64_t M = (int64_t)W * Lp;
-  if (M > m->scratch_rows) {
-    const int nt = m->d / 128;
-    for (auto& c : m->sc) {
-      HIP_TRY(c.x.ensure(M * m->d * 4));
-      HIP_TRY(c.xb.ensure(M * m->d * 2));
-      HIP_TRY(c.ss.ensure(M * nt * 4));
-      HIP_TRY(c.q.ensure(M * m->d * 2));
-      HIP_TRY(c.k.ensure(M * m->kvd * 2));
-      HIP_TRY(c.vt.ensure(M * m->kvd * 2));
-      HIP_TRY(c.o.ensure(M * m->d * 2));
-      HIP_TRY(c.h.ensure(M * m->F * 2));
-      if (m->max_depth > 0) HIP_TRY(c.slots.ensure((size_t)m->max_depth * M * m->d * 4));
-      if (m->lora_r > 0) HIP_TRY(c.lora_u.ensure(M * 2 * m->lora_r * 4));
-    }
-    m->scratch_rows = M;
+  const int nt = m->d / 128;
+  for (int i = 0; i < n_sets; ++i) {
+    auto& c = m->sc[i];
+    HIP_TRY(c.x.ensure(M * m->d * 4));
+    HIP_TRY(c.xb.ensure(M * m->d * 2));
+    HIP_TRY(c.ss.ensure(M * nt * 4));
+    HIP_TRY(c.q.ensure(M * m->d * 2));
+    HIP_TRY(c.k.ensure(M * m->kvd * 2));
+    HIP_TRY(c.vt.ensure(M * m->kvd * 2));
+    HIP_TRY(c.o.ensure(M * m->d * 2));
+    if (need_h) HIP_TRY(c.h.ensure(M * m->F * 2));
+    if (m->max_depth > 0) HIP_TRY(c.slots.ensure((size_t)m->max_depth * M * m->d * 4));
+    if (m->lora_r > 0) HIP_TRY(c.lora_u.ensure(M * 2 * m->lora_r * 4));
   }
   if (!m->aux) {
     HIP_TRY(hipStreamCreateWithFlags(&m->aux, hipStreamNonBlocking));
@@ -886,7 +887,8 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
   const bool qkv_tile = m->qkv_tile && Lp >= 128;
   int Wb = m->batch_windows > 0 ? m->batch_windows : std::max(1, (tail ? 131072 : 49152) / Lp);
   Wb = (int)std::min<int64_t>({(int64_t)Wb, K, max_rows / Lp});
-  int rc = ensure_scratch(m, Wb, Lp, s);
+  const bool two = m->streams == 2 && K > Wb;
+  int rc = ensure_scratch(m, Wb, Lp, s, two ? 2 : 1, !tail);
   if (rc) return rc;
 
   const int d = m->d, F = m->F, kvd = m->kvd, nt = d / 128;
@@ -900,7 +902,6 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
   // starts after the caller's prior work and the caller's stream waits for
   // it before the final reduction.
   const hipStream_t s_caller = s;
-  const bool two = m->streams == 2 && K > Wb;
   if (two) {
     HIP_TRY(hipEventRecord(m->ev_fork, s_caller));
     HIP_TRY(hipStreamWaitEvent(m->aux, m->ev_fork, 0));
