@@ -147,6 +147,39 @@ def test_two_streams_give_identical_results(name, L, S, N, bw):
     np.testing.assert_array_equal(one[5], two[5])
 
 
+def test_scratch_grows_with_the_options_of_one_model():
+    """Scratch is allocated for what a call needs: one set and no hidden
+    activations for the fused block tail; switching the same model to the
+    three-GEMM MLP, then to two streams, allocates the hidden buffer and the
+    second set on the calls that need them.  Each call's result is the
+    same as a fresh model's with those options."""
+    import torch
+    g = need_gpu()
+    name, L, S, N, bw = "11l", 256, 64, 1400, 4
+    cfg, model = make_case(name, seed=7)
+    tokens, nbytes = synth.make_stream(cfg, seed=7, n_tokens=N)
+    t, b = torch.from_numpy(tokens).cuda(), torch.from_numpy(nbytes).cuda()
+    gm, _ = gpu_model(g, model)
+    gm.set_batch_windows(bw)
+    runs = []
+    for fused, streams in ((True, 1), (False, 1), (False, 2), (True, 2)):
+        print_case("scratch", name, "fused_tail", fused, "streams", streams)
+        gm.set_fused_tail(fused)
+        gm.set_streams(streams)
+        nats, totals = gm.score(t, b, L, S)
+        torch.cuda.synchronize()
+        runs.append((nats.cpu().numpy(), totals.cpu().numpy()))
+    for (fused, streams), (nats, totals) in zip(((True, 1), (False, 1), (False, 2), (True, 2)), runs):
+        fresh = _run(g, name, L, S, N, seed=7, batch_windows=bw, streams=streams, fused_tail=fused)
+        np.testing.assert_array_equal(nats, fresh[4])
+        np.testing.assert_array_equal(totals, fresh[5])
+    np.testing.assert_allclose(runs[1][0], runs[0][0], rtol=1e-3, atol=0)
+    ref, ref_bpb = _full_oracle(model, tokens, nbytes, L, S)
+    compare_nats(runs[0][0], ref, label="fused tail, one scratch set")
+    compare_nats(runs[2][0], ref, label="three GEMMs, two scratch sets")
+    assert abs(runs[2][1][3] - ref_bpb) <= BPB_ATOL
+
+
 @pytest.mark.parametrize("name,L,S,N,ov,kw", [
     ("11l", 256, 64, 1000, {}, None), ("midcycle", 128, 128, 257, {}, None),
     ("largevocab", 200, 50, 700, {}, None), ("tiny", 256, 64, 700, {}, None),
