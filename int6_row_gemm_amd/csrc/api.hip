@@ -1072,6 +1072,12 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
         const double by_t =
             rows_mlp * per_row + (double)d * d + 2.0 * (double)F * d + (fuse ? (double)m->nqkv * d : 0.0);
         const double fl_t = fl_o + 2.0 * fl_fc + (fuse ? 2.0 * real_rows * m->nqkv * d : 0.0);
+        // residual rows spread over the output projection's K steps where a
+        // row's place in its tile does not depend on the batching: not in
+        // the final layer (whether its rows are pruned, and so remapped,
+        // depends on the batch), and only for windows padded to a multiple
+        // of the 128-row tile
+        ta.spread_residual = !last && Lp % 128 == 0;
         if ((rc = timed(m, I6G_K_TAIL, s, fl_t, by_t, [&] { return launch_tail(ta, s); })))
           return rc;
         qkv_done = fuse;

@@ -220,6 +220,10 @@ struct TailArgs {
   // the next layer's q/k/v projection from this tail's output rows (qkv.frag
   // null: none); needs row_map 0, M and Lp multiples of 64, Lp >= 128
   QkvOut qkv;
+  // 1: the residual rows enter the accumulators one row block per output-
+  // projection K step (row_map must be 0; results then depend on a row's
+  // place in its 128-row tile)
+  int32_t spread_residual;
 };
 hipError_t launch_tail(const TailArgs& a, hipStream_t s);
 

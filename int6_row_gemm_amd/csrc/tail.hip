@@ -93,8 +93,16 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 
 // PAR: parallel residual lanes (the MLP reads the layer input); otherwise
 // the MLP reads x + attention, normalised before it enters LDS.
+// SPREAD: the residual rows enter the accumulators one 16-row block per
+// output-projection K step (block i before step i, loaded a step ahead)
+// instead of all in the prologue, so their loads overlap the MFMAs.  A
+// row's rounding order then depends on its row block in the tile, which
+// is the same for every batching when windows are padded to a multiple of
+// 128 rows and the rows are not remapped; the host asks for SPREAD only
+// then, and never in the final layer (whose rows are remapped when the
+// batch is pruned, which depends on the batching).
 // 160 KB of LDS: one workgroup (two waves per SIMD) per CU.
-template <bool PAR>
+template <bool PAR, bool SPREAD>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) void tail_kernel(TailArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[ABYTES + HBYTES];
   char* const As = smem;
@@ -211,7 +219,37 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   else if (tid < 128)
     *reinterpret_cast<uint4*>(sc_lds + DM + 8 * (tid - 64)) =
         *reinterpret_cast<const uint4*>(a.proj_scale + 8 * (tid - 64));
-  {
+  // SPREAD: the 1 / s_o factors as fp32 in the hidden buffer (after the
+  // partial sums and the staged scales), read where a row block is added
+  float* const rs_lds = reinterpret_cast<float*>(Hs + 8192);
+  float4 xres[4];
+  auto load_res = [&](int i) {
+    const float* xr = a.x + (int64_t)grow(arow(i)) * DM;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xres[j] = *reinterpret_cast<const float4*>(xr + colj(j));
+  };
+  auto add_res = [&](int i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 r4 = *reinterpret_cast<const float4*>(rs_lds + colj(j));
+      acc[i][j] += f32x4{xres[j].x * r4.x, xres[j].y * r4.y, xres[j].z * r4.z, xres[j].w * r4.w};
+    }
+  };
+  if constexpr (SPREAD) {
+    if (tid < DM / 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(a.o_scale + 4 * tid);
+      *reinterpret_cast<float4*>(rs_lds + 4 * tid) =
+          make_float4(__builtin_amdgcn_rcpf(scale_or_one(h2f((uint16_t)(v.x & 0xffff)))),
+                      __builtin_amdgcn_rcpf(scale_or_one(h2f((uint16_t)(v.x >> 16)))),
+                      __builtin_amdgcn_rcpf(scale_or_one(h2f((uint16_t)(v.y & 0xffff)))),
+                      __builtin_amdgcn_rcpf(scale_or_one(h2f((uint16_t)(v.y >> 16)))));
+    }
+    load_res(0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
     float rs[2][8];
     load_scales8(a.o_scale + 64 * w + 8 * lg, rs[0]);
     load_scales8(a.o_scale + 64 * w + 32 + 8 * lg, rs[1]);
@@ -261,8 +299,20 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int j = 0; j < 4; ++j) acc[i][j] = MFMA(wf[j], af, acc[i][j]);
     }
   };
+  if constexpr (SPREAD) {
+    // step kt: block kt's residual rows (loaded during step kt - 1) are
+    // added, block kt + 1's are loaded, then the step's MFMAs
+#pragma unroll
+    for (int kt = 0; kt < 7; ++kt) {
+      add_res(kt);
+      load_res(kt + 1);
+      wide_step(As, DM * 2, 8 * kt, [&] { load_o(kt + 1); });
+    }
+    add_res(7);
+  } else {
 #pragma unroll 1
-  for (int kt = 0; kt < 7; ++kt) wide_step(As, DM * 2, 8 * kt, [&] { load_o(kt + 1); });
+    for (int kt = 0; kt < 7; ++kt) wide_step(As, DM * 2, 8 * kt, [&] { load_o(kt + 1); });
+  }
   wide_step(As, DM * 2, 56, [&] {
     load_f(0, 0, 0);
     load_f(0, 1, 1);
@@ -590,8 +640,14 @@ hipError_t launch_tail(const TailArgs& a, hipStream_t s) {
        !a.qkv.vt || !a.qkv.rope || !qkv_tile_supported(DM, qkvp::HD, a.qkv.n_heads, a.qkv.n_kv, a.qkv.rope_dims, 0)))
     return hipErrorInvalidValue;
   const int tiles = (a.M + TM - 1) / TM;
-  if (a.parallel) hipLaunchKernelGGL(tail_kernel<true>, dim3(tiles), dim3(NTH), 0, s, a);
-  else hipLaunchKernelGGL(tail_kernel<false>, dim3(tiles), dim3(NTH), 0, s, a);
+  if (a.spread_residual && a.row_map) return hipErrorInvalidValue;
+  if (a.parallel) {
+    if (a.spread_residual) hipLaunchKernelGGL((tail_kernel<true, true>), dim3(tiles), dim3(NTH), 0, s, a);
+    else hipLaunchKernelGGL((tail_kernel<true, false>), dim3(tiles), dim3(NTH), 0, s, a);
+  } else {
+    if (a.spread_residual) hipLaunchKernelGGL((tail_kernel<false, true>), dim3(tiles), dim3(NTH), 0, s, a);
+    else hipLaunchKernelGGL((tail_kernel<false, false>), dim3(tiles), dim3(NTH), 0, s, a);
+  }
   return hipGetLastError();
 }
 
