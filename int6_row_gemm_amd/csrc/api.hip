@@ -943,12 +943,15 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
 
     // set when the previous block tail computed this layer's q, k and v
     bool qkv_done = false;
+    // where the residual stream is: x, or the skip slot the previous block
+    // tail pushed it into without also writing x
+    const float* resid = sc.x.as<float>();
     for (int e = 0; e < m->n_eff; ++e) {
       const BlockDev& B = m->blocks[m->schedule[e]];
       const bool last = (e + 1 == m->n_eff);
       if (m->lora_r > 0) {
         LoraArgs la{};
-        la.x = sc.x.as<float>(); la.M = M; la.d = d; la.r = m->lora_r; la.eps = eps;
+        la.x = resid; la.M = M; la.d = d; la.r = m->lora_r; la.eps = eps;
         la.aq = m->lora_aq.as<float>() + (size_t)e * m->lora_r * d;
         la.av = m->lora_av.as<float>() + (size_t)e * m->lora_r * d;
         la.u = sc.lora_u.as<float>();
@@ -1039,6 +1042,7 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
         ta.fc_frag = B.fc_frag.as<int8_t>(); ta.fc_scale = B.fc_scales.as<uint16_t>();
         ta.proj_frag = B.proj_frag.as<int8_t>(); ta.proj_scale = B.proj_scales.as<uint16_t>();
         ta.M = pr ? R : M; ta.F = F; ta.eps = eps; ta.leaky = m->leaky;
+        ta.x_in = resid;
         ta.x = sc.x.as<float>();
         if (!last) { ta.xb = sc.xb.as<act>(); ta.ss_out = sc.ss.as<float>(); }
         if (m->push_after[e]) ta.push_dst = sc.slots.as<float>() + (size_t)m->push_slot[e] * M * d;
@@ -1066,7 +1070,12 @@ int i6g_score_tokens(i6g_model* m, const int32_t* tokens_dev, const int32_t* byt
           ta.Lp = Lp;
           if (!m->parallel) { ta.xb = nullptr; ta.ss_out = nullptr; }
         }
-        double per_row = 2.0 * d + 8.0 * d + (ta.xb ? 2.0 * d : 0.0) + (ta.push_dst ? 4.0 * d : 0.0) +
+        // a tail that pushes its result and pops nothing stores it only into
+        // the skip slot, and the next tail reads its residual from there
+        // (the final layer's result goes to x for the head)
+        if (!last && ta.push_dst && !ta.pop_src) ta.x = nullptr;
+        resid = ta.x ? sc.x.as<float>() : ta.push_dst;
+        double per_row = 2.0 * d + (ta.x ? 8.0 * d : 4.0 * d) + (ta.xb ? 2.0 * d : 0.0) + (ta.push_dst ? 4.0 * d : 0.0) +
                          (ta.pop_src && ta.pop_src != ta.push_dst ? 4.0 * d : 0.0) + (m->parallel ? 2.0 * d : 0.0) +
                          (fuse ? 2.0 * m->nqkv : 0.0);
         const double by_t =

@@ -200,7 +200,8 @@ struct TailArgs {
   const uint16_t* proj_scale;
   int32_t M, F;
   float eps, leaky;
-  float* x;                 // [rows, 512] residual, updated in place
+  const float* x_in;        // [rows, 512] residual read (may equal x)
+  float* x;                 // [rows, 512] result (null: stored only to push_dst)
   act* xb;                  // [rows, 512] binary16 copy of the result (or null)
   float* ss_out;            // [rows, 4] per-128-column sums of squares of the result (or null)
   float* push_dst;          // skip slot to store the result into (or null)

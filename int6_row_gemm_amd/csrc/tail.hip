@@ -224,7 +224,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float* const rs_lds = reinterpret_cast<float*>(Hs + 8192);
   float4 xres[4];
   auto load_res = [&](int i) {
-    const float* xr = a.x + (int64_t)grow(arow(i)) * DM;
+    const float* xr = a.x_in + (int64_t)grow(arow(i)) * DM;
 #pragma unroll
     for (int j = 0; j < 4; ++j) xres[j] = *reinterpret_cast<const float4*>(xr + colj(j));
   };
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int e = 0; e < 8; ++e) rs[h][e] = __builtin_amdgcn_rcpf(scale_or_one(rs[h][e]));
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const float* xr = a.x + (int64_t)grow(arow(i)) * DM;
+      const float* xr = a.x_in + (int64_t)grow(arow(i)) * DM;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float4 v = *reinterpret_cast<const float4*>(xr + colj(j));
@@ -573,10 +573,12 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // the q/k/v phase's A tile: the same binary16 values, in the layout
         // of the MLP input (chunks 8w + 4h + lg of physical row 16i + lr)
         if (qkv) *reinterpret_cast<uint4*>(As + a_off(16 * i + lr_e, 8 * w + 4 * h + lg_e)) = xbv;
-        if (ok) {
+        if (ok && a.x) {
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj)
             *reinterpret_cast<float4*>(a.x + off + colj(2 * h + jj)) = make_float4(xv[jj][0], xv[jj][1], xv[jj][2], xv[jj][3]);
+        }
+        if (ok) {
           if (a.xb) *reinterpret_cast<uint4*>(a.xb + off + colj(2 * h)) = xbv;
         }
       }
@@ -635,6 +637,8 @@ hipError_t launch_tail(const TailArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
   if (a.F <= 0 || a.F % HC != 0 || !a.flags || (a.parallel && (!a.ss_in || !a.xb_in || a.nt_in < 1)))
     return hipErrorInvalidValue;
+  // the result goes to x, or (x null) only to the skip slot of a push with no pop
+  if (!a.x_in || (!a.x && (!a.push_dst || a.pop_src))) return hipErrorInvalidValue;
   if (a.qkv.frag &&
       (a.row_map || a.M % 64 != 0 || a.Lp < TM || a.Lp % 64 != 0 || !a.qkv.scale || !a.qkv.q || !a.qkv.k ||
        !a.qkv.vt || !a.qkv.rope || !qkv_tile_supported(DM, qkvp::HD, a.qkv.n_heads, a.qkv.n_kv, a.qkv.rope_dims, 0)))
